@@ -1,0 +1,179 @@
+"""Python binding of libmr, the MI355X W-way sum-reduce and param-contiguous gather library.
+
+A thin ctypes layer over the C ABI declared in include/mr.h: it turns torch tensors into device
+pointers, sizes and the current HIP stream, calls the entry point of the same name and raises on a
+non-zero status.  Every step of the computation runs in the HIP kernels of libmr.so; there is no
+fallback.  If libmr.so has not been built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmr.so")
+
+MR_OK = 0
+STATUS = {
+    0: "MR_OK",
+    -1: "MR_ERR_INVALID_ARG",
+    -2: "MR_ERR_DTYPE",
+    -3: "MR_ERR_ALIAS",
+    -4: "MR_ERR_WORKSPACE",
+    -5: "MR_ERR_HIP",
+}
+DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2, "int32": 3}
+MODE_CODE = {"oneshot": 0, "twoshot": 1}
+MAX_W = 16
+MAX_PARAMS_PER_LAUNCH = 128
+
+# Exported symbols of include/mr.h, with ctypes signatures.
+_SIGS = {
+    "mr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mr_last_hip_error": (ctypes.c_int, []),
+    "mr_version": (ctypes.c_int, []),
+    "mr_allreduce_sum": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t,
+                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
+    "mr_allgather_param_contig": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_void_p, ctypes.c_void_p]),
+    "mr_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_size_t, ctypes.c_int]),
+    "mr_set_workspace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]),
+    "mr_workspace_check": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32)]),
+}
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+class MRError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmr.so (once).  Raises if it is missing: the product path has no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != MR_OK:
+        raise MRError(status, what)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def dtype_name(t) -> str:
+    torch = _torch()
+    return {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32", torch.int32: "int32"}[t.dtype]
+
+
+def _stream_handle(stream) -> int | None:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream or None
+
+
+def _dev_tensor(t, what: str):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous device tensor")
+
+
+def allreduce_sum(bufs: Sequence, out, mode: str = "oneshot", stream=None):
+    """out = elementwise fp32 sum (rank order 0..W-1) of the W same-shape, same-dtype tensors ``bufs``."""
+    W = len(bufs)
+    for b in bufs:
+        _dev_tensor(b, "rank buffer")
+        if b.dtype != out.dtype or b.numel() != out.numel():
+            raise ValueError("rank buffers and out must share dtype and element count")
+    _dev_tensor(out, "out")
+    ptrs = (ctypes.c_void_p * max(W, 1))(*[b.data_ptr() for b in bufs])
+    st = lib().mr_allreduce_sum(ptrs, W, out.numel(), DTYPE_CODE[dtype_name(out)], out.data_ptr(),
+                                MODE_CODE[mode], _stream_handle(stream))
+    _check(st, "mr_allreduce_sum")
+    return out
+
+
+def allgather_param_contig(src, W: int, G: int, splits: Sequence[int], out, stream=None):
+    """Scatter the rank-major ``src`` ([W][T], T = sum(splits)) into [param][rank] order in ``out``."""
+    _dev_tensor(src, "src")
+    _dev_tensor(out, "out")
+    if src.dtype != out.dtype or src.numel() != out.numel():
+        raise ValueError("src and out must share dtype and element count")
+    sp = (ctypes.c_uint64 * max(len(splits), 1))(*[int(x) for x in splits])
+    st = lib().mr_allgather_param_contig(src.data_ptr(), W, G, sp, len(splits), DTYPE_CODE[dtype_name(src)],
+                                         out.data_ptr(), _stream_handle(stream))
+    _check(st, "mr_allgather_param_contig")
+    return out
+
+
+def workspace_bytes(W: int, n: int, dtype: str) -> int:
+    return int(lib().mr_workspace_bytes(W, n, DTYPE_CODE[dtype]))
+
+
+def set_workspace(buf=None, stream=None) -> None:
+    """Bind a caller-owned uint8 device tensor as the two-shot workspace of ``stream`` (None unbinds)."""
+    ptr, nbytes = (None, 0) if buf is None else (buf.data_ptr(), buf.numel() * buf.element_size())
+    _check(lib().mr_set_workspace(_stream_handle(stream), ptr, nbytes), "mr_set_workspace")
+
+
+def workspace_check(stream=None) -> int:
+    """Synchronise ``stream`` and return (and clear) its two-shot barrier error word."""
+    flags = ctypes.c_uint32(0)
+    _check(lib().mr_workspace_check(_stream_handle(stream), ctypes.byref(flags)), "mr_workspace_check")
+    return int(flags.value)
+
+
+def prepare_allreduce(bufs: Sequence, out, mode: str = "oneshot", stream=None):
+    """Marshal the arguments of one mr_allreduce_sum call once; returns a no-argument callable that
+    enqueues that same call (for tight timing loops, where per-call marshalling would dominate)."""
+    W = len(bufs)
+    for b in bufs:
+        _dev_tensor(b, "rank buffer")
+    _dev_tensor(out, "out")
+    ptrs = (ctypes.c_void_p * max(W, 1))(*[b.data_ptr() for b in bufs])
+    f = lib().mr_allreduce_sum
+    args = (ptrs, W, out.numel(), DTYPE_CODE[dtype_name(out)], out.data_ptr(), MODE_CODE[mode],
+            _stream_handle(stream))
+
+    def call() -> None:
+        st = f(*args)
+        if st != MR_OK:
+            raise MRError(st, "mr_allreduce_sum")
+
+    call.keepalive = (ptrs, list(bufs), out)
+    return call
+
+
+def prepare_allgather_param_contig(src, W: int, G: int, splits: Sequence[int], out, stream=None):
+    """Pre-marshalled mr_allgather_param_contig call (see prepare_allreduce)."""
+    _dev_tensor(src, "src")
+    _dev_tensor(out, "out")
+    sp = (ctypes.c_uint64 * max(len(splits), 1))(*[int(x) for x in splits])
+    f = lib().mr_allgather_param_contig
+    args = (src.data_ptr(), W, G, sp, len(splits), DTYPE_CODE[dtype_name(src)], out.data_ptr(),
+            _stream_handle(stream))
+
+    def call() -> None:
+        st = f(*args)
+        if st != MR_OK:
+            raise MRError(st, "mr_allgather_param_contig")
+
+    call.keepalive = (sp, src, out)
+    return call

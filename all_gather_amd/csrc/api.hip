@@ -1,0 +1,280 @@
+// C ABI of libmr: argument validation, launch planning and the two-shot workspace registry.
+// The public contract (argument meaning, layout, ownership, errors) is documented in include/mr.h.
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "mr_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+uint32_t env_u32(const char* name, uint32_t dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  unsigned long x = std::strtoul(v, &end, 0);
+  return (end && *end == 0) ? static_cast<uint32_t>(x) : dflt;
+}
+
+// Debug and tuning overrides, read once at load.
+const uint32_t g_spin_limit = env_u32("MR_SPIN_LIMIT", 1u << 22);
+const bool g_trace = env_u32("MR_TRACE", 0) != 0;
+
+mr_status hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return MR_ERR_HIP;
+}
+
+bool is_float(mr_dtype d) { return d == MR_BF16 || d == MR_FP16 || d == MR_FP32; }
+bool valid_dtype(int d) { return d >= MR_BF16 && d <= MR_INT32; }
+
+bool overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
+  return na && nb && a < b + nb && b < a + na;
+}
+
+// ------------------------------------------------------------------------------ workspace registry
+struct Workspace {
+  char* base = nullptr;
+  size_t bytes = 0;
+  bool owned = false;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t ws_bytes_for(size_t n, int esize) {
+  return mr::kCtrlBytes + round_up(n * static_cast<size_t>(esize) + 16, mr::kStageAlign);
+}
+
+// Returns the workspace of (current device, stream), allocating or growing a library-owned one.
+mr_status get_workspace(hipStream_t st, size_t need, Workspace* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& w = g_ws[{dev, st}];
+  if (w.bytes >= need) {
+    *out = w;
+    return MR_OK;
+  }
+  if (w.base && !w.owned) return MR_ERR_WORKSPACE;  // caller-owned and too small
+  if (w.base) {  // grow: earlier work on this stream may still use the old buffer
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e);
+    hipFree(w.base);
+    w = Workspace{};
+  }
+  void* p = nullptr;
+  const size_t bytes = round_up(need, size_t(1) << 20);
+  e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) return hip_fail(e);
+  e = mr::launch_zero_ctrl(reinterpret_cast<mr::Ctrl*>(p), st);
+  if (e != hipSuccess) {
+    hipFree(p);
+    return hip_fail(e);
+  }
+  w.base = static_cast<char*>(p);
+  w.bytes = bytes;
+  w.owned = true;
+  *out = w;
+  return MR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mr_status_string(mr_status s) {
+  switch (s) {
+    case MR_OK: return "MR_OK";
+    case MR_ERR_INVALID_ARG: return "MR_ERR_INVALID_ARG: invalid argument";
+    case MR_ERR_DTYPE: return "MR_ERR_DTYPE: dtype not supported by this operation";
+    case MR_ERR_ALIAS: return "MR_ERR_ALIAS: output partially overlaps an input";
+    case MR_ERR_WORKSPACE: return "MR_ERR_WORKSPACE: two-shot workspace missing, too small or in error";
+    case MR_ERR_HIP: return "MR_ERR_HIP: HIP runtime call failed";
+    default: return "unknown mr_status";
+  }
+}
+
+int mr_last_hip_error(void) { return g_last_hip_error; }
+
+int mr_version(void) { return 100; }
+
+size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
+  if (W < 1 || W > MR_MAX_W || !is_float(dtype)) return 0;
+  const int es = mr::elem_size(dtype);
+  if (n > (SIZE_MAX - mr::kCtrlBytes - 1024) / static_cast<size_t>(es)) return 0;
+  return ws_bytes_for(n, es);
+}
+
+mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out, mr_mode mode,
+                           mr_stream stream) {
+  if (W < 1 || W > MR_MAX_W) return MR_ERR_INVALID_ARG;
+  if (mode != MR_ONESHOT && mode != MR_TWOSHOT) return MR_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
+  if (!is_float(dtype)) return MR_ERR_DTYPE;
+  if (n == 0) return MR_OK;
+  if (!bufs || !out) return MR_ERR_INVALID_ARG;
+  const int es = mr::elem_size(dtype);
+  if (n > (SIZE_MAX / 2 - mr::kCtrlBytes) / static_cast<size_t>(es)) return MR_ERR_INVALID_ARG;
+  const size_t nbytes = n * static_cast<size_t>(es);
+  const uintptr_t po = reinterpret_cast<uintptr_t>(out);
+  mr::RankPtrs in{};
+  bool same_phase = (po % static_cast<uintptr_t>(es)) == 0;
+  for (int r = 0; r < W; ++r) {
+    if (!bufs[r]) return MR_ERR_INVALID_ARG;
+    const uintptr_t pr = reinterpret_cast<uintptr_t>(bufs[r]);
+    if (pr != po && overlap(pr, nbytes, po, nbytes)) return MR_ERR_ALIAS;
+    if ((pr & 15u) != (po & 15u)) same_phase = false;
+    in.p[r] = static_cast<const char*>(bufs[r]);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  mr::ReduceShape sh{};
+  sh.n = n;
+  sh.vec = same_phase ? 1 : 0;
+  if (sh.vec) {
+    const size_t V = 16 / static_cast<size_t>(es);
+    size_t head = ((16u - (po & 15u)) & 15u) / static_cast<size_t>(es);
+    if (head > n) head = n;
+    sh.head = head;
+    sh.npacks = (n - head) / V;
+  }
+
+  hipError_t e;
+  if (mode == MR_ONESHOT) {
+    if (g_trace)
+      std::fprintf(stderr, "[mr] allreduce oneshot W=%d n=%zu dtype=%d vec=%d head=%zu packs=%zu\n", W, n,
+                   static_cast<int>(dtype), sh.vec, sh.head, sh.npacks);
+    e = mr::launch_oneshot(in, W, dtype, static_cast<char*>(out), sh, st);
+  } else {
+    Workspace ws;
+    mr_status s = get_workspace(st, ws_bytes_for(n, es), &ws);
+    if (s != MR_OK) return s;
+    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, g_spin_limit);
+    if (static_cast<uint64_t>(pl.n1) + pl.n2 >= (1ull << 24)) return MR_ERR_INVALID_ARG;
+    // the stage shares out's 16-byte phase so its body is 16-byte aligned too
+    char* stage = ws.base + mr::kCtrlBytes + (sh.vec ? (po & 15u) : 0);
+    if (g_trace)
+      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d chunk=%zu n1=%u n2=%u\n", W, n,
+                   static_cast<int>(dtype), sh.vec, pl.chunk_packs, pl.n1, pl.n2);
+    e = mr::launch_twoshot(in, W, dtype, static_cast<char*>(out), stage, reinterpret_cast<mr::Ctrl*>(ws.base), sh,
+                           pl, st);
+  }
+  return e == hipSuccess ? MR_OK : hip_fail(e);
+}
+
+mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_t* splits, int P, mr_dtype dtype,
+                                    void* out, mr_stream stream) {
+  if (W < 1 || W > 65535 || G < 1 || W % G != 0) return MR_ERR_INVALID_ARG;
+  if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
+  const uint64_t es = static_cast<uint64_t>(mr::elem_size(dtype));
+  uint64_t T = 0;
+  for (int s = 0; s < P; ++s) {
+    if (splits[s] > (1ull << 56) || T > (1ull << 56)) return MR_ERR_INVALID_ARG;
+    T += splits[s];
+  }
+  if (T > (1ull << 56) / (static_cast<uint64_t>(W) * es)) return MR_ERR_INVALID_ARG;
+  if (T == 0) return MR_OK;
+  if (!src || !out) return MR_ERR_INVALID_ARG;
+  const uint64_t total_bytes = static_cast<uint64_t>(W) * T * es;
+  if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
+    return MR_ERR_ALIAS;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  uint64_t base = 0;  // shard offset of the first parameter of this launch
+  for (int s0 = 0; s0 < P; s0 += mr::kMaxParams) {
+    const int np = (P - s0) < mr::kMaxParams ? (P - s0) : mr::kMaxParams;
+    mr::GatherArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.src = static_cast<const char*>(src);
+    a.out = static_cast<char*>(out);
+    a.T = T;
+    a.P = static_cast<uint32_t>(np);
+    a.W = static_cast<uint32_t>(W);
+    a.G = static_cast<uint32_t>(G);
+    a.elem = static_cast<uint32_t>(es);
+    uint64_t tiles = 0;
+    for (int i = 0; i < np; ++i) {
+      a.O[i] = base;
+      a.tile_prefix[i] = static_cast<uint32_t>(tiles);
+      const uint64_t E = splits[s0 + i];
+      tiles += static_cast<uint64_t>(G) * ((E * es + mr::kGatherTileBytes - 1) / mr::kGatherTileBytes);
+      base += E;
+      if (tiles >= (1ull << 31)) return MR_ERR_INVALID_ARG;
+    }
+    a.O[np] = base;
+    a.tile_prefix[np] = static_cast<uint32_t>(tiles);
+    a.tiles_per_block = static_cast<uint32_t>(tiles);
+    const uint64_t total = tiles * static_cast<uint64_t>(W / G);
+    if (total >= (1ull << 32)) return MR_ERR_INVALID_ARG;
+    a.total_tiles = static_cast<uint32_t>(total);
+    if (g_trace)
+      std::fprintf(stderr, "[mr] param_contig W=%d G=%d params=[%d,%d) T=%llu tiles=%u\n", W, G, s0, s0 + np,
+                   static_cast<unsigned long long>(T), a.total_tiles);
+    const hipError_t e = mr::launch_param_contig(a, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return MR_OK;
+}
+
+mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dev_ptr && (bytes < mr::kCtrlBytes || (reinterpret_cast<uintptr_t>(dev_ptr) % mr::kStageAlign) != 0))
+    return MR_ERR_INVALID_ARG;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& w = g_ws[{dev, st}];
+  if (w.base && w.owned) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e);
+    hipFree(w.base);
+  }
+  w = Workspace{};
+  if (!dev_ptr) return MR_OK;
+  e = mr::launch_zero_ctrl(static_cast<mr::Ctrl*>(dev_ptr), st);
+  if (e != hipSuccess) return hip_fail(e);
+  w.base = static_cast<char*>(dev_ptr);
+  w.bytes = bytes;
+  w.owned = false;
+  return MR_OK;
+}
+
+mr_status mr_workspace_check(mr_stream stream, uint32_t* flags) {
+  if (!flags) return MR_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  Workspace w;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws.find({dev, st});
+    if (it == g_ws.end() || !it->second.base) return MR_ERR_WORKSPACE;
+    w = it->second;
+  }
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  mr::Ctrl c;
+  e = hipMemcpy(&c, w.base, sizeof(c), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e);
+  *flags = c.err;
+  // clear the error bit and re-arm every barrier word (a timed-out call may have left counts behind)
+  e = mr::launch_zero_ctrl(reinterpret_cast<mr::Ctrl*>(w.base), st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  return MR_OK;
+}
+
+}  // extern "C"

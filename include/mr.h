@@ -1,0 +1,138 @@
+/*
+ * mr.h -- C ABI of libmr: the W-way elementwise sum-reduce and the param-contiguous gather on one
+ * MI355X (gfx950).
+ *
+ * Plain C. Only <stddef.h> and <stdint.h> are needed.  Every pointer argument marked "device" is GPU
+ * memory (hipMalloc'd or torch-allocated) on the current HIP device; "host" pointers are CPU memory
+ * read during the call only.  Streams are hipStream_t values (NULL = the default stream); the type
+ * below is layout-compatible with hipStream_t, so HIP callers pass their stream directly.
+ *
+ * Semantics shared by every entry point:
+ *  - Work is enqueued asynchronously on `stream`; no call synchronises the host except
+ *    mr_workspace_check.  Kernel faults surface at the caller's next synchronisation (HIP convention).
+ *  - Arguments are validated before any HIP call; an invalid call enqueues nothing.
+ *  - The caller owns every buffer it passes and keeps it alive until the stream work completes (with
+ *    a caching allocator and side streams, record the buffer on the stream).  The library never frees
+ *    caller memory.
+ *  - Return value: MR_OK (0) or a negative mr_status code; mr_status_string() names it and
+ *    mr_last_hip_error() gives the hipError_t behind the calling thread's last MR_ERR_HIP.
+ */
+#ifndef MR_H_
+#define MR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* mr_stream; /* == hipStream_t */
+
+typedef int mr_status;
+#define MR_OK 0
+#define MR_ERR_INVALID_ARG (-1) /* null pointer, W/G/P out of range, size overflow */
+#define MR_ERR_DTYPE (-2)       /* dtype not supported by this operation */
+#define MR_ERR_ALIAS (-3)       /* output partially overlaps an input */
+#define MR_ERR_WORKSPACE (-4)   /* two-shot workspace missing, too small, or barrier error seen */
+#define MR_ERR_HIP (-5)         /* a HIP runtime call failed; see mr_last_hip_error() */
+
+typedef enum mr_dtype { MR_BF16 = 0, MR_FP16 = 1, MR_FP32 = 2, MR_INT32 = 3 } mr_dtype;
+typedef enum mr_mode { MR_ONESHOT = 0, MR_TWOSHOT = 1 } mr_mode;
+
+#define MR_MAX_W 16
+#define MR_MAX_PARAMS_PER_LAUNCH 128
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mr_status_string(mr_status status);
+
+/* hipError_t value behind the calling thread's most recent MR_ERR_HIP (0 if none). */
+int mr_last_hip_error(void);
+
+/*
+ * mr_allreduce_sum -- one rank's result of a sum all-reduce over W rank buffers.
+ *
+ * Computes, for every element i < n,
+ *     out[i] = narrow( (((widen(bufs[0][i]) + widen(bufs[1][i])) + ...) + widen(bufs[W-1][i])) )
+ * with each term widened exactly to fp32, every add an fp32 round-to-nearest-even add in rank order
+ * 0..W-1 (no reassociation, subnormals kept), and the sum rounded to nearest even into `dtype`.
+ * That is the elementwise sum each block of a one-shot custom all-reduce forms after pulling its
+ * chunk from every peer (page "Question and suggestions about custom allreduce", the quoted one-shot
+ * block schedule), and the per-slice sum of two-shot (same page, reduce-scatter then gather; page
+ * "triton_multimem_all_reduce.py", the per-rank slice of 128-bit packs).  The result is bit-identical
+ * in both modes.
+ *
+ *  bufs   host array of W device pointers, each to n contiguous elements of `dtype` (read only).
+ *         Pointers may repeat.  Any alignment is accepted: when every pointer (and out) has the same
+ *         address modulo 16 the kernels use 16-byte loads, otherwise a slower element-wise path.
+ *  W      1 .. MR_MAX_W.
+ *  n      elements per buffer; n == 0 is a successful no-op.
+ *  dtype  MR_BF16, MR_FP16 or MR_FP32 (output has the same dtype); MR_INT32 -> MR_ERR_DTYPE.
+ *  out    device pointer to n elements.  out == bufs[k] (exactly) is allowed (in place); any other
+ *         overlap with an input -> MR_ERR_ALIAS.
+ *  mode   MR_ONESHOT: one pass, W reads and one write per element.
+ *         MR_TWOSHOT: phase 1 reduces each of the W chunks of ceil(n/W) elements (rounded up to 16
+ *         bytes) into a stage buffer, an intra-GPU release/acquire flag barrier orders the phases,
+ *         phase 2 copies the stage into out.  Needs a workspace (see below).
+ *  stream hipStream_t to enqueue on.
+ */
+mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out,
+                           mr_mode mode, mr_stream stream);
+
+/*
+ * mr_allgather_param_contig -- scatter a rank-major gathered buffer into [param][rank] order.
+ *
+ * src holds W rank shards of T = sum(splits) elements each, back to back ([W][T]).  Shard r is laid
+ * out as P parameter pieces of splits[s] elements at offset O_s = splits[0] + ... + splits[s-1].
+ * out receives, for every parameter s, the W pieces of s one after another:
+ *     out[O_s*W + r*splits[s] + j] = src[r*T + O_s + j]
+ * Ranks form W/G node-blocks of G ranks; the launch walks node-block m, then parameter s, then slot g
+ * (rank r = m*G + g), placing node-block m of parameter s at O_s*W + m*G*splits[s] with slot stride
+ * splits[s] (page "ccl: hierarchical cross-node AllGather (intra-node SDMA + inter-node RDMA) #441",
+ * the commit adding enqueue_param_contiguous and the commit fusing the node-block x split loop into
+ * one launch).  The output does not depend on G.  It is a pure bit copy: every dtype bit pattern,
+ * NaN payloads included, is preserved; dtype only sets the element size.
+ *
+ *  src     device pointer, W*T elements (read only).
+ *  W       1 .. 65535;  G >= 1 with W % G == 0 (G == W: one node-block).
+ *  splits  host array of P element counts (splits[s] == 0 allowed).  Read during the call only.
+ *  P       >= 1.  Up to MR_MAX_PARAMS_PER_LAUNCH parameters go in one kernel launch; more are split
+ *          into independent launches of up to that many parameters each.
+ *  dtype   any mr_dtype (element size 2 or 4 bytes).
+ *  out     device pointer, W*T elements.  Any overlap with src -> MR_ERR_ALIAS.
+ *  All offsets are 64-bit; buffers beyond 2^31 bytes are supported.
+ */
+mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, const uint64_t* splits,
+                                    int P, mr_dtype dtype, void* out, mr_stream stream);
+
+/*
+ * Two-shot workspace.
+ *
+ * By default the library allocates, on first two-shot use of a (device, stream) pair, a grow-only
+ * workspace of mr_workspace_bytes() bytes holding the stage buffer and the barrier words; that first
+ * call (and a call that grows it) allocates and is therefore not safe under graph capture.  One
+ * workspace per (device, stream): two-shot calls on different streams never share barrier words.
+ *
+ * mr_workspace_bytes: bytes a caller-owned workspace needs for a two-shot call of this shape.
+ * mr_set_workspace:   bind caller-owned device memory (256-byte aligned) as the workspace of `stream`
+ *                     on the current device, replacing any library-owned one; the barrier words are
+ *                     cleared on `stream` here.  dev_ptr == NULL unbinds (the library allocates
+ *                     again on next use).  Not thread-safe against concurrent calls on that stream.
+ * mr_workspace_check: synchronises `stream`, then reads and clears the barrier error word of its
+ *                     workspace.  *flags receives it (0 = no error; bit 0 = a phase-2 block gave up
+ *                     waiting for phase 1, so that call's output is not valid).  Returns
+ *                     MR_ERR_WORKSPACE if there is no workspace for the stream.
+ */
+size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype);
+mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes);
+mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
+
+/* Library ABI version (major*100 + minor). */
+int mr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MR_H_ */

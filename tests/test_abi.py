@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/mr.h declares, and every
+argument error returns its code before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import all_gather_amd as mr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mr.h")
+
+OK, EINVAL, EDTYPE, EALIAS, EWS = 0, -1, -2, -3, -4
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mr_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mr.LIB_PATH):
+        pytest.fail("libmr.so is not built; run __graft_entry__.build() first")
+    return mr.lib()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(mr.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", mr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (mr_[a-z_]+)$", out, flags=re.M))
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_version_and_status_strings(L):
+    assert L.mr_version() == 100
+    for code, name in mr.STATUS.items():
+        assert L.mr_status_string(code).decode().startswith(name)
+    assert b"unknown" in L.mr_status_string(-99)
+    assert L.mr_last_hip_error() == 0
+
+
+def _ptrs(*vals):
+    return (ctypes.c_void_p * max(len(vals), 1))(*vals)
+
+
+@pytest.mark.parametrize("W", [0, -1, 17, 1000])
+def test_allreduce_rejects_bad_W(L, W):
+    assert L.mr_allreduce_sum(_ptrs(0x1000), W, 16, 0, 0x9000, 0, None) == EINVAL
+
+
+def test_allreduce_argument_errors(L):
+    p = _ptrs(0x10000, 0x20000)
+    assert L.mr_allreduce_sum(p, 2, 16, 3, 0x90000, 0, None) == EDTYPE          # int32 is not reduced
+    assert L.mr_allreduce_sum(p, 2, 16, 7, 0x90000, 0, None) == EINVAL          # unknown dtype
+    assert L.mr_allreduce_sum(p, 2, 16, 0, 0x90000, 2, None) == EINVAL          # unknown mode
+    assert L.mr_allreduce_sum(None, 2, 16, 0, 0x90000, 0, None) == EINVAL       # no buffer array
+    assert L.mr_allreduce_sum(p, 2, 16, 0, None, 0, None) == EINVAL             # no out
+    assert L.mr_allreduce_sum(_ptrs(0x10000, None), 2, 16, 0, 0x90000, 0, None) == EINVAL
+    assert L.mr_allreduce_sum(p, 2, 2 ** 63, 0, 0x90000, 0, None) == EINVAL     # size overflow
+    # n == 0 is a no-op that enqueues nothing (null pointers allowed)
+    assert L.mr_allreduce_sum(None, 2, 0, 0, None, 0, None) == OK
+    assert L.mr_allreduce_sum(None, 2, 0, 0, None, 1, None) == OK
+
+
+def test_allreduce_alias_rules(L):
+    n, es = 64, 2
+    a, b = 0x100000, 0x200000
+    # out overlapping an input without being equal to it
+    assert L.mr_allreduce_sum(_ptrs(a, b), 2, n, 0, a + 2, 0, None) == EALIAS
+    assert L.mr_allreduce_sum(_ptrs(a, b), 2, n, 0, b - es, 1, None) == EALIAS
+    assert L.mr_allreduce_sum(_ptrs(a, b), 2, n, 0, a - n * es + es, 0, None) == EALIAS
+    # fp32 elements are 4 bytes: an out 64 bytes past b still overlaps 64 fp32 elements of b
+    assert L.mr_allreduce_sum(_ptrs(a, b), 2, n, 2, b + 64, 0, None) == EALIAS
+
+
+def test_gather_argument_errors(L):
+    sp = (ctypes.c_uint64 * 3)(8, 16, 24)
+    src, out = 0x100000, 0x800000
+    assert L.mr_allgather_param_contig(src, 8, 3, sp, 3, 0, out, None) == EINVAL    # G does not divide W
+    assert L.mr_allgather_param_contig(src, 8, 0, sp, 3, 0, out, None) == EINVAL
+    assert L.mr_allgather_param_contig(src, 0, 1, sp, 3, 0, out, None) == EINVAL
+    assert L.mr_allgather_param_contig(src, 70000, 1, sp, 3, 0, out, None) == EINVAL
+    assert L.mr_allgather_param_contig(src, 8, 4, sp, 0, 0, out, None) == EINVAL    # no params
+    assert L.mr_allgather_param_contig(src, 8, 4, None, 3, 0, out, None) == EINVAL
+    assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 9, out, None) == EINVAL    # unknown dtype
+    assert L.mr_allgather_param_contig(None, 8, 4, sp, 3, 0, out, None) == EINVAL
+    assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 0, None, None) == EINVAL
+    huge = (ctypes.c_uint64 * 2)(2 ** 62, 2 ** 62)
+    assert L.mr_allgather_param_contig(src, 8, 4, huge, 2, 0, out, None) == EINVAL  # size overflow
+    zero = (ctypes.c_uint64 * 2)(0, 0)
+    assert L.mr_allgather_param_contig(None, 8, 4, zero, 2, 0, None, None) == OK     # empty: no-op
+    # overlap of src and out (W*T*s = 8*48*2 = 768 bytes)
+    assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 0, src + 766, None) == EALIAS
+    assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 0, src - 766, None) == EALIAS
+
+
+def test_workspace_sizes_and_errors(L):
+    assert L.mr_workspace_bytes(8, 0, 0) >= 1024
+    b = L.mr_workspace_bytes(8, 8_388_608, 0)
+    assert b >= 1024 + 8_388_608 * 2 and b % 256 == 0
+    assert L.mr_workspace_bytes(8, 1000, 2) >= 1024 + 4000
+    assert L.mr_workspace_bytes(0, 1000, 0) == 0
+    assert L.mr_workspace_bytes(8, 1000, 3) == 0
+    assert L.mr_set_workspace(None, 0x100010, 1 << 20) == EINVAL      # not 256-byte aligned
+    assert L.mr_set_workspace(None, 0x100000, 16) == EINVAL           # smaller than the barrier words
+    assert L.mr_workspace_check(None, None) == EINVAL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    x = torch.zeros(8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mr.allreduce_sum([x, x], torch.zeros_like(x))
+    with pytest.raises(ValueError):
+        mr.allgather_param_contig(x, 2, 1, [4], torch.zeros_like(x))
+
+
+def test_product_path_does_not_import_the_oracle():
+    # the package and its sources never reference the oracle or the workloads module
+    pkg = os.path.join(ROOT, "all_gather_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "workloads" not in txt, f

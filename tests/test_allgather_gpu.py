@@ -1,0 +1,129 @@
+"""GPU parity of mr_allgather_param_contig against the CPU oracle, through the C ABI.  Bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import all_gather_amd as mr
+import oracle
+import workloads
+from gpu_util import TORCH_DT, device, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gather(src_bits, W, G, splits, dtype):
+    src = to_dev(src_bits, dtype)
+    out = torch.empty_like(src)
+    out.view(torch.uint8).fill_(0xA5)
+    mr.allgather_param_contig(src, W, G, splits, out)
+    torch.cuda.synchronize()
+    return to_bits(out)
+
+
+def _check(src_bits, W, G, splits, dtype, what):
+    print(f"[case] {what}", flush=True)
+    want = oracle.allgather_param_contig_ref(src_bits, W, G, splits)
+    got = _gather(src_bits, W, G, splits, dtype)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:8].tolist()}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32", "int32"])
+def test_config4_random_bits(dtype):
+    c = workloads.CONFIG4
+    splits = workloads.log_uniform_splits(c["cfg"], c["P"])
+    T = int(splits.sum())
+    src = workloads.gather_source(c["cfg"], c["W"], T, dtype)
+    _check(src, c["W"], c["G"], splits, dtype, f"config4 {dtype} T={T}")
+
+
+def test_G_does_not_change_the_output():
+    W = 8
+    splits = [int(x) for x in workloads.log_uniform_splits(50, 20, lo=8, hi=100_000)]
+    T = sum(splits)
+    src = workloads.gather_source(50, W, T, "fp16")
+    outs = [_gather(src, W, G, splits, "fp16") for G in (1, 2, 4, 8)]
+    want = oracle.allgather_param_contig_ref(src, W, 4, splits)
+    for o in outs:
+        assert np.array_equal(o, want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_ragged_and_empty_splits(dtype):
+    # odd element counts give pieces whose source and destination 16-byte phases differ
+    W, G = 6, 3
+    splits = [0, 1, 7, 8, 9, 4095, 4096, 4097, 0, 8191, 16385, 3, 100_001]
+    T = sum(splits)
+    src = workloads.gather_source(51, W, T, dtype)
+    _check(src, W, G, splits, dtype, f"ragged {dtype}")
+
+
+def test_single_split_and_single_rank():
+    src = workloads.gather_source(52, 4, 10_000, "int32")
+    _check(src, 4, 2, [10_000], "int32", "P=1")
+    src = workloads.gather_source(53, 1, 777, "bf16")
+    _check(src, 1, 1, [100, 600, 77], "bf16", "W=1")
+
+
+def test_more_params_than_one_launch():
+    W, G = 8, 4
+    splits = [int(x) for x in workloads.log_uniform_splits(54, 300, lo=8, hi=20_000)]
+    T = sum(splits)
+    src = workloads.gather_source(54, W, T, "bf16")
+    _check(src, W, G, splits, "bf16", "P=300 (3 launches)")
+
+
+def test_unaligned_base_pointers():
+    W, G = 4, 2
+    splits = [64, 1000, 24, 8]
+    T = sum(splits)
+    src = workloads.gather_source(55, W, T + 8, "bf16")[: W * T + 8]
+    full = to_dev(src, "bf16")
+    for so, do in ((1, 1), (1, 0), (3, 5)):
+        s = full[so:so + W * T]
+        ob = torch.empty(W * T + 8, dtype=torch.bfloat16, device=device())
+        o = ob[do:do + W * T]
+        mr.allgather_param_contig(s, W, G, splits, o)
+        torch.cuda.synchronize()
+        want = oracle.allgather_param_contig_ref(src[so:so + W * T], W, G, splits)
+        assert np.array_equal(to_bits(o), want), (so, do)
+
+
+def test_over_2GiB_int32_68M_per_rank():
+    """Eight ranks of 68,157,440 int32 elements: the gathered buffer is 2.18 GB, past 2^31 bytes, so a
+    32-bit byte offset anywhere would misplace data."""
+    W, G = 8, 4
+    splits = [33_554_432, 33_554_432, 1_048_576]
+    T = sum(splits)
+    src = np.arange(W * T, dtype=np.uint32)  # every element tagged with its own index
+    print(f"[case] 68M int32 per rank, {W * T * 4 / 1e9:.2f} GB", flush=True)
+    dsrc = torch.arange(W * T, dtype=torch.int32, device=device())
+    out = torch.empty_like(dsrc)
+    mr.allgather_param_contig(dsrc, W, G, splits, out)
+    torch.cuda.synchronize()
+    want = oracle.allgather_param_contig_ref(src, W, G, splits)
+    got = to_bits(out)
+    assert np.array_equal(got, want)
+    del dsrc, out
+    torch.cuda.empty_cache()
+
+
+def test_gather_on_side_stream_with_event_consumer():
+    W, G = 8, 4
+    splits = [int(x) for x in workloads.log_uniform_splits(56, 16, lo=1024, hi=2_000_000)]
+    T = sum(splits)
+    side = torch.cuda.Stream()
+    out = torch.empty(W * T, dtype=torch.float32, device=device())
+    for rep in range(3):
+        src = workloads.gather_source(60 + rep, W, T, "fp32")
+        want = oracle.allgather_param_contig_ref(src, W, G, splits)
+        dsrc = to_dev(src, "fp32")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            mr.allgather_param_contig(dsrc, W, G, splits, out)
+            ev = torch.cuda.Event()
+            ev.record(side)
+        torch.cuda.current_stream().wait_event(ev)
+        copy = out.clone()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(copy), want), rep

@@ -1,0 +1,227 @@
+"""GPU parity of mr_allreduce_sum (one-shot and two-shot) against the CPU oracle, through the C ABI.
+
+Bit-exact in both modes (NaN payloads compare by NaN-ness only)."""
+import numpy as np
+import pytest
+import torch
+
+import all_gather_amd as mr
+import oracle
+import workloads
+from gpu_util import TORCH_DT, assert_reduce_equal, device, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+MODES = ("oneshot", "twoshot")
+
+
+def _run(dbufs, dtype, n, mode, out=None):
+    if out is None:
+        out = torch.empty(n, dtype=TORCH_DT[dtype], device=device())
+    mr.allreduce_sum(dbufs, out, mode=mode)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_modes(bufs, dtype, what):
+    n = len(bufs[0])
+    want = oracle.allreduce_sum_ref(bufs, dtype)
+    dbufs = [to_dev(b, dtype) for b in bufs]
+    for mode in MODES:
+        print(f"[case] {what} {mode}", flush=True)
+        got = to_bits(_run(dbufs, dtype, n, mode))
+        assert_reduce_equal(got, want, dtype, f"{what} {mode}")
+    assert mr.workspace_check() == 0
+
+
+def test_config1_w4_bf16_uniform():
+    c = workloads.CONFIG1
+    _check_modes(workloads.rank_buffers(c["cfg"], c["W"], c["n"], c["dtype"], c["dist"]), "bf16", "config1")
+
+
+def test_config2_w8_bf16_16MiB_normal():
+    c = workloads.CONFIG2
+    _check_modes(workloads.rank_buffers(c["cfg"], c["W"], c["n"], c["dtype"], c["dist"]), "bf16", "config2")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 8, 11, 16])
+def test_dtypes_W_and_ragged_sizes(dtype, W):
+    for n in (1, 7, 8, 9, 1000, 4096 * W + 3, 300_007):
+        bufs = workloads.rank_buffers(100 + W, W, n, dtype, "uniform")
+        _check_modes(bufs, dtype, f"{dtype} W={W} n={n}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_random_bit_patterns_specials(dtype):
+    # uniformly random bits: NaNs, infinities, subnormals, signed zeros and overflow all occur
+    W, n = 8, 200_003
+    bufs = [workloads.random_bits(7, r, n, dtype) for r in range(W)]
+    _check_modes(bufs, dtype, f"random bits {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_structured_special_values(dtype):
+    g = np.random.default_rng(3)
+    bd = np.uint16 if dtype != "fp32" else np.uint32
+    if dtype == "bf16":
+        pats = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC0, 0x3F80,
+                0xBF80, 0x3380, 0x3B80, 0x3F81]
+    else:
+        pats = [0, 0x80000000, 1, 0x80000001, 0x007FFFFF, 0x00800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F800000,
+                0xFF800000, 0x7FC00000, 0x3F800000, 0xBF800000, 0x33800000]
+    W, n = 4, 16 ** 3
+    bufs = [np.array(g.choice(pats, size=n), dtype=bd) for _ in range(W)]
+    _check_modes(bufs, dtype, f"specials {dtype}")
+
+
+def test_in_place_out_is_an_input():
+    W, n = 8, 100_000
+    bufs = workloads.rank_buffers(11, W, n, "bf16", "normal")
+    want = oracle.allreduce_sum_ref(bufs, "bf16")
+    for mode in MODES:
+        for k in (0, 5):
+            dbufs = [to_dev(b, "bf16") for b in bufs]
+            mr.allreduce_sum(dbufs, dbufs[k], mode=mode)
+            torch.cuda.synchronize()
+            assert_reduce_equal(to_bits(dbufs[k]), want, "bf16", f"in place k={k} {mode}")
+
+
+def test_repeated_input_pointer():
+    n = 50_001
+    b = workloads.rank_buffer(12, 0, n, "fp16", "uniform")
+    want = oracle.allreduce_sum_ref([b, b, b], "fp16")
+    d = to_dev(b, "fp16")
+    for mode in MODES:
+        assert_reduce_equal(to_bits(_run([d, d, d], "fp16", n, mode)), want, "fp16", mode)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_unaligned_views(dtype):
+    W, n = 5, 70_001
+    es = 2 if dtype == "bf16" else 4
+    bufs = workloads.rank_buffers(13, W, n + 16, dtype, "uniform")
+    dev_full = [to_dev(b, dtype) for b in bufs]
+    # (a) every pointer shifted by the same element offset: 16-byte body plus element-wise head
+    for off in (1, 3):
+        views = [d[off:off + n] for d in dev_full]
+        want = oracle.allreduce_sum_ref([b[off:off + n] for b in bufs], dtype)
+        for mode in MODES:
+            outbuf = torch.empty(n + 16, dtype=TORCH_DT[dtype], device=device())
+            out = outbuf[off:off + n]
+            mr.allreduce_sum(views, out, mode=mode)
+            torch.cuda.synchronize()
+            assert_reduce_equal(to_bits(out), want, dtype, f"same phase off={off} {mode}")
+    # (b) pointers with different 16-byte phases: element-wise path
+    offs = [r % (16 // es) for r in range(W)]
+    views = [dev_full[r][offs[r]:offs[r] + n] for r in range(W)]
+    want = oracle.allreduce_sum_ref([bufs[r][offs[r]:offs[r] + n] for r in range(W)], dtype)
+    for mode in MODES:
+        got = to_bits(_run(views, dtype, n, mode))
+        assert_reduce_equal(got, want, dtype, f"mixed phases {mode}")
+
+
+def test_oneshot_equals_twoshot_and_is_deterministic():
+    W, n = 8, 1_048_579
+    bufs = [workloads.random_bits(14, r, n, "bf16") for r in range(W)]
+    dbufs = [to_dev(b, "bf16") for b in bufs]
+    ref = to_bits(_run(dbufs, "bf16", n, "oneshot"))
+    out = torch.empty(n, dtype=torch.bfloat16, device=device())
+    for i in range(50):
+        mode = MODES[i % 2]
+        mr.allreduce_sum(dbufs, out, mode=mode)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(out), ref), f"launch {i} ({mode}) differs"
+    assert mr.workspace_check() == 0
+
+
+def test_twoshot_poisoned_stage_caller_workspace():
+    """The stage is refilled with NaN bits before every launch, so a phase-2 copy that ran ahead of
+    phase 1 would surface as a mismatch."""
+    W, n = 8, 4_194_304 + 24
+    bufs = workloads.rank_buffers(15, W, n, "bf16", "normal")
+    want = oracle.allreduce_sum_ref(bufs, "bf16")
+    dbufs = [to_dev(b, "bf16") for b in bufs]
+    nbytes = mr.workspace_bytes(W, n, "bf16")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device())
+    mr.set_workspace(ws)
+    try:
+        out = torch.empty(n, dtype=torch.bfloat16, device=device())
+        for i in range(200):
+            ws[1024:].fill_(0xFF)
+            out.fill_(0)
+            mr.allreduce_sum(dbufs, out, mode="twoshot")
+            if i % 20 == 0 or i == 199:
+                torch.cuda.synchronize()
+                assert_reduce_equal(to_bits(out), want, "bf16", f"poisoned launch {i}")
+        assert mr.workspace_check() == 0
+        # a caller workspace that is too small is refused
+        small = torch.empty(4096, dtype=torch.uint8, device=device())
+        mr.set_workspace(small)
+        with pytest.raises(mr.MRError) as ei:
+            mr.allreduce_sum(dbufs, out, mode="twoshot")
+        assert ei.value.status == -4
+    finally:
+        mr.set_workspace(None)
+
+
+def test_twoshot_on_two_streams_concurrently():
+    W, n = 8, 2_097_152 + 8
+    sets = [workloads.rank_buffers(16 + k, W, n, "bf16", "uniform") for k in range(2)]
+    wants = [oracle.allreduce_sum_ref(b, "bf16") for b in sets]
+    dsets = [[to_dev(b, "bf16") for b in s] for s in sets]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(2)]
+    torch.cuda.synchronize()
+    for rep in range(20):
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                mr.allreduce_sum(dsets[k], outs[k], mode="twoshot")
+    torch.cuda.synchronize()
+    for k in range(2):
+        assert_reduce_equal(to_bits(outs[k]), wants[k], "bf16", f"stream {k}")
+        assert mr.workspace_check(streams[k]) == 0
+
+
+def test_cross_stream_consumer_waits_on_event():
+    """The reduce runs on a side stream with per-rep inputs; a consumer on the main stream waits on an
+    event recorded after it and reads the output (the overlap pattern of FSDP's all-gather hook)."""
+    W, n = 8, 1_000_003
+    side = torch.cuda.Stream()
+    out = torch.empty(n, dtype=torch.bfloat16, device=device())
+    for rep in range(4):
+        bufs = workloads.rank_buffers(30 + rep, W, n, "bf16", "normal")
+        want = oracle.allreduce_sum_ref(bufs, "bf16")
+        dbufs = [to_dev(b, "bf16") for b in bufs]
+        torch.cuda.synchronize()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            mr.allreduce_sum(dbufs, out, mode="twoshot" if rep % 2 else "oneshot")
+            ev = torch.cuda.Event()
+            ev.record(side)
+        torch.cuda.current_stream().wait_event(ev)
+        copy = out.clone()  # consumer on the main stream
+        torch.cuda.synchronize()
+        assert_reduce_equal(to_bits(copy), want, "bf16", f"rep {rep}")
+
+
+@pytest.mark.parametrize("per_rank", workloads.CONFIG3_BYTES, ids=lambda b: f"{b >> 10}KiB")
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_config3_size_sweep(dtype, per_rank):
+    es = 2 if dtype == "bf16" else 4
+    n = per_rank // es
+    bufs = workloads.rank_buffers(3, 8, n, dtype, "uniform")
+    dbufs = [to_dev(b, dtype) for b in bufs]
+    if n <= 32 * 2 ** 20:
+        want = oracle.allreduce_sum_ref(bufs, dtype)
+        idx = None
+    else:  # sampled outputs: the oracle on 2^20 strided columns
+        idx = np.linspace(0, n - 1, 1 << 20).astype(np.int64)
+        want = oracle.allreduce_sum_ref([b[idx] for b in bufs], dtype)
+    del bufs
+    for mode in MODES:
+        print(f"[case] config3 {dtype} per-rank {per_rank >> 10} KiB {mode}", flush=True)
+        got = to_bits(_run(dbufs, dtype, n, mode))
+        assert_reduce_equal(got if idx is None else got[idx], want, dtype, f"{dtype} {per_rank} {mode}")
+    del dbufs
+    torch.cuda.empty_cache()
+    assert mr.workspace_check() == 0
