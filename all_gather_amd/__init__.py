@@ -25,6 +25,8 @@ STATUS = {
 }
 DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2, "int32": 3}
 MODE_CODE = {"oneshot": 0, "twoshot": 1}
+OPTION_CODE = {"twoshot_sync": 0, "spin_limit": 1}
+TWOSHOT_SYNC = {"tile": 0, "chunk": 1, "grid": 2}
 MAX_W = 16
 MAX_PARAMS_PER_LAUNCH = 128
 
@@ -41,6 +43,8 @@ _SIGS = {
     "mr_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_size_t, ctypes.c_int]),
     "mr_set_workspace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]),
     "mr_workspace_check": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32)]),
+    "mr_set_option": (ctypes.c_int, [ctypes.c_int, ctypes.c_int64]),
+    "mr_get_option": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -138,6 +142,21 @@ def workspace_check(stream=None) -> int:
     flags = ctypes.c_uint32(0)
     _check(lib().mr_workspace_check(_stream_handle(stream), ctypes.byref(flags)), "mr_workspace_check")
     return int(flags.value)
+
+
+def set_option(name: str, value) -> None:
+    """Set a process-wide option: ``twoshot_sync`` ("tile", "chunk", "grid") or ``spin_limit`` (int)."""
+    if name == "twoshot_sync" and isinstance(value, str):
+        value = TWOSHOT_SYNC[value]
+    _check(lib().mr_set_option(OPTION_CODE[name], int(value)), "mr_set_option")
+
+
+def get_option(name: str):
+    v = ctypes.c_int64(0)
+    _check(lib().mr_get_option(OPTION_CODE[name], ctypes.byref(v)), "mr_get_option")
+    if name == "twoshot_sync":
+        return {c: k for k, c in TWOSHOT_SYNC.items()}[v.value]
+    return int(v.value)
 
 
 def prepare_allreduce(bufs: Sequence, out, mode: str = "oneshot", stream=None):

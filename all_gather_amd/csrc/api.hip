@@ -1,8 +1,10 @@
 // C ABI of libmr: argument validation, launch planning and the two-shot workspace registry.
 // The public contract (argument meaning, layout, ownership, errors) is documented in include/mr.h.
 
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
+#include <cstddef>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -22,8 +24,9 @@ uint32_t env_u32(const char* name, uint32_t dflt) {
   return (end && *end == 0) ? static_cast<uint32_t>(x) : dflt;
 }
 
-// Debug and tuning overrides, read once at load.
-const uint32_t g_spin_limit = env_u32("MR_SPIN_LIMIT", 1u << 22);
+// Process-wide options (mr_set_option); defaults may be overridden by the environment at load.
+std::atomic<uint32_t> g_spin_limit{env_u32("MR_SPIN_LIMIT", 1u << 22)};
+std::atomic<uint32_t> g_twoshot_sync{env_u32("MR_TWOSHOT_SYNC", mr::kSyncTile)};
 const bool g_trace = env_u32("MR_TRACE", 0) != 0;
 
 mr_status hip_fail(hipError_t e) {
@@ -50,18 +53,31 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Smallest workspace whose layout (barrier words, flag capacity bytes/256 words, stage) holds a stage
+// of n elements plus 16 bytes of alignment slack.
 size_t ws_bytes_for(size_t n, int esize) {
-  return mr::kCtrlBytes + round_up(n * static_cast<size_t>(esize) + 16, mr::kStageAlign);
+  const size_t base = mr::kCtrlBytes + n * static_cast<size_t>(esize) + 16 + 256;
+  return round_up(base + base / 63 + 4096, 4096);
 }
 
-// Returns the workspace of (current device, stream), allocating or growing a library-owned one.
-mr_status get_workspace(hipStream_t st, size_t need, Workspace* out) {
+bool ws_fits(size_t bytes, size_t n, int esize, size_t flags_needed) {
+  return mr::ws_stage_offset(bytes) + n * static_cast<size_t>(esize) + 16 <= bytes &&
+         flags_needed <= mr::ws_flag_words(bytes);
+}
+
+hipError_t ws_clear(char* base, size_t bytes, hipStream_t st) {
+  return mr::launch_zero_words(base, mr::ws_stage_offset(bytes) / 4, st);
+}
+
+// Returns the workspace of (current device, stream) able to hold a two-shot call of n elements
+// needing `flags` producer flags, allocating or growing a library-owned one.
+mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Workspace* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace& w = g_ws[{dev, st}];
-  if (w.bytes >= need) {
+  if (w.base && ws_fits(w.bytes, n, esize, flags)) {
     *out = w;
     return MR_OK;
   }
@@ -73,10 +89,10 @@ mr_status get_workspace(hipStream_t st, size_t need, Workspace* out) {
     w = Workspace{};
   }
   void* p = nullptr;
-  const size_t bytes = round_up(need, size_t(1) << 20);
+  const size_t bytes = round_up(ws_bytes_for(n, esize), size_t(1) << 20);
   e = hipMalloc(&p, bytes);
   if (e != hipSuccess) return hip_fail(e);
-  e = mr::launch_zero_ctrl(reinterpret_cast<mr::Ctrl*>(p), st);
+  e = ws_clear(static_cast<char*>(p), bytes, st);
   if (e != hipSuccess) {
     hipFree(p);
     return hip_fail(e);
@@ -111,8 +127,32 @@ int mr_version(void) { return 100; }
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
   if (W < 1 || W > MR_MAX_W || !is_float(dtype)) return 0;
   const int es = mr::elem_size(dtype);
-  if (n > (SIZE_MAX - mr::kCtrlBytes - 1024) / static_cast<size_t>(es)) return 0;
+  if (n > (SIZE_MAX / 4) / static_cast<size_t>(es)) return 0;
   return ws_bytes_for(n, es);
+}
+
+mr_status mr_set_option(mr_option opt, int64_t value) {
+  switch (opt) {
+    case MR_OPT_TWOSHOT_SYNC:
+      if (value < MR_TWOSHOT_SYNC_TILE || value > MR_TWOSHOT_SYNC_GRID) return MR_ERR_INVALID_ARG;
+      g_twoshot_sync.store(static_cast<uint32_t>(value));
+      return MR_OK;
+    case MR_OPT_SPIN_LIMIT:
+      if (value < 0 || value > 0xffffffffll) return MR_ERR_INVALID_ARG;
+      g_spin_limit.store(static_cast<uint32_t>(value));
+      return MR_OK;
+    default:
+      return MR_ERR_INVALID_ARG;
+  }
+}
+
+mr_status mr_get_option(mr_option opt, int64_t* value) {
+  if (!value) return MR_ERR_INVALID_ARG;
+  switch (opt) {
+    case MR_OPT_TWOSHOT_SYNC: *value = g_twoshot_sync.load(); return MR_OK;
+    case MR_OPT_SPIN_LIMIT: *value = g_spin_limit.load(); return MR_OK;
+    default: return MR_ERR_INVALID_ARG;
+  }
 }
 
 mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out, mr_mode mode,
@@ -156,18 +196,21 @@ mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dt
                    static_cast<int>(dtype), sh.vec, sh.head, sh.npacks);
     e = mr::launch_oneshot(in, W, dtype, static_cast<char*>(out), sh, st);
   } else {
+    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, g_twoshot_sync.load(), g_spin_limit.load());
+    const uint64_t grid = static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
+    if (grid >= (1ull << 24)) return MR_ERR_INVALID_ARG;
+    const size_t flags_needed = static_cast<size_t>(pl.chunks) * pl.t1;
     Workspace ws;
-    mr_status s = get_workspace(st, ws_bytes_for(n, es), &ws);
+    mr_status s = get_workspace(st, n, es, flags_needed, &ws);
     if (s != MR_OK) return s;
-    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, g_spin_limit);
-    if (static_cast<uint64_t>(pl.n1) + pl.n2 >= (1ull << 24)) return MR_ERR_INVALID_ARG;
-    // the stage shares out's 16-byte phase so its body is 16-byte aligned too
-    char* stage = ws.base + mr::kCtrlBytes + (sh.vec ? (po & 15u) : 0);
+    // the stage shares out's 16-byte phase so that its body is 16-byte aligned too
+    char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (sh.vec ? (po & 15u) : 0);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws.base + mr::kCtrlBytes);
     if (g_trace)
-      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d chunk=%zu n1=%u n2=%u\n", W, n,
-                   static_cast<int>(dtype), sh.vec, pl.chunk_packs, pl.n1, pl.n2);
-    e = mr::launch_twoshot(in, W, dtype, static_cast<char*>(out), stage, reinterpret_cast<mr::Ctrl*>(ws.base), sh,
-                           pl, st);
+      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu t1=%u t2=%u\n", W, n,
+                   static_cast<int>(dtype), sh.vec, pl.sync, pl.chunk_units, pl.t1, pl.t2);
+    e = mr::launch_twoshot(in, W, dtype, static_cast<char*>(out), stage, reinterpret_cast<mr::Ctrl*>(ws.base), flags,
+                           sh, pl, st);
   }
   return e == hipSuccess ? MR_OK : hip_fail(e);
 }
@@ -229,7 +272,7 @@ mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_
 
 mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (dev_ptr && (bytes < mr::kCtrlBytes || (reinterpret_cast<uintptr_t>(dev_ptr) % mr::kStageAlign) != 0))
+  if (dev_ptr && (bytes < mr::ws_stage_offset(bytes) + 256 || (reinterpret_cast<uintptr_t>(dev_ptr) % 256) != 0))
     return MR_ERR_INVALID_ARG;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -243,7 +286,7 @@ mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {
   }
   w = Workspace{};
   if (!dev_ptr) return MR_OK;
-  e = mr::launch_zero_ctrl(static_cast<mr::Ctrl*>(dev_ptr), st);
+  e = ws_clear(static_cast<char*>(dev_ptr), bytes, st);
   if (e != hipSuccess) return hip_fail(e);
   w.base = static_cast<char*>(dev_ptr);
   w.bytes = bytes;
@@ -266,12 +309,12 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags) {
   }
   e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e);
-  mr::Ctrl c;
-  e = hipMemcpy(&c, w.base, sizeof(c), hipMemcpyDeviceToHost);
+  uint32_t err = 0;
+  e = hipMemcpy(&err, w.base + offsetof(mr::Ctrl, err), sizeof(err), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e);
-  *flags = c.err;
-  // clear the error bit and re-arm every barrier word (a timed-out call may have left counts behind)
-  e = mr::launch_zero_ctrl(reinterpret_cast<mr::Ctrl*>(w.base), st);
+  *flags = err;
+  // clear the error bit and re-arm every barrier word and flag (a timed-out call may leave counts)
+  e = ws_clear(w.base, w.bytes, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e);
   return MR_OK;

@@ -9,24 +9,41 @@
 
 namespace mr {
 
-constexpr int kBlock = 256;             // threads per workgroup (4 wave64s)
-constexpr size_t kCtrlBytes = 1024;     // barrier words at the head of a two-shot workspace
-constexpr size_t kStageAlign = 256;
+constexpr int kBlock = 256;    // element-wise and gather workgroups (4 wave64s)
+constexpr int kRBlock = 1024;  // vector reduce workgroups (16 wave64s): fewer, larger groups ramp up faster
 
 inline int elem_size(mr_dtype d) { return (d == MR_BF16 || d == MR_FP16) ? 2 : 4; }
 
-// Barrier words of a two-shot workspace; each counter sits on its own 256-byte line.
+// ------------------------------------------------------------------------------- two-shot workspace
+//
+//   [0, 16 KiB)                 Ctrl: ticket counters and barrier words, one 256-byte line each
+//   [16 KiB, stage_off)         producer flags, one u32 per phase-1 tile (capacity bytes/1024 tiles)
+//   [stage_off, bytes)          stage buffer (n elements + 16 bytes of alignment slack)
+// Every word before stage_off is zero between calls; the calls restore that themselves.
+constexpr size_t kCtrlBytes = 16384;
+
 struct Ctrl {
-  uint32_t claim;     // ticket counter: the order in which workgroups start
-  uint32_t pad0[63];
-  uint32_t done1;     // phase-1 tiles released
-  uint32_t pad1[63];
-  uint32_t done2;     // phase-2 tiles finished (the last one resets the words)
-  uint32_t pad2[63];
-  uint32_t err;       // bit 0: a phase-2 wait gave up
-  uint32_t pad3[63];
+  uint32_t claim[MR_MAX_W][64];  // per-chunk ticket counters (start order of that chunk's workgroups)
+  uint32_t done1[MR_MAX_W][64];  // per-chunk phase-1 completions (chunk barrier)
+  uint32_t done2[MR_MAX_W][64];  // per-chunk phase-2 completions (resets the chunk words)
+  uint32_t gclaim[64];           // grid ticket counter (grid barrier)
+  uint32_t gdone1[64];           // grid phase-1 completions
+  uint32_t gdone2[64];           // grid phase-2 completions
+  uint32_t err[64];              // bit 0: a wait gave up after the spin limit
 };
-static_assert(sizeof(Ctrl) == kCtrlBytes, "ctrl layout");
+static_assert(sizeof(Ctrl) <= kCtrlBytes, "ctrl layout");
+
+inline size_t ws_flag_words(size_t bytes) { return bytes >> 10; }
+inline size_t ws_stage_offset(size_t bytes) {
+  return kCtrlBytes + ((ws_flag_words(bytes) * 4 + 255) & ~size_t(255));
+}
+
+// How phase 2 waits for phase 1.
+enum TwoShotSync : uint32_t {
+  kSyncTile = 0,   // per-tile producer flags: a phase-2 tile waits for the phase-1 tiles it copies
+  kSyncChunk = 1,  // per-chunk barrier: waits for every phase-1 tile of its chunk
+  kSyncGrid = 2,   // grid barrier: waits for every phase-1 tile of every chunk
+};
 
 struct RankPtrs {
   const char* p[MR_MAX_W];
@@ -40,25 +57,28 @@ struct RankPtrs {
 struct ReduceShape {
   size_t n;
   size_t head;
-  size_t npacks;   // packs of the vector body (or elements when vec == 0)
+  size_t npacks;   // packs of the vector body
   int vec;
 };
 
 struct TwoShotPlan {
-  uint32_t chunks;           // W chunks
-  size_t chunk_packs;        // packs per chunk (the last chunk may be shorter or empty)
-  uint32_t tiles1_per_chunk; // phase-1 tiles per chunk
-  uint32_t tiles2_per_chunk; // phase-2 tiles per chunk
-  uint32_t n1, n2;           // phase-1 / phase-2 tile counts
-  uint32_t spin_limit;       // bounded wait of a phase-2 workgroup (polls)
+  uint32_t chunks;       // W chunks
+  size_t chunk_units;    // packs (or elements on the element-wise path) per chunk
+  uint32_t t1;           // phase-1 tiles per chunk
+  uint32_t t2;           // phase-2 tiles per chunk
+  uint32_t ratio;        // phase-1 tiles per phase-2 tile
+  uint32_t unit1;        // units per phase-1 tile
+  uint32_t unit2;        // units per phase-2 tile
+  uint32_t sync;         // TwoShotSync
+  uint32_t spin_limit;   // bounded wait (polls)
 };
 
 hipError_t launch_oneshot(const RankPtrs& in, int W, mr_dtype dt, char* out, const ReduceShape& sh,
                           hipStream_t st);
 hipError_t launch_twoshot(const RankPtrs& in, int W, mr_dtype dt, char* out, char* stage, Ctrl* ctrl,
-                          const ReduceShape& sh, const TwoShotPlan& pl, hipStream_t st);
-TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t spin_limit);
-hipError_t launch_zero_ctrl(Ctrl* ctrl, hipStream_t st);
+                          uint32_t* flags, const ReduceShape& sh, const TwoShotPlan& pl, hipStream_t st);
+TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit);
+hipError_t launch_zero_words(void* p, size_t words, hipStream_t st);
 
 // ---------------------------------------------------------------------------------- param-contiguous
 constexpr int kMaxParams = MR_MAX_PARAMS_PER_LAUNCH;
@@ -67,14 +87,14 @@ constexpr uint32_t kGatherTileBytes = 16384;
 struct GatherArgs {
   const char* src;
   char* out;
-  uint64_t T;                       // elements per rank shard
-  uint64_t O[kMaxParams + 1];       // O[s]: element offset of parameter s inside a shard; O[P] = its end
+  uint64_t T;                            // elements per rank shard
+  uint64_t O[kMaxParams + 1];            // O[s]: element offset of parameter s inside a shard; O[P] = its end
   uint32_t tile_prefix[kMaxParams + 1];  // node-block-local tile prefix: G * sum of tiles of params < s
   uint32_t P;
   uint32_t W, G;
-  uint32_t elem;                    // bytes per element
-  uint32_t tiles_per_block;         // tiles of one node-block (= tile_prefix[P])
-  uint32_t total_tiles;             // W/G node-blocks * tiles_per_block
+  uint32_t elem;                         // bytes per element
+  uint32_t tiles_per_block;              // tiles of one node-block (= tile_prefix[P])
+  uint32_t total_tiles;                  // W/G node-blocks * tiles_per_block
 };
 
 hipError_t launch_param_contig(const GatherArgs& a, hipStream_t st);

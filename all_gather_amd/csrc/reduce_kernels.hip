@@ -4,10 +4,10 @@
 // custom allreduce": the quoted one-shot schedule pulls a chunk from every peer and sums it; the same
 // page's two-shot question: reduce-scatter, then gather).  Each term is widened exactly to fp32 and
 // added in rank order 0..W-1 with fp32 round-to-nearest-even adds; the sum is rounded to nearest even
-// into the buffer dtype.  The work is HBM streaming (W+1 bytes moved per element byte, at most W-1
+// into the buffer dtype.  The work is HBM streaming ((W+1) bytes moved per output byte, at most W-1
 // adds per element), so the kernels are shaped for memory-level parallelism: one 16-byte load per
-// lane per rank buffer, all W loads of U packs issued before any arithmetic, wave64 workgroups of 256
-// lanes, non-temporal hints because no byte is touched twice.  No LDS, no MFMA.
+// lane per rank buffer, all W loads issued before any arithmetic, 1024-lane workgroups (fewer groups
+// to dispatch and drain), non-temporal hints because no byte is touched twice.  No LDS, no MFMA.
 
 #include "mr_internal.h"
 
@@ -15,6 +15,28 @@ namespace mr {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer loads/stores, used for the two-shot stage because they carry an explicit cache policy.
+__device__ i32x4 raw_buffer_load_v4(i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ void raw_buffer_store_v4(i32x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.v4i32");
+
+// Cache policy: sc1 (device-scope coherence: stores write through the XCD's L2, loads do not hit a
+// line another XCD may have changed) plus nt (streaming).
+constexpr int kDeviceNT = (1 << 4) | (1 << 1);
+
+// Buffer resource for `bytes` bytes at `base` (raw, stride 0; gfx9 data-format word).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = static_cast<int32_t>(static_cast<uint32_t>(a));
+  r[1] = static_cast<int32_t>((a >> 32) & 0xffffu);
+  r[2] = static_cast<int32_t>(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
 
 // ------------------------------------------------------------------------------------- dtype traits
 
@@ -31,12 +53,8 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 struct Bf16 {
   static constexpr int kSize = 2;
   static constexpr int V = 8;
-  __device__ static float load1(const char* p) {
-    return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
-  }
-  __device__ static void store1(char* p, float f) {
-    *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(bf16_rne(f));
-  }
+  __device__ static float widen1(uint32_t b) { return __uint_as_float(b << 16); }
+  __device__ static uint32_t narrow1(float f) { return bf16_rne(f); }
   __device__ static void widen(const u32x4& w, float (&f)[V]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -57,25 +75,21 @@ struct Bf16 {
 struct Fp16 {
   static constexpr int kSize = 2;
   static constexpr int V = 8;
-  __device__ static float h2f(uint32_t b) {
+  __device__ static float widen1(uint32_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
   }
-  __device__ static uint32_t f2h(float f) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
-  }
-  __device__ static float load1(const char* p) { return h2f(*reinterpret_cast<const uint16_t*>(p)); }
-  __device__ static void store1(char* p, float f) { *reinterpret_cast<uint16_t*>(p) = f2h(f); }
+  __device__ static uint32_t narrow1(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
   __device__ static void widen(const u32x4& w, float (&f)[V]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[2 * i] = h2f(w[i] & 0xffffu);
-      f[2 * i + 1] = h2f(w[i] >> 16);
+      f[2 * i] = widen1(w[i] & 0xffffu);
+      f[2 * i + 1] = widen1(w[i] >> 16);
     }
   }
   __device__ static u32x4 narrow(const float (&f)[V]) {
     u32x4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = f2h(f[2 * i]) | (f2h(f[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = narrow1(f[2 * i]) | (narrow1(f[2 * i + 1]) << 16);
     return w;
   }
 };
@@ -83,8 +97,8 @@ struct Fp16 {
 struct Fp32 {
   static constexpr int kSize = 4;
   static constexpr int V = 4;
-  __device__ static float load1(const char* p) { return *reinterpret_cast<const float*>(p); }
-  __device__ static void store1(char* p, float f) { *reinterpret_cast<float*>(p) = f; }
+  __device__ static float widen1(uint32_t b) { return __uint_as_float(b); }
+  __device__ static uint32_t narrow1(float f) { return __float_as_uint(f); }
   __device__ static void widen(const u32x4& w, float (&f)[V]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
@@ -97,248 +111,307 @@ struct Fp32 {
   }
 };
 
+// Raw element bits.  `Dev` accesses are relaxed agent-scope atomics: device-coherent (sc1) loads and
+// write-through stores, used for the two-shot stage.
+template <int S, bool Dev>
+__device__ __forceinline__ uint32_t load_bits(const char* p) {
+  if (S == 2) {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+    return Dev ? __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *q;
+  }
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  return Dev ? __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *q;
+}
+template <int S, bool Dev>
+__device__ __forceinline__ void store_bits(char* p, uint32_t b) {
+  if (S == 2) {
+    uint16_t* q = reinterpret_cast<uint16_t*>(p);
+    if (Dev) __hip_atomic_store(q, static_cast<uint16_t>(b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *q = static_cast<uint16_t>(b);
+    return;
+  }
+  uint32_t* q = reinterpret_cast<uint32_t*>(p);
+  if (Dev) __hip_atomic_store(q, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *q = b;
+}
+
 // ---------------------------------------------------------------------------------- shared bodies
 
 // One element, any alignment: fp32 accumulation in rank order.
-template <typename D, int W>
+template <typename D, int W, bool Dev>
 __device__ __forceinline__ void reduce_elem(const RankPtrs& in, char* dst, size_t e) {
   const size_t off = e * D::kSize;
-  float acc = D::load1(in.p[0] + off);
+  float acc = D::widen1(load_bits<D::kSize, false>(in.p[0] + off));
 #pragma unroll
-  for (int r = 1; r < W; ++r) acc = acc + D::load1(in.p[r] + off);
-  D::store1(dst + off, acc);
+  for (int r = 1; r < W; ++r) acc = acc + D::widen1(load_bits<D::kSize, false>(in.p[r] + off));
+  store_bits<D::kSize, Dev>(dst + off, D::narrow1(acc));
 }
 
-// U packs per lane, lane-interleaved: pack index i = first + u*kBlock + lane, for i < end.
-// All W*U loads are issued before the first add so they are in flight together.
-template <typename D, int W, int U>
-__device__ __forceinline__ void reduce_packs(const RankPtrs& in, size_t head, char* dst, size_t first,
-                                             size_t end) {
-  const size_t hb = head * D::kSize;
-  u32x4 v[U][W];
+// One 16-byte pack per lane: W loads in flight together, then W-1 adds per element.
+template <typename D, int W>
+__device__ __forceinline__ u32x4 reduce_pack(const RankPtrs& in, size_t hb, size_t i) {
+  u32x4 v[W];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const size_t i = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
-    if (i < end) {
+  for (int r = 0; r < W; ++r) v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
+  float acc[D::V];
+  D::widen(v[0], acc);
 #pragma unroll
-      for (int r = 0; r < W; ++r)
-        v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
-    }
+  for (int r = 1; r < W; ++r) {
+    float t[D::V];
+    D::widen(v[r], t);
+#pragma unroll
+    for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
   }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const size_t i = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
-    if (i < end) {
-      float acc[D::V];
-      D::widen(v[u][0], acc);
-#pragma unroll
-      for (int r = 1; r < W; ++r) {
-        float t[D::V];
-        D::widen(v[u][r], t);
-#pragma unroll
-        for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
-      }
-      __builtin_nontemporal_store(D::narrow(acc), reinterpret_cast<u32x4*>(dst + hb) + i);
-    }
-  }
-}
-
-template <int U>
-__device__ __forceinline__ void copy_packs(const char* src, char* dst, size_t hb, size_t first, size_t end) {
-  u32x4 v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const size_t i = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
-    if (i < end) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + hb) + i);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const size_t i = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
-    if (i < end) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + hb) + i);
-  }
+  return D::narrow(acc);
 }
 
 // Elements outside the 16-byte body: [0, head) and [head + npacks*V, n).  At most 2V-2 of them.
-template <typename D, int W>
+template <typename D, int W, bool Dev>
 __device__ __forceinline__ void reduce_edges(const RankPtrs& in, char* dst, const ReduceShape& sh) {
   const size_t tail0 = sh.head + sh.npacks * D::V;
   const size_t count = sh.head + (sh.n - tail0);
-  for (size_t k = threadIdx.x; k < count; k += kBlock) reduce_elem<D, W>(in, dst, k < sh.head ? k : tail0 + (k - sh.head));
+  for (size_t k = threadIdx.x; k < count; k += blockDim.x)
+    reduce_elem<D, W, Dev>(in, dst, k < sh.head ? k : tail0 + (k - sh.head));
 }
 
 template <typename D>
-__device__ __forceinline__ void copy_edges(const char* src, char* dst, const ReduceShape& sh) {
+__device__ __forceinline__ void copy_edges_from_stage(const char* stage, char* dst, const ReduceShape& sh) {
   const size_t tail0 = sh.head + sh.npacks * D::V;
   const size_t count = sh.head + (sh.n - tail0);
-  for (size_t k = threadIdx.x; k < count; k += kBlock) {
+  for (size_t k = threadIdx.x; k < count; k += blockDim.x) {
     const size_t off = (k < sh.head ? k : tail0 + (k - sh.head)) * D::kSize;
-    if (D::kSize == 2)
-      *reinterpret_cast<uint16_t*>(dst + off) = *reinterpret_cast<const uint16_t*>(src + off);
-    else
-      *reinterpret_cast<uint32_t*>(dst + off) = *reinterpret_cast<const uint32_t*>(src + off);
+    store_bits<D::kSize, false>(dst + off, load_bits<D::kSize, true>(stage + off));
   }
 }
 
 // ---------------------------------------------------------------------------------------- one-shot
 
-constexpr int kOneShotU = 2;  // packs per lane per tile
-
 template <typename D, int W>
-__global__ __launch_bounds__(kBlock) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
-  constexpr size_t kTile = static_cast<size_t>(kBlock) * kOneShotU;
+__global__ __launch_bounds__(kRBlock) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
+  const size_t hb = sh.head * D::kSize;
   for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const size_t first = t * kTile;
-    reduce_packs<D, W, kOneShotU>(in, sh.head, out, first, sh.npacks);
+    const size_t i = t * kRBlock + threadIdx.x;
+    if (i < sh.npacks)
+      __builtin_nontemporal_store(reduce_pack<D, W>(in, hb, i), reinterpret_cast<u32x4*>(out + hb) + i);
   }
-  if (blockIdx.x == 0) reduce_edges<D, W>(in, out, sh);
+  if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
 
 template <typename D, int W>
 __global__ __launch_bounds__(kBlock) void oneshot_elem(RankPtrs in, char* out, size_t n) {
   for (size_t e = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; e < n;
        e += static_cast<size_t>(gridDim.x) * kBlock)
-    reduce_elem<D, W>(in, out, e);
+    reduce_elem<D, W, false>(in, out, e);
 }
 
 // ---------------------------------------------------------------------------------------- two-shot
 //
-// Phase 1 (reduce-scatter): chunk c of the message, c = 0..W-1, is reduced tile by tile into the
-// stage buffer.  Phase 2 (gather-copy): the stage is copied into out, chunks taken in the reverse
-// order, so a phase-2 workgroup copies bytes other workgroups reduced.
+// Phase 1 (reduce-scatter): chunk c = 0..W-1 of the message (a 1/W share, whole 16-byte packs) is
+// reduced into the stage buffer in tiles.  Phase 2 (gather-copy): the stage is copied into out in
+// tiles of `ratio` phase-1 tiles, so a phase-2 workgroup copies bytes that other workgroups reduced.
 //
-// Ordering the phases.  Workgroups take a ticket from an atomic counter when they start; tickets
-// below n1 do phase-1 tiles, the rest phase-2 tiles.  A phase-1 workgroup releases its stores with an
-// agent-scope release increment of done1 (after a workgroup barrier, so every lane's stores are in
-// its XCD's L2 before the release writes them back).  A phase-2 workgroup acquire-waits until done1
-// reaches n1.  Because tickets follow start order, every phase-1 tile belongs to a workgroup that
-// already runs and never waits, so the wait ends whether or not the whole grid is co-resident (no
-// reliance on workgroup 0 starting first, nor on two such kernels never sharing the GPU).  The wait
-// is bounded all the same: past spin_limit polls it sets an error bit and goes on.  Words reset
-// themselves: the holder of the last ticket clears `claim`, the last phase-2 workgroup clears done1
-// and done2, so consecutive launches on one stream need no host-side reset.
+// Start order.  A workgroup's role comes from a ticket taken when it starts, not from its index: with
+// the tile and chunk barriers, workgroup b belongs to chunk c = b % W and takes the next ticket of
+// that chunk's counter (tickets < t1 reduce phase-1 tile `ticket`, the rest copy phase-2 tiles); with
+// the grid barrier one counter orders every workgroup.  A phase-2 tile only waits for phase-1 tiles
+// whose tickets were handed out before its own, so their workgroups are already running and never
+// wait themselves: the wait ends whether or not the grid fits the GPU at once, and two such kernels
+// may share the GPU.  Each wait is still bounded (spin_limit polls), after which it sets an error bit.
+//
+// Release and acquire.  Phase-1 stage stores write through the XCD's L2 (device-scope coherence,
+// sc1); every lane waits for its stores to be acknowledged (vmcnt 0) before the workgroup barrier, and
+// only then does one lane publish the tile with a relaxed agent-scope atomic (performed at the device
+// coherence point).  Phase-2 lanes read the stage with device-scope loads (sc1), which do not return
+// a line another XCD may have changed.  That is release/acquire for exactly the stage bytes; the
+// compiler's agent-scope release would instead write back every dirty line of the whole L2 once per
+// workgroup, which costs several times the reduce itself.
+//
+// Barrier granularity (sync):
+//   tile  -- phase-2 tile q of chunk c waits for the flags of phase-1 tiles [q*ratio, (q+1)*ratio) of
+//            chunk c and clears them; the claim counter is cleared by the holder of the last ticket.
+//   chunk -- waits until done1[c] counts all t1 phase-1 tiles of chunk c.
+//   grid  -- waits until gdone1 counts every phase-1 tile of every chunk (one ticket counter).
+// In every mode the words return to zero by the end of the launch, so back-to-back launches on one
+// stream need no host reset.
 
-constexpr int kTwoShotU1 = 2;  // packs per lane per phase-1 tile
-constexpr int kTwoShotU2 = 8;  // packs per lane per phase-2 tile
-
-__device__ __forceinline__ uint32_t take_ticket(Ctrl* ctrl, uint32_t total) {
-  __shared__ uint32_t s_ticket;
+__device__ __forceinline__ void take_ticket(Ctrl* ctrl, const TwoShotPlan& pl, uint32_t& c, uint32_t& k) {
+  __shared__ uint32_t s_c, s_k;
   if (threadIdx.x == 0) {
-    const uint32_t t = __hip_atomic_fetch_add(&ctrl->claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == total - 1) __hip_atomic_store(&ctrl->claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_ticket = t;
-  }
-  __syncthreads();
-  return s_ticket;
-}
-
-__device__ __forceinline__ void release_phase1(Ctrl* ctrl) {
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(&ctrl->done1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void acquire_phase1(Ctrl* ctrl, uint32_t n1, uint32_t spin_limit) {
-  if (threadIdx.x == 0) {
-    uint32_t spins = 0;
-    while (__hip_atomic_load(&ctrl->done1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n1) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > spin_limit) {
-        __hip_atomic_fetch_or(&ctrl->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
+    const uint32_t per = pl.t1 + pl.t2;
+    if (pl.sync == kSyncGrid) {
+      const uint32_t g = __hip_atomic_fetch_add(&ctrl->gclaim[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (g == pl.chunks * per - 1) __hip_atomic_store(&ctrl->gclaim[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t n1 = pl.chunks * pl.t1;
+      if (g < n1) {
+        s_c = g / pl.t1;
+        s_k = g % pl.t1;
+      } else {  // phase-2 tiles take the chunks in reverse order
+        const uint32_t h = g - n1;
+        s_c = (pl.chunks - 1) - h / pl.t2;
+        s_k = pl.t1 + h % pl.t2;
       }
+    } else {
+      const uint32_t cc = blockIdx.x % pl.chunks;
+      const uint32_t t = __hip_atomic_fetch_add(&ctrl->claim[cc][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t == per - 1) __hip_atomic_store(&ctrl->claim[cc][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_c = cc;
+      s_k = t;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  c = s_c;
+  k = s_k;
+}
+
+__device__ __forceinline__ void publish_phase1(Ctrl* ctrl, uint32_t* flags, const TwoShotPlan& pl, uint32_t c, uint32_t k) {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's write-through stage stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (pl.sync == kSyncTile)
+      __hip_atomic_store(&flags[static_cast<size_t>(c) * pl.t1 + k], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else if (pl.sync == kSyncChunk)
+      __hip_atomic_fetch_add(&ctrl->done1[c][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_fetch_add(&ctrl->gdone1[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Thread 0 polls `word` until it reaches `target`; false if it gave up.
+__device__ __forceinline__ bool wait_at_least(uint32_t* word, uint32_t target, uint32_t spin_limit) {
+  uint32_t spins = 0;
+  while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > spin_limit) return false;
+  }
+  return true;
+}
+
+__device__ __forceinline__ void wait_phase1(Ctrl* ctrl, uint32_t* flags, const TwoShotPlan& pl, uint32_t c, uint32_t q) {
+  if (threadIdx.x == 0) {
+    bool ok = true;
+    if (pl.sync == kSyncTile) {
+      const uint32_t j0 = q * pl.ratio;
+      const uint32_t j1 = j0 + pl.ratio < pl.t1 ? j0 + pl.ratio : pl.t1;
+      for (uint32_t j = j0; j < j1; ++j) {
+        uint32_t* f = &flags[static_cast<size_t>(c) * pl.t1 + j];
+        ok = wait_at_least(f, 1u, pl.spin_limit) && ok;
+        __hip_atomic_store(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // consumed: re-arm
+      }
+    } else if (pl.sync == kSyncChunk) {
+      ok = wait_at_least(&ctrl->done1[c][0], pl.t1, pl.spin_limit);
+    } else {
+      ok = wait_at_least(&ctrl->gdone1[0], pl.chunks * pl.t1, pl.spin_limit);
+    }
+    if (!ok) __hip_atomic_fetch_or(&ctrl->err[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ void finish_phase2(Ctrl* ctrl, uint32_t n2) {
-  if (threadIdx.x == 0) {
-    const uint32_t d = __hip_atomic_fetch_add(&ctrl->done2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == n2 - 1) {
-      __hip_atomic_store(&ctrl->done1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ctrl->done2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void finish_phase2(Ctrl* ctrl, const TwoShotPlan& pl, uint32_t c) {
+  if (threadIdx.x != 0 || pl.sync == kSyncTile) return;
+  if (pl.sync == kSyncChunk) {
+    const uint32_t d = __hip_atomic_fetch_add(&ctrl->done2[c][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == pl.t2 - 1) {
+      __hip_atomic_store(&ctrl->done1[c][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctrl->done2[c][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    const uint32_t d = __hip_atomic_fetch_add(&ctrl->gdone2[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == pl.chunks * pl.t2 - 1) {
+      __hip_atomic_store(&ctrl->gdone1[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctrl->gdone2[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
+
+constexpr uint32_t kRatio = 4;  // phase-1 tiles per phase-2 tile
 
 template <typename D, int W>
-__global__ __launch_bounds__(kBlock) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
-                                                      ReduceShape sh, TwoShotPlan pl) {
-  const uint32_t t = take_ticket(ctrl, pl.n1 + pl.n2);
+__global__ __launch_bounds__(kRBlock) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
+                                                       uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
+  uint32_t c, k;
+  take_ticket(ctrl, pl, c, k);
   const size_t hb = sh.head * D::kSize;
-  if (t < pl.n1) {
-    const uint32_t c = t / pl.tiles1_per_chunk, k = t % pl.tiles1_per_chunk;
-    const size_t c0 = static_cast<size_t>(c) * pl.chunk_packs;
-    const size_t c1 = c0 + pl.chunk_packs < sh.npacks ? c0 + pl.chunk_packs : sh.npacks;
-    reduce_packs<D, W, kTwoShotU1>(in, sh.head, stage, c0 + static_cast<size_t>(k) * kBlock * kTwoShotU1, c1);
-    if (t == 0) reduce_edges<D, W>(in, stage, sh);
-    release_phase1(ctrl);
+  const size_t c0 = static_cast<size_t>(c) * pl.chunk_units;
+  const size_t cend = c0 + pl.chunk_units < sh.npacks ? c0 + pl.chunk_units : sh.npacks;
+  char* stage_body = stage + hb;
+  if (k < pl.t1) {
+    const size_t first = c0 + static_cast<size_t>(k) * kRBlock;
+    const size_t i = first + threadIdx.x;
+    if (i < cend) {
+      const u32x4 o = reduce_pack<D, W>(in, hb, i);
+      raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), make_rsrc(stage_body + first * 16, kRBlock * 16),
+                          threadIdx.x * 16, 0, kDeviceNT);
+    }
+    if (c == 0 && k == 0) reduce_edges<D, W, true>(in, stage, sh);
+    publish_phase1(ctrl, flags, pl, c, k);
   } else {
-    const uint32_t q = t - pl.n1;
-    acquire_phase1(ctrl, pl.n1, pl.spin_limit);
-    const uint32_t c = (pl.chunks - 1) - q / pl.tiles2_per_chunk, k = q % pl.tiles2_per_chunk;
-    const size_t c0 = static_cast<size_t>(c) * pl.chunk_packs;
-    const size_t c1 = c0 + pl.chunk_packs < sh.npacks ? c0 + pl.chunk_packs : sh.npacks;
-    copy_packs<kTwoShotU2>(stage, out, hb, c0 + static_cast<size_t>(k) * kBlock * kTwoShotU2, c1);
-    if (q == 0) copy_edges<D>(stage, out, sh);
-    finish_phase2(ctrl, pl.n2);
+    const uint32_t q = k - pl.t1;
+    wait_phase1(ctrl, flags, pl, c, q);
+    constexpr uint32_t kU = kRatio;
+    const size_t first = c0 + static_cast<size_t>(q) * (kRBlock * kU);
+    const i32x4 rs = make_rsrc(stage_body + first * 16, kRBlock * kU * 16);
+    u32x4 v[kU];
+#pragma unroll
+    for (uint32_t u = 0; u < kU; ++u) {
+      const size_t i = first + u * kRBlock + threadIdx.x;
+      if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, (u * kRBlock + threadIdx.x) * 16, 0, kDeviceNT));
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kU; ++u) {
+      const size_t i = first + u * kRBlock + threadIdx.x;
+      if (i < cend) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + hb) + i);
+    }
+    if (c == 0 && q == 0) copy_edges_from_stage<D>(stage, out, sh);
+    finish_phase2(ctrl, pl, c);
   }
 }
 
-// Element-wise two-shot for pointers that do not share one 16-byte alignment (V = 1).
+// Element-wise two-shot for pointers that do not share one 16-byte alignment (one element per unit).
 template <typename D, int W>
 __global__ __launch_bounds__(kBlock) void twoshot_elem(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
-                                                       ReduceShape sh, TwoShotPlan pl) {
-  const uint32_t t = take_ticket(ctrl, pl.n1 + pl.n2);
-  if (t < pl.n1) {
-    const uint32_t c = t / pl.tiles1_per_chunk, k = t % pl.tiles1_per_chunk;
-    const size_t c0 = static_cast<size_t>(c) * pl.chunk_packs;
-    const size_t c1 = c0 + pl.chunk_packs < sh.n ? c0 + pl.chunk_packs : sh.n;
-    const size_t first = c0 + static_cast<size_t>(k) * kBlock * kTwoShotU1;
-#pragma unroll
-    for (int u = 0; u < kTwoShotU1; ++u) {
-      const size_t e = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
-      if (e < c1) reduce_elem<D, W>(in, stage, e);
-    }
-    release_phase1(ctrl);
+                                                       uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
+  uint32_t c, k;
+  take_ticket(ctrl, pl, c, k);
+  const size_t c0 = static_cast<size_t>(c) * pl.chunk_units;
+  const size_t cend = c0 + pl.chunk_units < sh.n ? c0 + pl.chunk_units : sh.n;
+  if (k < pl.t1) {
+    const size_t e = c0 + static_cast<size_t>(k) * kBlock + threadIdx.x;
+    if (e < cend) reduce_elem<D, W, true>(in, stage, e);
+    publish_phase1(ctrl, flags, pl, c, k);
   } else {
-    const uint32_t q = t - pl.n1;
-    acquire_phase1(ctrl, pl.n1, pl.spin_limit);
-    const uint32_t c = (pl.chunks - 1) - q / pl.tiles2_per_chunk, k = q % pl.tiles2_per_chunk;
-    const size_t c0 = static_cast<size_t>(c) * pl.chunk_packs;
-    const size_t c1 = c0 + pl.chunk_packs < sh.n ? c0 + pl.chunk_packs : sh.n;
-    const size_t first = c0 + static_cast<size_t>(k) * kBlock * kTwoShotU2;
+    const uint32_t q = k - pl.t1;
+    wait_phase1(ctrl, flags, pl, c, q);
+    const size_t first = c0 + static_cast<size_t>(q) * (kBlock * kRatio);
 #pragma unroll
-    for (int u = 0; u < kTwoShotU2; ++u) {
-      const size_t e = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
-      if (e < c1) {
+    for (uint32_t u = 0; u < kRatio; ++u) {
+      const size_t e = first + u * kBlock + threadIdx.x;
+      if (e < cend) {
         const size_t off = e * D::kSize;
-        if (D::kSize == 2)
-          *reinterpret_cast<uint16_t*>(out + off) = *reinterpret_cast<const uint16_t*>(stage + off);
-        else
-          *reinterpret_cast<uint32_t*>(out + off) = *reinterpret_cast<const uint32_t*>(stage + off);
+        store_bits<D::kSize, false>(out + off, load_bits<D::kSize, true>(stage + off));
       }
     }
-    finish_phase2(ctrl, pl.n2);
+    finish_phase2(ctrl, pl, c);
   }
 }
 
-__global__ void zero_ctrl(Ctrl* ctrl) {
-  reinterpret_cast<uint32_t*>(ctrl)[threadIdx.x] = 0u;
+__global__ void zero_words(uint32_t* p, size_t words) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
 }
 
 // ------------------------------------------------------------------------------------- dispatch
 
-constexpr size_t kMaxGrid = size_t(1) << 22;  // workgroups; beyond this the one-shot kernels grid-stride
+constexpr size_t kMaxGrid = size_t(1) << 20;  // workgroups; beyond this the one-shot kernels grid-stride
 
 template <typename D, int W>
 hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
   if (sh.vec) {
-    const size_t tile = static_cast<size_t>(kBlock) * kOneShotU;
-    const size_t ntiles = (sh.npacks + tile - 1) / tile;
+    const size_t ntiles = (sh.npacks + kRBlock - 1) / kRBlock;
     size_t grid = ntiles < kMaxGrid ? ntiles : kMaxGrid;
     if (grid == 0) grid = 1;  // edges only
-    hipLaunchKernelGGL((oneshot_vec<D, W>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, st, in, out, sh, ntiles);
+    hipLaunchKernelGGL((oneshot_vec<D, W>), dim3(static_cast<unsigned>(grid)), dim3(kRBlock), 0, st, in, out, sh, ntiles);
   } else {
     const size_t need = (sh.n + kBlock - 1) / kBlock;
     const size_t grid = need < kMaxGrid ? need : kMaxGrid;
@@ -348,18 +421,18 @@ hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, hipSt
 }
 
 template <typename D, int W>
-hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, const ReduceShape& sh,
+hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uint32_t* flags, const ReduceShape& sh,
                      const TwoShotPlan& pl, hipStream_t st) {
-  const unsigned grid = pl.n1 + pl.n2;
+  const unsigned grid = pl.chunks * (pl.t1 + pl.t2);
   if (sh.vec)
-    hipLaunchKernelGGL((twoshot_vec<D, W>), dim3(grid), dim3(kBlock), 0, st, in, out, stage, ctrl, sh, pl);
+    hipLaunchKernelGGL((twoshot_vec<D, W>), dim3(grid), dim3(kRBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
   else
-    hipLaunchKernelGGL((twoshot_elem<D, W>), dim3(grid), dim3(kBlock), 0, st, in, out, stage, ctrl, sh, pl);
+    hipLaunchKernelGGL((twoshot_elem<D, W>), dim3(grid), dim3(kBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
   return hipGetLastError();
 }
 
-#define MR_W_CASES(F, D, ...)       \
-  switch (W) {                      \
+#define MR_W_CASES(F, D, ...)              \
+  switch (W) {                             \
     case 1: return F<D, 1>(__VA_ARGS__);   \
     case 2: return F<D, 2>(__VA_ARGS__);   \
     case 3: return F<D, 3>(__VA_ARGS__);   \
@@ -385,9 +458,9 @@ hipError_t oneshot_d(const RankPtrs& in, int W, char* out, const ReduceShape& sh
 }
 
 template <typename D>
-hipError_t twoshot_d(const RankPtrs& in, int W, char* out, char* stage, Ctrl* ctrl, const ReduceShape& sh,
-                     const TwoShotPlan& pl, hipStream_t st) {
-  MR_W_CASES(twoshot_w, D, in, out, stage, ctrl, sh, pl, st)
+hipError_t twoshot_d(const RankPtrs& in, int W, char* out, char* stage, Ctrl* ctrl, uint32_t* flags,
+                     const ReduceShape& sh, const TwoShotPlan& pl, hipStream_t st) {
+  MR_W_CASES(twoshot_w, D, in, out, stage, ctrl, flags, sh, pl, st)
 }
 
 }  // namespace
@@ -403,41 +476,43 @@ hipError_t launch_oneshot(const RankPtrs& in, int W, mr_dtype dt, char* out, con
 }
 
 hipError_t launch_twoshot(const RankPtrs& in, int W, mr_dtype dt, char* out, char* stage, Ctrl* ctrl,
-                          const ReduceShape& sh, const TwoShotPlan& pl, hipStream_t st) {
+                          uint32_t* flags, const ReduceShape& sh, const TwoShotPlan& pl, hipStream_t st) {
   switch (dt) {
-    case MR_BF16: return twoshot_d<Bf16>(in, W, out, stage, ctrl, sh, pl, st);
-    case MR_FP16: return twoshot_d<Fp16>(in, W, out, stage, ctrl, sh, pl, st);
-    case MR_FP32: return twoshot_d<Fp32>(in, W, out, stage, ctrl, sh, pl, st);
+    case MR_BF16: return twoshot_d<Bf16>(in, W, out, stage, ctrl, flags, sh, pl, st);
+    case MR_FP16: return twoshot_d<Fp16>(in, W, out, stage, ctrl, flags, sh, pl, st);
+    case MR_FP32: return twoshot_d<Fp32>(in, W, out, stage, ctrl, flags, sh, pl, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Chunk c holds ceil(units / W) consecutive 16-byte packs of the body (elements on the element-wise
-// path), so every chunk boundary is 16-byte aligned and, when n is a multiple of the pack, chunk c is
-// exactly elements [c*C, (c+1)*C) with C = ceil(n/W) rounded up to a whole pack.  The last chunks may
-// be short or empty.  The few elements outside the body (an unaligned head, a tail shorter than a
-// pack) ride with the first tile of each phase.
-TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t spin_limit) {
+// Chunk c holds ceil(units / W) consecutive units: 16-byte packs of the body (elements on the
+// element-wise path).  When n is a multiple of the pack, chunk c is exactly elements [c*C, (c+1)*C)
+// with C = ceil(n/W) rounded up to a whole pack, so every chunk boundary is 16-byte aligned; the last
+// chunks may be short or empty.  The few elements outside the body (an unaligned head, a tail shorter
+// than a pack) ride with phase-1 tile 0 and phase-2 tile 0 of chunk 0.
+TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit) {
   TwoShotPlan pl{};
   pl.chunks = static_cast<uint32_t>(W);
   const size_t units = sh.vec ? sh.npacks : sh.n;
-  pl.chunk_packs = (units + W - 1) / W;
-  const size_t t1 = static_cast<size_t>(kBlock) * kTwoShotU1;
-  const size_t t2 = static_cast<size_t>(kBlock) * kTwoShotU2;
-  size_t tiles1 = (pl.chunk_packs + t1 - 1) / t1;
-  size_t tiles2 = (pl.chunk_packs + t2 - 1) / t2;
-  if (tiles1 == 0) tiles1 = 1;  // an edges-only call still needs one tile of each phase
-  if (tiles2 == 0) tiles2 = 1;
-  pl.tiles1_per_chunk = static_cast<uint32_t>(tiles1);
-  pl.tiles2_per_chunk = static_cast<uint32_t>(tiles2);
-  pl.n1 = static_cast<uint32_t>(tiles1 * W);
-  pl.n2 = static_cast<uint32_t>(tiles2 * W);
+  pl.chunk_units = (units + W - 1) / W;
+  pl.unit1 = sh.vec ? kRBlock : kBlock;
+  pl.ratio = kRatio;
+  pl.unit2 = pl.unit1 * kRatio;
+  size_t t1 = (pl.chunk_units + pl.unit1 - 1) / pl.unit1;
+  if (t1 == 0) t1 = 1;  // an edges-only call still has one tile of each phase
+  const size_t t2 = (t1 + kRatio - 1) / kRatio;
+  pl.t1 = static_cast<uint32_t>(t1);
+  pl.t2 = static_cast<uint32_t>(t2);
+  pl.sync = sync;
   pl.spin_limit = spin_limit;
   return pl;
 }
 
-hipError_t launch_zero_ctrl(Ctrl* ctrl, hipStream_t st) {
-  hipLaunchKernelGGL(zero_ctrl, dim3(1), dim3(kCtrlBytes / 4), 0, st, ctrl);
+hipError_t launch_zero_words(void* p, size_t words, hipStream_t st) {
+  if (words == 0) return hipSuccess;
+  size_t grid = (words + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, static_cast<uint32_t*>(p), words);
   return hipGetLastError();
 }
 

@@ -144,17 +144,21 @@ def main():
         ms_w = time_steps(one[:1], K, args.warmup, stream)
         paths["oneshot_cache_resident"] = {"us": ms_w / K * 1e3, "GBps_algorithmic": algo / (ms_w / K * 1e-3) / 1e9,
                                            "note": "one buffer set reused; served partly from cache, not HBM"}
-        # two-shot, rotating sets
+        # two-shot, rotating sets, under each phase hand-off
         two = [mr.prepare_allreduce(b, o, "twoshot") for b, o in sets]
-        two[0]()
-        torch.cuda.synchronize()
-        ms2 = time_steps(two, K, args.warmup, stream)
-        t2 = ms2 / K * 1e-3
         actual2 = (W + 3) * n * s
-        paths["twoshot"] = {"us": t2 * 1e6, "GBps_metric_bytes": algo / t2 / 1e9, "GBps_actual_bytes": actual2 / t2 / 1e9,
-                            "actual_bytes": actual2, "barrier_error_word": mr.workspace_check()}
-        log(f"[bench] twoshot: {t2 * 1e6:.2f} us/launch, {algo / t2 / 1e9:.1f} GB/s (metric bytes), "
-            f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")
+        for sync in ("tile", "chunk", "grid"):
+            mr.set_option("twoshot_sync", sync)
+            two[0]()
+            torch.cuda.synchronize()
+            ms2 = time_steps(two, K, args.warmup, stream)
+            t2 = ms2 / K * 1e-3
+            paths[f"twoshot_{sync}"] = {"us": t2 * 1e6, "GBps_metric_bytes": algo / t2 / 1e9,
+                                        "GBps_actual_bytes": actual2 / t2 / 1e9, "actual_bytes": actual2,
+                                        "barrier_error_word": mr.workspace_check()}
+            log(f"[bench] twoshot ({sync}): {t2 * 1e6:.2f} us/launch, {algo / t2 / 1e9:.1f} GB/s (metric bytes), "
+                f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")
+        mr.set_option("twoshot_sync", "tile")
         # param-contiguous scatter: W=8, G=4, P=64 log-uniform splits, bf16 random bits
         c4 = workloads.CONFIG4
         splits = [int(x) for x in workloads.log_uniform_splits(c4["cfg"], c4["P"])]

@@ -116,9 +116,12 @@ mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, co
  *
  * mr_workspace_bytes: bytes a caller-owned workspace needs for a two-shot call of this shape.
  * mr_set_workspace:   bind caller-owned device memory (256-byte aligned) as the workspace of `stream`
- *                     on the current device, replacing any library-owned one; the barrier words are
- *                     cleared on `stream` here.  dev_ptr == NULL unbinds (the library allocates
- *                     again on next use).  Not thread-safe against concurrent calls on that stream.
+ *                     on the current device, replacing any library-owned one; the barrier words and
+ *                     flags are cleared on `stream` here.  Memory too small to hold them plus some
+ *                     stage -> MR_ERR_INVALID_ARG; a bound workspace too small for a later call makes
+ *                     that call return MR_ERR_WORKSPACE.  dev_ptr == NULL unbinds (the library
+ *                     allocates again on next use).  Not thread-safe against concurrent calls on that
+ *                     stream.
  * mr_workspace_check: synchronises `stream`, then reads and clears the barrier error word of its
  *                     workspace.  *flags receives it (0 = no error; bit 0 = a phase-2 block gave up
  *                     waiting for phase 1, so that call's output is not valid).  Returns
@@ -127,6 +130,28 @@ mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, co
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype);
 mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes);
 mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
+
+/*
+ * Process-wide options (thread-safe; they apply to calls made after the change).
+ *
+ * MR_OPT_TWOSHOT_SYNC  how a two-shot phase-2 tile waits for phase 1 (all give identical results):
+ *   MR_TWOSHOT_SYNC_TILE  (default) per-tile producer flags: a phase-2 tile waits only for the
+ *                         phase-1 tiles it copies (the per-block flag hand-off of the custom
+ *                         allreduce page's block_barrier, applied to the two phases);
+ *   MR_TWOSHOT_SYNC_CHUNK per-chunk barrier: waits for every phase-1 tile of its 1/W chunk;
+ *   MR_TWOSHOT_SYNC_GRID  grid barrier: waits for every phase-1 tile of every chunk.
+ * MR_OPT_SPIN_LIMIT    polls a waiting workgroup makes before it gives up and sets the workspace error
+ *                      word (see mr_workspace_check); default 2^22.  A value of 0 makes every wait
+ *                      that is not already satisfied give up at once (for testing error handling).
+ * Unknown options or out-of-range values -> MR_ERR_INVALID_ARG.  Environment variables
+ * MR_TWOSHOT_SYNC and MR_SPIN_LIMIT set the initial values when the library loads.
+ */
+typedef enum mr_option { MR_OPT_TWOSHOT_SYNC = 0, MR_OPT_SPIN_LIMIT = 1 } mr_option;
+#define MR_TWOSHOT_SYNC_TILE 0
+#define MR_TWOSHOT_SYNC_CHUNK 1
+#define MR_TWOSHOT_SYNC_GRID 2
+mr_status mr_set_option(mr_option opt, int64_t value);
+mr_status mr_get_option(mr_option opt, int64_t* value);
 
 /* Library ABI version (major*100 + minor). */
 int mr_version(void);

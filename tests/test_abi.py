@@ -104,15 +104,32 @@ def test_gather_argument_errors(L):
 
 
 def test_workspace_sizes_and_errors(L):
-    assert L.mr_workspace_bytes(8, 0, 0) >= 1024
+    assert L.mr_workspace_bytes(8, 0, 0) >= 16384
     b = L.mr_workspace_bytes(8, 8_388_608, 0)
-    assert b >= 1024 + 8_388_608 * 2 and b % 256 == 0
-    assert L.mr_workspace_bytes(8, 1000, 2) >= 1024 + 4000
+    assert 16384 + 8_388_608 * 2 < b < 1.05 * 8_388_608 * 2 + 65536 and b % 256 == 0
+    assert L.mr_workspace_bytes(8, 1000, 2) >= 16384 + 4000
     assert L.mr_workspace_bytes(0, 1000, 0) == 0
     assert L.mr_workspace_bytes(8, 1000, 3) == 0
     assert L.mr_set_workspace(None, 0x100010, 1 << 20) == EINVAL      # not 256-byte aligned
     assert L.mr_set_workspace(None, 0x100000, 16) == EINVAL           # smaller than the barrier words
+    assert L.mr_set_workspace(None, 0x100000, 16384) == EINVAL        # no room for flags and stage
     assert L.mr_workspace_check(None, None) == EINVAL
+
+
+def test_options_validate_and_round_trip(L):
+    v = ctypes.c_int64(-7)
+    assert L.mr_get_option(0, ctypes.byref(v)) == OK and v.value == 0          # tile flags by default
+    assert L.mr_get_option(1, ctypes.byref(v)) == OK and v.value == 1 << 22
+    assert L.mr_set_option(0, 3) == EINVAL and L.mr_set_option(0, -1) == EINVAL
+    assert L.mr_set_option(1, -1) == EINVAL and L.mr_set_option(1, 2 ** 32) == EINVAL
+    assert L.mr_set_option(9, 0) == EINVAL and L.mr_get_option(9, ctypes.byref(v)) == EINVAL
+    assert L.mr_get_option(0, None) == EINVAL
+    for sync in ("chunk", "grid", "tile"):
+        mr.set_option("twoshot_sync", sync)
+        assert mr.get_option("twoshot_sync") == sync
+    mr.set_option("spin_limit", 1000)
+    assert mr.get_option("spin_limit") == 1000
+    mr.set_option("spin_limit", 1 << 22)
 
 
 def test_binding_rejects_host_tensors():

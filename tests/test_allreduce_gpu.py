@@ -11,13 +11,25 @@ import workloads
 from gpu_util import TORCH_DT, assert_reduce_equal, device, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
-MODES = ("oneshot", "twoshot")
+# one-shot, and two-shot under each phase hand-off (per-tile flags, per-chunk barrier, grid barrier)
+MODES = ("oneshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid")
+
+
+def _call(dbufs, out, mode):
+    kind, _, sync = mode.partition(":")
+    if sync:
+        mr.set_option("twoshot_sync", sync)
+    try:
+        mr.allreduce_sum(dbufs, out, mode=kind)
+    finally:
+        if sync:
+            mr.set_option("twoshot_sync", "tile")
 
 
 def _run(dbufs, dtype, n, mode, out=None):
     if out is None:
         out = torch.empty(n, dtype=TORCH_DT[dtype], device=device())
-    mr.allreduce_sum(dbufs, out, mode=mode)
+    _call(dbufs, out, mode)
     torch.cuda.synchronize()
     return out
 
@@ -81,7 +93,7 @@ def test_in_place_out_is_an_input():
     for mode in MODES:
         for k in (0, 5):
             dbufs = [to_dev(b, "bf16") for b in bufs]
-            mr.allreduce_sum(dbufs, dbufs[k], mode=mode)
+            _call(dbufs, dbufs[k], mode)
             torch.cuda.synchronize()
             assert_reduce_equal(to_bits(dbufs[k]), want, "bf16", f"in place k={k} {mode}")
 
@@ -108,7 +120,7 @@ def test_unaligned_views(dtype):
         for mode in MODES:
             outbuf = torch.empty(n + 16, dtype=TORCH_DT[dtype], device=device())
             out = outbuf[off:off + n]
-            mr.allreduce_sum(views, out, mode=mode)
+            _call(views, out, mode)
             torch.cuda.synchronize()
             assert_reduce_equal(to_bits(out), want, dtype, f"same phase off={off} {mode}")
     # (b) pointers with different 16-byte phases: element-wise path
@@ -126,42 +138,87 @@ def test_oneshot_equals_twoshot_and_is_deterministic():
     dbufs = [to_dev(b, "bf16") for b in bufs]
     ref = to_bits(_run(dbufs, "bf16", n, "oneshot"))
     out = torch.empty(n, dtype=torch.bfloat16, device=device())
-    for i in range(50):
-        mode = MODES[i % 2]
-        mr.allreduce_sum(dbufs, out, mode=mode)
+    for i in range(60):
+        mode = MODES[i % len(MODES)]
+        _call(dbufs, out, mode)
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(out), ref), f"launch {i} ({mode}) differs"
     assert mr.workspace_check() == 0
 
 
-def test_twoshot_poisoned_stage_caller_workspace():
-    """The stage is refilled with NaN bits before every launch, so a phase-2 copy that ran ahead of
-    phase 1 would surface as a mismatch."""
+@pytest.mark.parametrize("sync", ["tile", "chunk", "grid"])
+def test_twoshot_stale_stage_is_never_read(sync):
+    """Two input sets alternate on one caller-owned workspace, so when a call starts its stage still
+    holds the previous call's (different) sums: a phase-2 copy that ran ahead of its phase-1 producer
+    would surface as a mismatch."""
     W, n = 8, 4_194_304 + 24
-    bufs = workloads.rank_buffers(15, W, n, "bf16", "normal")
-    want = oracle.allreduce_sum_ref(bufs, "bf16")
-    dbufs = [to_dev(b, "bf16") for b in bufs]
-    nbytes = mr.workspace_bytes(W, n, "bf16")
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=device())
+    sets = [workloads.rank_buffers(15 + k, W, n, "bf16", "normal") for k in range(2)]
+    wants = [oracle.allreduce_sum_ref(b, "bf16") for b in sets]
+    dsets = [[to_dev(b, "bf16") for b in s] for s in sets]
+    ws = torch.empty(mr.workspace_bytes(W, n, "bf16"), dtype=torch.uint8, device=device())
     mr.set_workspace(ws)
+    mr.set_option("twoshot_sync", sync)
     try:
-        out = torch.empty(n, dtype=torch.bfloat16, device=device())
+        outs = [torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(2)]
         for i in range(200):
-            ws[1024:].fill_(0xFF)
-            out.fill_(0)
-            mr.allreduce_sum(dbufs, out, mode="twoshot")
-            if i % 20 == 0 or i == 199:
+            k = i % 2
+            outs[k].fill_(0)
+            mr.allreduce_sum(dsets[k], outs[k], mode="twoshot")
+            if i % 20 in (0, 1) or i >= 198:
                 torch.cuda.synchronize()
-                assert_reduce_equal(to_bits(out), want, "bf16", f"poisoned launch {i}")
+                assert_reduce_equal(to_bits(outs[k]), wants[k], "bf16", f"{sync} launch {i}")
         assert mr.workspace_check() == 0
-        # a caller workspace that is too small is refused
-        small = torch.empty(4096, dtype=torch.uint8, device=device())
-        mr.set_workspace(small)
+    finally:
+        mr.set_option("twoshot_sync", "tile")
+        mr.set_workspace(None)
+
+
+def test_caller_workspace_too_small():
+    W, n = 8, 1_000_000
+    bufs = [to_dev(b, "bf16") for b in workloads.rank_buffers(17, W, n, "bf16", "uniform")]
+    out = torch.empty(n, dtype=torch.bfloat16, device=device())
+    with pytest.raises(mr.MRError) as ei:  # cannot even hold the barrier words
+        mr.set_workspace(torch.empty(4096, dtype=torch.uint8, device=device()))
+    assert ei.value.status == -1
+    small = torch.empty(1 << 16, dtype=torch.uint8, device=device())
+    mr.set_workspace(small)
+    try:
         with pytest.raises(mr.MRError) as ei:
-            mr.allreduce_sum(dbufs, out, mode="twoshot")
+            mr.allreduce_sum(bufs, out, mode="twoshot")
         assert ei.value.status == -4
     finally:
         mr.set_workspace(None)
+    mr.allreduce_sum(bufs, out, mode="twoshot")  # library-owned workspace again
+    torch.cuda.synchronize()
+    assert mr.workspace_check() == 0
+
+
+def test_bounded_wait_reports_and_recovers():
+    """With a spin limit of 0, a grid-barrier phase-2 workgroup that starts while the last phase-1
+    tiles still run gives up at its first poll: the call finishes, the workspace error word says so,
+    mr_workspace_check clears it, and the next call is correct."""
+    W, n = 8, 8_388_608
+    bufs = workloads.rank_buffers(18, W, n, "bf16", "normal")
+    want = oracle.allreduce_sum_ref(bufs, "bf16")
+    dbufs = [to_dev(b, "bf16") for b in bufs]
+    out = torch.empty(n, dtype=torch.bfloat16, device=device())
+    mr.allreduce_sum(dbufs, out, mode="twoshot")  # a library-owned workspace exists and is clean
+    assert mr.workspace_check() == 0
+    mr.set_option("twoshot_sync", "grid")
+    mr.set_option("spin_limit", 0)
+    try:
+        mr.allreduce_sum(dbufs, out, mode="twoshot")
+        flags = mr.workspace_check()
+    finally:
+        mr.set_option("spin_limit", 1 << 22)
+        mr.set_option("twoshot_sync", "tile")
+    assert flags & 1, "a phase-2 wait should have given up"
+    for mode in ("twoshot:tile", "twoshot:grid"):
+        out.fill_(0)
+        _call(dbufs, out, mode)
+        torch.cuda.synchronize()
+        assert_reduce_equal(to_bits(out), want, "bf16", f"after recovery {mode}")
+    assert mr.workspace_check() == 0
 
 
 def test_twoshot_on_two_streams_concurrently():
@@ -172,10 +229,10 @@ def test_twoshot_on_two_streams_concurrently():
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = [torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(2)]
     torch.cuda.synchronize()
-    for rep in range(20):
+    for rep in range(30):
         for k in range(2):
             with torch.cuda.stream(streams[k]):
-                mr.allreduce_sum(dsets[k], outs[k], mode="twoshot")
+                _call(dsets[k], outs[k], MODES[1 + rep % 3])
     torch.cuda.synchronize()
     for k in range(2):
         assert_reduce_equal(to_bits(outs[k]), wants[k], "bf16", f"stream {k}")
@@ -195,7 +252,7 @@ def test_cross_stream_consumer_waits_on_event():
         torch.cuda.synchronize()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            mr.allreduce_sum(dbufs, out, mode="twoshot" if rep % 2 else "oneshot")
+            _call(dbufs, out, MODES[rep % len(MODES)])
             ev = torch.cuda.Event()
             ev.record(side)
         torch.cuda.current_stream().wait_event(ev)
