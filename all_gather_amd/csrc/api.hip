@@ -53,8 +53,9 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Smallest workspace whose layout (barrier words, flag capacity bytes/256 words, stage) holds a stage
-// of n elements plus 16 bytes of alignment slack.
+// Smallest workspace whose layout (barrier words, flags, stage) holds a stage of n elements plus 16
+// bytes of alignment slack.  Its flag capacity (bytes/256 words) covers the largest plan for n: one
+// flag per 256-element tile on the element-wise path, plus one per chunk for ragged chunks.
 size_t ws_bytes_for(size_t n, int esize) {
   const size_t base = mr::kCtrlBytes + n * static_cast<size_t>(esize) + 16 + 256;
   return round_up(base + base / 63 + 4096, 4096);
@@ -90,6 +91,7 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
   }
   void* p = nullptr;
   const size_t bytes = round_up(ws_bytes_for(n, esize), size_t(1) << 20);
+  if (!ws_fits(bytes, n, esize, flags)) return MR_ERR_WORKSPACE;  // the sizing rule covers every plan
   e = hipMalloc(&p, bytes);
   if (e != hipSuccess) return hip_fail(e);
   e = ws_clear(static_cast<char*>(p), bytes, st);
@@ -251,7 +253,7 @@ mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_
       a.O[i] = base;
       a.tile_prefix[i] = static_cast<uint32_t>(tiles);
       const uint64_t E = splits[s0 + i];
-      tiles += static_cast<uint64_t>(G) * ((E * es + mr::kGatherTileBytes - 1) / mr::kGatherTileBytes);
+      tiles += static_cast<uint64_t>(G) * mr::gather_tiles_per_segment(E, static_cast<uint32_t>(es));
       base += E;
       if (tiles >= (1ull << 31)) return MR_ERR_INVALID_ARG;
     }

@@ -17,7 +17,8 @@ inline int elem_size(mr_dtype d) { return (d == MR_BF16 || d == MR_FP16) ? 2 : 4
 // ------------------------------------------------------------------------------- two-shot workspace
 //
 //   [0, 16 KiB)                 Ctrl: ticket counters and barrier words, one 256-byte line each
-//   [16 KiB, stage_off)         producer flags, one u32 per phase-1 tile (capacity bytes/1024 tiles)
+//   [16 KiB, stage_off)         producer flags, one u32 per phase-1 tile (capacity bytes/256 tiles,
+//                               enough for the element-wise path's one tile per 256 elements)
 //   [stage_off, bytes)          stage buffer (n elements + 16 bytes of alignment slack)
 // Every word before stage_off is zero between calls; the calls restore that themselves.
 constexpr size_t kCtrlBytes = 16384;
@@ -33,7 +34,7 @@ struct Ctrl {
 };
 static_assert(sizeof(Ctrl) <= kCtrlBytes, "ctrl layout");
 
-inline size_t ws_flag_words(size_t bytes) { return bytes >> 10; }
+inline size_t ws_flag_words(size_t bytes) { return bytes >> 8; }
 inline size_t ws_stage_offset(size_t bytes) {
   return kCtrlBytes + ((ws_flag_words(bytes) * 4 + 255) & ~size_t(255));
 }
@@ -82,7 +83,18 @@ hipError_t launch_zero_words(void* p, size_t words, hipStream_t st);
 
 // ---------------------------------------------------------------------------------- param-contiguous
 constexpr int kMaxParams = MR_MAX_PARAMS_PER_LAUNCH;
-constexpr uint32_t kGatherTileBytes = 16384;
+#ifndef MR_GATHER_TILE
+#define MR_GATHER_TILE 16384
+#endif
+#ifndef MR_GATHER_BLOCK
+#define MR_GATHER_BLOCK 512
+#endif
+#ifndef MR_GATHER_LINE
+#define MR_GATHER_LINE 256
+#endif
+constexpr uint32_t kGatherTileBytes = MR_GATHER_TILE;  // bytes per tile (one workgroup)
+constexpr int kGatherBlock = MR_GATHER_BLOCK;          // lanes per gather workgroup
+constexpr uint32_t kGatherLine = MR_GATHER_LINE;       // tile boundaries fall on destination lines of this size (1: off)
 
 struct GatherArgs {
   const char* src;
@@ -98,5 +110,6 @@ struct GatherArgs {
 };
 
 hipError_t launch_param_contig(const GatherArgs& a, hipStream_t st);
+uint64_t gather_tiles_per_segment(uint64_t E, uint32_t elem);
 
 }  // namespace mr

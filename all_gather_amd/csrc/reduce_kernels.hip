@@ -23,9 +23,22 @@ __device__ i32x4 raw_buffer_load_v4(i32x4 rsrc, int voffset, int soffset, int au
 __device__ void raw_buffer_store_v4(i32x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 
-// Cache policy: sc1 (device-scope coherence: stores write through the XCD's L2, loads do not hit a
-// line another XCD may have changed) plus nt (streaming).
-constexpr int kDeviceNT = (1 << 4) | (1 << 1);
+// Cache policy of the stage accesses: sc1, device-scope coherence (stores write through the XCD's
+// L2, loads do not return a line another XCD may have changed).  Adding nt measured 2-3% slower.
+#ifndef MR_TS_STORE_AUX
+#define MR_TS_STORE_AUX (1 << 4)
+#endif
+#ifndef MR_TS_LOAD_AUX
+#define MR_TS_LOAD_AUX (1 << 4)
+#endif
+#ifndef MR_TS_U1
+#define MR_TS_U1 1
+#endif
+#ifndef MR_TS_RATIO
+#define MR_TS_RATIO 4
+#endif
+constexpr int kStageStoreAux = MR_TS_STORE_AUX;
+constexpr int kStageLoadAux = MR_TS_LOAD_AUX;
 
 // Buffer resource for `bytes` bytes at `base` (raw, stride 0; gfx9 data-format word).
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
@@ -165,6 +178,37 @@ __device__ __forceinline__ u32x4 reduce_pack(const RankPtrs& in, size_t hb, size
   return D::narrow(acc);
 }
 
+// U packs per lane (pack i = first + u*kRBlock + lane, i < end), all W*U loads issued before the
+// first add, each result stored through `st(u, pack)`.
+template <typename D, int W, int U, typename Store>
+__device__ __forceinline__ void reduce_packs(const RankPtrs& in, size_t hb, size_t first, size_t end, Store st) {
+  u32x4 v[U][W];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const size_t i = first + static_cast<size_t>(u) * kRBlock + threadIdx.x;
+    if (i < end) {
+#pragma unroll
+      for (int r = 0; r < W; ++r) v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const size_t i = first + static_cast<size_t>(u) * kRBlock + threadIdx.x;
+    if (i < end) {
+      float acc[D::V];
+      D::widen(v[u][0], acc);
+#pragma unroll
+      for (int r = 1; r < W; ++r) {
+        float t[D::V];
+        D::widen(v[u][r], t);
+#pragma unroll
+        for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
+      }
+      st(u, D::narrow(acc));
+    }
+  }
+}
+
 // Elements outside the 16-byte body: [0, head) and [head + npacks*V, n).  At most 2V-2 of them.
 template <typename D, int W, bool Dev>
 __device__ __forceinline__ void reduce_edges(const RankPtrs& in, char* dst, const ReduceShape& sh) {
@@ -287,21 +331,18 @@ __device__ __forceinline__ bool wait_at_least(uint32_t* word, uint32_t target, u
 }
 
 __device__ __forceinline__ void wait_phase1(Ctrl* ctrl, uint32_t* flags, const TwoShotPlan& pl, uint32_t c, uint32_t q) {
-  if (threadIdx.x == 0) {
-    bool ok = true;
-    if (pl.sync == kSyncTile) {
-      const uint32_t j0 = q * pl.ratio;
-      const uint32_t j1 = j0 + pl.ratio < pl.t1 ? j0 + pl.ratio : pl.t1;
-      for (uint32_t j = j0; j < j1; ++j) {
-        uint32_t* f = &flags[static_cast<size_t>(c) * pl.t1 + j];
-        ok = wait_at_least(f, 1u, pl.spin_limit) && ok;
-        __hip_atomic_store(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // consumed: re-arm
-      }
-    } else if (pl.sync == kSyncChunk) {
-      ok = wait_at_least(&ctrl->done1[c][0], pl.t1, pl.spin_limit);
-    } else {
-      ok = wait_at_least(&ctrl->gdone1[0], pl.chunks * pl.t1, pl.spin_limit);
+  if (pl.sync == kSyncTile) {
+    // lanes 0..ratio-1 of the first wave each wait for one producer flag, so the waits overlap
+    const uint32_t j = q * pl.ratio + threadIdx.x;
+    if (threadIdx.x < pl.ratio && j < pl.t1) {
+      uint32_t* f = &flags[static_cast<size_t>(c) * pl.t1 + j];
+      if (!wait_at_least(f, 1u, pl.spin_limit))
+        __hip_atomic_fetch_or(&ctrl->err[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // consumed: re-arm
     }
+  } else if (threadIdx.x == 0) {
+    const bool ok = pl.sync == kSyncChunk ? wait_at_least(&ctrl->done1[c][0], pl.t1, pl.spin_limit)
+                                          : wait_at_least(&ctrl->gdone1[0], pl.chunks * pl.t1, pl.spin_limit);
     if (!ok) __hip_atomic_fetch_or(&ctrl->err[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
@@ -324,7 +365,10 @@ __device__ __forceinline__ void finish_phase2(Ctrl* ctrl, const TwoShotPlan& pl,
   }
 }
 
-constexpr uint32_t kRatio = 4;  // phase-1 tiles per phase-2 tile
+constexpr uint32_t kRatio = MR_TS_RATIO;  // phase-1 tiles per phase-2 tile
+static_assert(kRatio >= 1 && kRatio <= 64, "one lane of the first wave waits for each producer flag");
+// packs per lane in a phase-1 tile: 16-byte loads of W ranks stay in registers, so wide W takes one
+template <int W> struct PhaseOneU { static constexpr int value = W <= 8 ? MR_TS_U1 : 1; };
 
 template <typename D, int W>
 __global__ __launch_bounds__(kRBlock) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
@@ -336,26 +380,25 @@ __global__ __launch_bounds__(kRBlock) void twoshot_vec(RankPtrs in, char* out, c
   const size_t cend = c0 + pl.chunk_units < sh.npacks ? c0 + pl.chunk_units : sh.npacks;
   char* stage_body = stage + hb;
   if (k < pl.t1) {
-    const size_t first = c0 + static_cast<size_t>(k) * kRBlock;
-    const size_t i = first + threadIdx.x;
-    if (i < cend) {
-      const u32x4 o = reduce_pack<D, W>(in, hb, i);
-      raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), make_rsrc(stage_body + first * 16, kRBlock * 16),
-                          threadIdx.x * 16, 0, kDeviceNT);
-    }
+    constexpr int kU1 = PhaseOneU<W>::value;
+    const size_t first = c0 + static_cast<size_t>(k) * (kRBlock * kU1);
+    const i32x4 rs = make_rsrc(stage_body + first * 16, kRBlock * kU1 * 16);
+    reduce_packs<D, W, kU1>(in, hb, first, cend, [&](int u, const u32x4& o) {
+      raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), rs, (u * kRBlock + threadIdx.x) * 16, 0, kStageStoreAux);
+    });
     if (c == 0 && k == 0) reduce_edges<D, W, true>(in, stage, sh);
     publish_phase1(ctrl, flags, pl, c, k);
   } else {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
-    constexpr uint32_t kU = kRatio;
+    constexpr uint32_t kU = kRatio * PhaseOneU<W>::value;
     const size_t first = c0 + static_cast<size_t>(q) * (kRBlock * kU);
     const i32x4 rs = make_rsrc(stage_body + first * 16, kRBlock * kU * 16);
     u32x4 v[kU];
 #pragma unroll
     for (uint32_t u = 0; u < kU; ++u) {
       const size_t i = first + u * kRBlock + threadIdx.x;
-      if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, (u * kRBlock + threadIdx.x) * 16, 0, kDeviceNT));
+      if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, (u * kRBlock + threadIdx.x) * 16, 0, kStageLoadAux));
     }
 #pragma unroll
     for (uint32_t u = 0; u < kU; ++u) {
@@ -495,7 +538,10 @@ TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t s
   pl.chunks = static_cast<uint32_t>(W);
   const size_t units = sh.vec ? sh.npacks : sh.n;
   pl.chunk_units = (units + W - 1) / W;
-  pl.unit1 = sh.vec ? kRBlock : kBlock;
+  static const int kU1[MR_MAX_W + 1] = {1, PhaseOneU<1>::value, PhaseOneU<2>::value, PhaseOneU<3>::value,
+                                        PhaseOneU<4>::value, PhaseOneU<5>::value, PhaseOneU<6>::value,
+                                        PhaseOneU<7>::value, PhaseOneU<8>::value, 1, 1, 1, 1, 1, 1, 1, 1};
+  pl.unit1 = sh.vec ? kRBlock * kU1[W] : kBlock;
   pl.ratio = kRatio;
   pl.unit2 = pl.unit1 * kRatio;
   size_t t1 = (pl.chunk_units + pl.unit1 - 1) / pl.unit1;

@@ -116,6 +116,21 @@ def test_workspace_sizes_and_errors(L):
     assert L.mr_workspace_check(None, None) == EINVAL
 
 
+@pytest.mark.parametrize("es,dt", [(2, 0), (4, 2)])
+def test_workspace_rule_covers_every_two_shot_plan(L, es, dt):
+    # layout: 16 KiB of barrier words, then bytes/256 u32 flags (rounded to 256 B), then the stage.
+    # The largest plan for n elements is the element-wise one: W chunks of ceil(n/W) elements in tiles
+    # of 256, one flag per tile.
+    for n in [1, 255, 256, 257, 4097, 65_536, 1_000_003, 10_000_019, 123_456_789]:
+        for W in (1, 3, 8, 16):
+            b = L.mr_workspace_bytes(W, n, dt)
+            flags_cap = b >> 8
+            stage_off = 16384 + ((flags_cap * 4 + 255) // 256) * 256
+            tiles = -(-(-(-n // W)) // 256)
+            assert W * tiles <= flags_cap, (n, W)
+            assert stage_off + n * es + 16 <= b, (n, W)
+
+
 def test_options_validate_and_round_trip(L):
     v = ctypes.c_int64(-7)
     assert L.mr_get_option(0, ctypes.byref(v)) == OK and v.value == 0          # tile flags by default

@@ -282,3 +282,19 @@ def test_config3_size_sweep(dtype, per_rank):
     del dbufs
     torch.cuda.empty_cache()
     assert mr.workspace_check() == 0
+
+
+def test_twoshot_elementwise_path_large():
+    """Pointers with different 16-byte phases take the element-wise path, whose two-shot plan needs a
+    producer flag per 256 elements; a large call checks that the workspace sizing covers it."""
+    W, n = 8, 20_000_003
+    bufs = workloads.rank_buffers(19, W, n + 8, "bf16", "uniform")
+    offs = [r % 8 for r in range(W)]
+    dev_full = [to_dev(b, "bf16") for b in bufs]
+    views = [dev_full[r][offs[r]:offs[r] + n] for r in range(W)]
+    idx = np.linspace(0, n - 1, 1 << 18).astype(np.int64)
+    want = oracle.allreduce_sum_ref([bufs[r][offs[r]:offs[r] + n][idx] for r in range(W)], "bf16")
+    for mode in ("oneshot", "twoshot:tile", "twoshot:chunk"):
+        got = to_bits(_run(views, "bf16", n, mode))
+        assert_reduce_equal(got[idx], want, "bf16", f"element path {mode}")
+    assert mr.workspace_check() == 0
