@@ -6,8 +6,8 @@
 // added in rank order 0..W-1 with fp32 round-to-nearest-even adds; the sum is rounded to nearest even
 // into the buffer dtype.  The work is HBM streaming ((W+1) bytes moved per output byte, at most W-1
 // adds per element), so the kernels are shaped for memory-level parallelism: one 16-byte load per
-// lane per rank buffer, all W loads issued before any arithmetic, 1024-lane workgroups (fewer groups
-// to dispatch and drain), non-temporal hints because no byte is touched twice.  No LDS, no MFMA.
+// lane per rank buffer, all of a lane's loads issued before any arithmetic, large workgroups (fewer
+// groups to dispatch and drain), non-temporal hints because no byte is touched twice.  No LDS, no MFMA.
 
 #include "mr_internal.h"
 
@@ -160,24 +160,6 @@ __device__ __forceinline__ void reduce_elem(const RankPtrs& in, char* dst, size_
   store_bits<D::kSize, Dev>(dst + off, D::narrow1(acc));
 }
 
-// One 16-byte pack per lane: W loads in flight together, then W-1 adds per element.
-template <typename D, int W>
-__device__ __forceinline__ u32x4 reduce_pack(const RankPtrs& in, size_t hb, size_t i) {
-  u32x4 v[W];
-#pragma unroll
-  for (int r = 0; r < W; ++r) v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
-  float acc[D::V];
-  D::widen(v[0], acc);
-#pragma unroll
-  for (int r = 1; r < W; ++r) {
-    float t[D::V];
-    D::widen(v[r], t);
-#pragma unroll
-    for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
-  }
-  return D::narrow(acc);
-}
-
 // U packs per lane (pack i = first + u*kRBlock + lane, i < end), all W*U loads issued before the
 // first add, each result stored through `st(u, pack)`.
 template <typename D, int W, int U, typename Store>
@@ -230,13 +212,56 @@ __device__ __forceinline__ void copy_edges_from_stage(const char* stage, char* d
 
 // ---------------------------------------------------------------------------------------- one-shot
 
+// One-shot tile: kOneShotBlock lanes x U packs.  Wave w of the workgroup owns U*64 consecutive packs
+// and loads them rank by rank (the U loads of one rank are adjacent 1 KiB pieces), so each wave reads
+// U KiB contiguous per rank buffer at a time.  Same-GPU A/B at W=8 bf16, 16 MiB per rank: 256 lanes x
+// 4 packs wave-contiguous 26.2 us; 512 x 1 interleaved 26.3; 512 x 2 interleaved 26.5; 1024 x 2
+// wave-contiguous 26.9; 512 x 2 wave-contiguous 27.0; 1024 x 1 interleaved 27.5.
+#ifndef MR_OS_BLOCK
+#define MR_OS_BLOCK 256
+#endif
+#ifndef MR_OS_U
+#define MR_OS_U 4
+#endif
+#ifndef MR_OS_WAVE_CONTIG
+#define MR_OS_WAVE_CONTIG 1
+#endif
+constexpr int kOneShotBlock = MR_OS_BLOCK;
+template <int W> struct OneShotU { static constexpr int value = W <= 8 ? MR_OS_U : 1; };
+
 template <typename D, int W>
-__global__ __launch_bounds__(kRBlock) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
+__global__ __launch_bounds__(kOneShotBlock) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
+  constexpr int U = OneShotU<W>::value;
   const size_t hb = sh.head * D::kSize;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const size_t i = t * kRBlock + threadIdx.x;
-    if (i < sh.npacks)
-      __builtin_nontemporal_store(reduce_pack<D, W>(in, hb, i), reinterpret_cast<u32x4*>(out + hb) + i);
+    // pack of (lane, u): wave-contiguous first + u*64, or lane-interleaved first + u*kOneShotBlock
+    constexpr size_t kStep = MR_OS_WAVE_CONTIG ? 64 : kOneShotBlock;
+    const size_t first = t * (kOneShotBlock * U) + (MR_OS_WAVE_CONTIG ? static_cast<size_t>(wave) * (64 * U) + lane : threadIdx.x);
+    u32x4 v[U][W];
+#pragma unroll
+    for (int r = 0; r < W; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t i = first + u * kStep;
+        if (i < sh.npacks) v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = first + u * kStep;
+      if (i < sh.npacks) {
+        float acc[D::V];
+        D::widen(v[u][0], acc);
+#pragma unroll
+        for (int r = 1; r < W; ++r) {
+          float tv[D::V];
+          D::widen(v[u][r], tv);
+#pragma unroll
+          for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + tv[k];
+        }
+        __builtin_nontemporal_store(D::narrow(acc), reinterpret_cast<u32x4*>(out + hb) + i);
+      }
+    }
   }
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
@@ -451,10 +476,11 @@ constexpr size_t kMaxGrid = size_t(1) << 20;  // workgroups; beyond this the one
 template <typename D, int W>
 hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
   if (sh.vec) {
-    const size_t ntiles = (sh.npacks + kRBlock - 1) / kRBlock;
+    const size_t tile = static_cast<size_t>(kOneShotBlock) * OneShotU<W>::value;
+    const size_t ntiles = (sh.npacks + tile - 1) / tile;
     size_t grid = ntiles < kMaxGrid ? ntiles : kMaxGrid;
     if (grid == 0) grid = 1;  // edges only
-    hipLaunchKernelGGL((oneshot_vec<D, W>), dim3(static_cast<unsigned>(grid)), dim3(kRBlock), 0, st, in, out, sh, ntiles);
+    hipLaunchKernelGGL((oneshot_vec<D, W>), dim3(static_cast<unsigned>(grid)), dim3(kOneShotBlock), 0, st, in, out, sh, ntiles);
   } else {
     const size_t need = (sh.n + kBlock - 1) / kBlock;
     const size_t grid = need < kMaxGrid ? need : kMaxGrid;

@@ -68,6 +68,63 @@ def time_steps(calls, K, W_, stream):
     return e0.elapsed_time(e1)  # ms
 
 
+def contention_leg(mr, torch, dev, stream, R=20, G=24):
+    """W=8 fp32 one-shot at 512 MiB per rank, alone and while bf16 8192^3 GEMMs run on a second
+    stream (default priority): reduce GB/s and GEMM TFLOP/s alone and together."""
+    W, n = 8, 134_217_728
+    algo = (W + 1) * n * 4
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    bufs = [torch.rand(n, device=dev, generator=g) * 2 - 1 for _ in range(W)]
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    call = mr.prepare_allreduce(bufs, out, "oneshot")
+    a = (torch.randn(8192, 8192, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    b = (torch.randn(8192, 8192, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+    flop = 2.0 * 8192 ** 3
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def reduce_run():
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(R):
+            call()
+        e1.record(stream)
+        return e0, e1
+
+    def gemm_run():
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(side):
+            e0.record(side)
+            for _ in range(G):
+                torch.matmul(a, b, out=c)
+            e1.record(side)
+        return e0, e1
+
+    call(); torch.matmul(a, b, out=c); torch.cuda.synchronize()
+    r0, r1 = reduce_run(); torch.cuda.synchronize()
+    t_red = r0.elapsed_time(r1) / R * 1e-3
+    g0, g1 = gemm_run(); torch.cuda.synchronize()
+    t_gemm = g0.elapsed_time(g1) / G * 1e-3
+    side.wait_stream(stream)
+    g0, g1 = gemm_run()
+    r0, r1 = reduce_run()
+    torch.cuda.synchronize()
+    t_red_c = r0.elapsed_time(r1) / R * 1e-3
+    t_gemm_c = g0.elapsed_time(g1) / G * 1e-3
+    res = {"reduce_GBps_alone": algo / t_red / 1e9, "reduce_GBps_with_gemm": algo / t_red_c / 1e9,
+           "gemm_TFLOPs_alone": flop / t_gemm / 1e12, "gemm_TFLOPs_with_reduce": flop / t_gemm_c / 1e12,
+           "reduce_us_alone": t_red * 1e6, "reduce_us_with_gemm": t_red_c * 1e6, "bytes_per_reduce": algo,
+           "note": "reduce window overlaps the GEMM stream; GEMM figure averaged over its own window"}
+    log(f"[bench] contention fp32 512 MiB/rank: reduce {res['reduce_GBps_alone']:.1f} GB/s alone, "
+        f"{res['reduce_GBps_with_gemm']:.1f} GB/s beside GEMM; GEMM {res['gemm_TFLOPs_alone']:.0f} TFLOP/s alone, "
+        f"{res['gemm_TFLOPs_with_reduce']:.0f} TFLOP/s beside reduce")
+    del bufs, out, a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +233,7 @@ def main():
         log(f"[bench] param_contig: {tg * 1e6:.1f} us/launch, {gbytes / tg / 1e9:.1f} GB/s ({gbytes} B)")
         del gsets
         torch.cuda.empty_cache()
+        paths["contention_fp32_512MiB"] = contention_leg(mr, torch, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -298,3 +298,43 @@ def test_twoshot_elementwise_path_large():
         got = to_bits(_run(views, "bf16", n, mode))
         assert_reduce_equal(got[idx], want, "bf16", f"element path {mode}")
     assert mr.workspace_check() == 0
+
+
+def test_config5_fp32_512MiB_alone_and_beside_a_gemm():
+    """W=8 fp32 rank buffers of 134,217,728 elements (512 MiB each), uniform[-1,1): sampled outputs
+    against the oracle, alone and while bf16 8192^3 GEMMs run on a second stream."""
+    c = workloads.CONFIG5
+    W, n = c["W"], c["n"]
+    idx = np.linspace(0, n - 1, 1 << 20).astype(np.int64)
+    dbufs, cols = [], []
+    for r in range(W):  # one rank at a time keeps host memory near 1 GiB
+        b = workloads.rank_buffer(c["cfg"], r, n, "fp32", c["dist"])
+        cols.append(b[idx].copy())
+        dbufs.append(to_dev(b, "fp32"))
+        del b
+    want = oracle.allreduce_sum_ref(cols, "fp32")
+    out = torch.empty(n, dtype=torch.float32, device=device())
+    for mode in ("oneshot", "twoshot:tile"):
+        out.zero_()
+        got = to_bits(_run(dbufs, "fp32", n, mode))
+        assert_reduce_equal(got[idx], want, "fp32", f"config5 {mode}")
+    # beside a GEMM on another stream (default priority)
+    g = torch.Generator(device=device())
+    g.manual_seed(5)
+    a = (torch.randn(8192, 8192, device=device(), generator=g) * 0.02).to(torch.bfloat16)
+    bm = (torch.randn(8192, 8192, device=device(), generator=g) * 0.02).to(torch.bfloat16)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for _ in range(6):
+            cgemm = torch.matmul(a, bm)
+    for mode in ("oneshot", "twoshot:tile"):
+        out.zero_()
+        _call(dbufs, out, mode)
+    torch.cuda.synchronize()
+    got = to_bits(out)
+    assert_reduce_equal(got[idx], want, "fp32", "config5 under GEMM")
+    assert torch.isfinite(cgemm.float()).all()
+    assert mr.workspace_check() == 0
+    del dbufs, out, a, bm, cgemm
+    torch.cuda.empty_cache()
