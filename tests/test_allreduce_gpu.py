@@ -338,3 +338,28 @@ def test_config5_fp32_512MiB_alone_and_beside_a_gemm():
     assert mr.workspace_check() == 0
     del dbufs, out, a, bm, cgemm
     torch.cuda.empty_cache()
+
+
+def _structured_partners(dtype, count=64):
+    g = np.random.default_rng(21)
+    if dtype == "bf16":
+        base = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F, 0x0080, 0x8080, 0x3F80, 0xBF80, 0x3B80, 0xBB80,
+                0x3380, 0xB380, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC0, 0x3F00, 0x4000, 0xC000, 0x3C00, 0x0100]
+    else:
+        base = [0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x83FF, 0x0400, 0x8400, 0x3C00, 0xBC00, 0x1000, 0x9000,
+                0x1400, 0x9400, 0x7BFF, 0xFBFF, 0x7C00, 0xFC00, 0x7E00, 0x3800, 0x4000, 0xC000, 0x4C00, 0x4800]
+    extra = g.integers(0, 65536, size=count - len(base), dtype=np.uint32)
+    return np.array(base + list(extra), dtype=np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_every_16bit_pattern_against_structured_partners(dtype):
+    """All 65,536 input patterns, each summed with 64 structured partners (signed zeros, subnormal
+    edges, rounding ties, largest finite, infinities, NaN): the hardware conversions and adds agree
+    with the oracle bit for bit, in both modes; W=3 adds the negated partner (exact cancellation)."""
+    part = _structured_partners(dtype)
+    x0 = np.tile(np.arange(65536, dtype=np.uint32).astype(np.uint16), len(part))
+    x1 = np.repeat(part, 65536)
+    x2 = x1 ^ np.uint16(0x8000)
+    for bufs in ([x0, x1], [x1, x0, x2]):
+        _check_modes(bufs, dtype, f"16-bit sweep {dtype} W={len(bufs)}")
