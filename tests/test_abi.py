@@ -166,3 +166,17 @@ def test_product_path_does_not_import_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "workloads" not in txt, f
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/mr.h compiles as C99 with no HIP headers, and a C program links libmr.so and gets the
+    documented error codes."""
+    exe = tmp_path / "c_abi_check"
+    src = os.path.join(ROOT, "tests", "c_abi_check.c")
+    libdir = os.path.dirname(mr.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"), src,
+           "-L", libdir, "-lmr", f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "c abi ok" in r.stdout, r.stdout + r.stderr
