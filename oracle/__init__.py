@@ -20,11 +20,17 @@ blocking, fusion or reordering beyond what the definitions below state.  Two ope
   loop into one launch): for node-block m, split s and slot g, rank r = m*G + g lands at
   ``O_s*W + m*G*E_s + g*E_s``.
 
+Also: ``reduce_scatter_sum_ref`` (one owner's 1/W share of the same sum, the phase-1 half of two-shot),
+``allgather_into_tensor_ref`` / ``allgather_list_ref`` (rank-major and list-output all-gather of W shards)
+and ``allgather_param_contig_shards_ref`` (the param-contiguous placement straight from W shards).
+
 Pins (tests/test_oracle.py) tie every function to something other than itself: exact-rational IEEE
 arithmetic written from the standard, closed forms, invariants and library routines.
 """
 from __future__ import annotations
 
 from .numerics import narrow, widen  # noqa: F401
-from .reduce import allreduce_sum_ref, allreduce_sum_ref_threaded  # noqa: F401
-from .gather import allgather_param_contig_ref, param_offsets  # noqa: F401
+from .reduce import (allreduce_sum_ref, allreduce_sum_ref_threaded, reduce_scatter_chunk,  # noqa: F401
+                     reduce_scatter_sum_ref)
+from .gather import (allgather_into_tensor_ref, allgather_list_ref, allgather_param_contig_ref,  # noqa: F401
+                     allgather_param_contig_shards_ref, param_offsets)

@@ -45,3 +45,27 @@ def allgather_param_contig_ref(src: np.ndarray, W: int, G: int, splits) -> np.nd
                 dst = dst_block + g * E
                 out[dst:dst + E] = src[r * T + O:r * T + O + E]
     return out
+
+
+def allgather_into_tensor_ref(shards: list[np.ndarray]) -> np.ndarray:
+    """Rank-major all-gather of W equal shards (torch.distributed.all_gather_into_tensor's layout):
+    out[r*T + j] = shards[r][j]."""
+    T = shards[0].shape[0]
+    out = np.empty(len(shards) * T, dtype=shards[0].dtype)
+    for r, x in enumerate(shards):
+        if x.shape != (T,):
+            raise ValueError("shards must have the same length")
+        out[r * T:(r + 1) * T] = x
+    return out
+
+
+def allgather_list_ref(shards: list[np.ndarray]) -> list[np.ndarray]:
+    """List-output all-gather (torch.distributed.all_gather's layout): output r is a copy of shard r."""
+    return [x.copy() for x in shards]
+
+
+def allgather_param_contig_shards_ref(shards: list[np.ndarray], G: int, splits) -> np.ndarray:
+    """Param-contiguous all-gather straight from W separate rank shards (the zero-copy push of the
+    page's enqueue_param_contiguous): the same placement as allgather_param_contig_ref applied to the
+    rank-major concatenation of the shards."""
+    return allgather_param_contig_ref(allgather_into_tensor_ref(shards), len(shards), G, splits)

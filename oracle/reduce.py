@@ -56,3 +56,25 @@ def allreduce_sum_ref_threaded(bufs: list[np.ndarray], dtype: str, threads: int 
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(part, range(threads)))
     return out
+
+
+def reduce_scatter_chunk(n: int, W: int, dtype: str, rank: int) -> tuple[int, int]:
+    """Element range [start, stop) of rank ``rank``'s share of an n-element reduce-scatter.
+
+    Two-shot's reduce-scatter hands chunk c to owner c.  The pages leave the chunk length open when W
+    does not divide n (the Triton page's per-rank slice is cdiv(numel/8, W) 128-bit packs and is not
+    masked); the reading taken: C = ceil(n/W) rounded up to a whole 16-byte pack, chunk c =
+    [c*C, min((c+1)*C, n)), so trailing chunks may be short or empty.
+    """
+    V = 16 // {"bf16": 2, "fp16": 2, "fp32": 4}[dtype]
+    per = -(-n // W)
+    C = -(-per // V) * V
+    start = min(rank * C, n)
+    return start, min(start + C, n)
+
+
+def reduce_scatter_sum_ref(bufs: list[np.ndarray], dtype: str, rank: int) -> np.ndarray:
+    """Rank ``rank``'s share of the reduce-scatter: the W-way sum over its chunk only."""
+    n = bufs[0].shape[0]
+    a, b = reduce_scatter_chunk(n, len(bufs), dtype, rank)
+    return allreduce_sum_ref([x[a:b] for x in bufs], dtype)

@@ -395,3 +395,57 @@ def test_rank_buffers_are_seeded_and_in_range():
     assert not np.array_equal(a[0], a[1])
     v = oracle.widen(a[0], "bf16")
     assert v.min() >= -1.0 and v.max() <= 1.0
+
+
+# ------------------------------------------------------------------------------------ next-step ops
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 8), ("fp16", 8), ("fp32", 4)])
+def test_reduce_scatter_chunks_tile_the_message(dtype, V):
+    # closed form: chunks are [c*C, (c+1)*C) with C a whole number of 16-byte packs, covering [0, n)
+    # exactly once; for n a multiple of W*V every chunk is n/W long
+    for n in (0, 1, 7, 8, 9, 63, 64, 65, 1000, 8_388_608, 8_388_611):
+        for W in (1, 2, 3, 8, 16):
+            spans = [oracle.reduce_scatter_chunk(n, W, dtype, r) for r in range(W)]
+            assert spans[0][0] == 0 and spans[-1][1] == n
+            for (a0, b0), (a1, b1) in zip(spans, spans[1:]):
+                assert b0 == a1
+            C = spans[0][1] - spans[0][0]
+            if n > 0:
+                assert C % V == 0 or C == n
+                assert C >= n / W
+            if n % (W * V) == 0:
+                assert all(b - a == n // W for a, b in spans)
+
+
+def test_reduce_scatter_shares_concatenate_to_the_all_reduce():
+    W, n = 8, 100_003
+    bufs = workloads.rank_buffers(60, W, n, "bf16", "normal")
+    full = oracle.allreduce_sum_ref(bufs, "bf16")
+    parts = [oracle.reduce_scatter_sum_ref(bufs, "bf16", r) for r in range(W)]
+    assert np.array_equal(np.concatenate(parts), full)
+    # each share only reads its own chunk: poisoning the rest of the inputs leaves it unchanged
+    a, b = oracle.reduce_scatter_chunk(n, W, "bf16", 3)
+    poisoned = [x.copy() for x in bufs]
+    for x in poisoned:
+        x[:a] = 0x7FC0
+        x[b:] = 0x7FC0
+    assert np.array_equal(oracle.reduce_scatter_sum_ref(poisoned, "bf16", 3), full[a:b])
+
+
+def test_allgather_into_tensor_and_list_against_torch():
+    W, T = 6, 1001
+    shards = [workloads.random_bits(61, r, T, "fp16") for r in range(W)]
+    want = torch.cat([torch.from_numpy(x.astype(np.int32)) for x in shards]).numpy()
+    assert np.array_equal(oracle.allgather_into_tensor_ref(shards).astype(np.int32), want)
+    outs = oracle.allgather_list_ref(shards)
+    assert all(np.array_equal(o, x) and o is not x for o, x in zip(outs, shards))
+
+
+def test_param_contig_from_shards_matches_split_and_cat():
+    W, G = 8, 4
+    splits = [int(v) for v in workloads.log_uniform_splits(62, 7, lo=8, hi=4096)]
+    T = sum(splits)
+    shards = [workloads.random_bits(62, r, T, "int32") for r in range(W)]
+    pieces = [torch.from_numpy(x.view(np.int32)).split(splits) for x in shards]
+    want = torch.cat([torch.cat([pieces[r][s] for r in range(W)]) for s in range(len(splits))]).numpy()
+    assert np.array_equal(oracle.allgather_param_contig_shards_ref(shards, G, splits).view(np.int32), want)
