@@ -29,6 +29,7 @@ OPTION_CODE = {"twoshot_sync": 0, "spin_limit": 1}
 TWOSHOT_SYNC = {"tile": 0, "chunk": 1, "grid": 2}
 MAX_W = 16
 MAX_PARAMS_PER_LAUNCH = 128
+MAX_TABLE_W = 64
 
 # Exported symbols of include/mr.h, with ctypes signatures.
 _SIGS = {
@@ -43,6 +44,17 @@ _SIGS = {
     "mr_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_size_t, ctypes.c_int]),
     "mr_set_workspace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]),
     "mr_workspace_check": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32)]),
+    "mr_reduce_scatter_chunk": (ctypes.c_int, [ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+    "mr_reduce_scatter_sum": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+    "mr_allgather_into_tensor": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t,
+                                                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+    "mr_allgather_list": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t,
+                                         ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
+    "mr_allgather_param_contig_shards": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int,
+                                                        ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int,
+                                                        ctypes.c_void_p, ctypes.c_void_p]),
     "mr_set_option": (ctypes.c_int, [ctypes.c_int, ctypes.c_int64]),
     "mr_get_option": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -127,6 +139,80 @@ def allgather_param_contig(src, W: int, G: int, splits: Sequence[int], out, stre
     return out
 
 
+def reduce_scatter_chunk(n: int, W: int, dtype: str, rank: int) -> tuple[int, int]:
+    """(offset, count) of rank ``rank``'s chunk of an n-element reduce-scatter."""
+    off, cnt = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().mr_reduce_scatter_chunk(n, W, DTYPE_CODE[dtype], rank, ctypes.byref(off), ctypes.byref(cnt)),
+           "mr_reduce_scatter_chunk")
+    return int(off.value), int(cnt.value)
+
+
+def reduce_scatter_sum(bufs: Sequence, rank: int, out, stream=None):
+    """out = rank ``rank``'s chunk of the elementwise sum of the W same-shape tensors ``bufs``."""
+    W = len(bufs)
+    for b in bufs:
+        _dev_tensor(b, "rank buffer")
+        if b.dtype != out.dtype or b.numel() != bufs[0].numel():
+            raise ValueError("rank buffers must share dtype and element count with each other and out")
+    _dev_tensor(out, "out")
+    n = bufs[0].numel() if W else 0
+    _, cnt = reduce_scatter_chunk(n, W, dtype_name(out), rank)
+    if out.numel() != cnt:
+        raise ValueError(f"out must hold the chunk's {cnt} elements")
+    ptrs = (ctypes.c_void_p * max(W, 1))(*[b.data_ptr() for b in bufs])
+    _check(lib().mr_reduce_scatter_sum(ptrs, W, n, DTYPE_CODE[dtype_name(out)], rank, out.data_ptr(),
+                                       _stream_handle(stream)), "mr_reduce_scatter_sum")
+    return out
+
+
+def _shard_ptrs(shards):
+    for t in shards:
+        _dev_tensor(t, "shard")
+        if t.dtype != shards[0].dtype or t.numel() != shards[0].numel():
+            raise ValueError("shards must share dtype and element count")
+    return (ctypes.c_void_p * max(len(shards), 1))(*[t.data_ptr() for t in shards])
+
+
+def allgather_into_tensor(shards: Sequence, out, stream=None):
+    """out[r*T:(r+1)*T] = shards[r] (rank-major all-gather of W shards of T elements)."""
+    ptrs = _shard_ptrs(shards)
+    _dev_tensor(out, "out")
+    T = shards[0].numel()
+    if out.dtype != shards[0].dtype or out.numel() != len(shards) * T:
+        raise ValueError("out must hold W*T elements of the shards' dtype")
+    _check(lib().mr_allgather_into_tensor(ptrs, len(shards), T, DTYPE_CODE[dtype_name(out)], out.data_ptr(),
+                                          _stream_handle(stream)), "mr_allgather_into_tensor")
+    return out
+
+
+def allgather_list(shards: Sequence, outs: Sequence, stream=None):
+    """outs[r] = shards[r] for every rank (list-output all-gather), one launch."""
+    ptrs = _shard_ptrs(shards)
+    if len(outs) != len(shards):
+        raise ValueError("one output per shard")
+    for o in outs:
+        _dev_tensor(o, "output")
+        if o.dtype != shards[0].dtype or o.numel() != shards[0].numel():
+            raise ValueError("outputs must match the shards")
+    optrs = (ctypes.c_void_p * max(len(outs), 1))(*[o.data_ptr() for o in outs])
+    _check(lib().mr_allgather_list(ptrs, len(shards), shards[0].numel(), DTYPE_CODE[dtype_name(shards[0])], optrs,
+                                   _stream_handle(stream)), "mr_allgather_list")
+    return outs
+
+
+def allgather_param_contig_shards(shards: Sequence, G: int, splits: Sequence[int], out, stream=None):
+    """[param][rank] all-gather written straight from W shards (each sum(splits) elements)."""
+    ptrs = _shard_ptrs(shards)
+    _dev_tensor(out, "out")
+    if out.dtype != shards[0].dtype or out.numel() != len(shards) * shards[0].numel():
+        raise ValueError("out must hold W*T elements of the shards' dtype")
+    sp = (ctypes.c_uint64 * max(len(splits), 1))(*[int(x) for x in splits])
+    _check(lib().mr_allgather_param_contig_shards(ptrs, len(shards), G, sp, len(splits),
+                                                  DTYPE_CODE[dtype_name(out)], out.data_ptr(),
+                                                  _stream_handle(stream)), "mr_allgather_param_contig_shards")
+    return out
+
+
 def workspace_bytes(W: int, n: int, dtype: str) -> int:
     return int(lib().mr_workspace_bytes(W, n, DTYPE_CODE[dtype]))
 
@@ -177,6 +263,44 @@ def prepare_allreduce(bufs: Sequence, out, mode: str = "oneshot", stream=None):
             raise MRError(st, "mr_allreduce_sum")
 
     call.keepalive = (ptrs, list(bufs), out)
+    return call
+
+
+def prepare_reduce_scatter(bufs: Sequence, rank: int, out, stream=None):
+    """Pre-marshalled mr_reduce_scatter_sum call (see prepare_allreduce)."""
+    W = len(bufs)
+    ptrs = (ctypes.c_void_p * max(W, 1))(*[b.data_ptr() for b in bufs])
+    f = lib().mr_reduce_scatter_sum
+    args = (ptrs, W, bufs[0].numel(), DTYPE_CODE[dtype_name(out)], rank, out.data_ptr(), _stream_handle(stream))
+
+    def call() -> None:
+        st = f(*args)
+        if st != MR_OK:
+            raise MRError(st, "mr_reduce_scatter_sum")
+
+    call.keepalive = (ptrs, list(bufs), out)
+    return call
+
+
+def prepare_allgather_shards(shards: Sequence, out, G: int | None = None, splits: Sequence[int] | None = None,
+                             stream=None):
+    """Pre-marshalled shard-list gather: rank-major (``splits`` None) or param-contiguous."""
+    ptrs = _shard_ptrs(shards)
+    W, T = len(shards), shards[0].numel()
+    dt = DTYPE_CODE[dtype_name(out)]
+    if splits is None:
+        f, args = lib().mr_allgather_into_tensor, (ptrs, W, T, dt, out.data_ptr(), _stream_handle(stream))
+    else:
+        sp = (ctypes.c_uint64 * max(len(splits), 1))(*[int(x) for x in splits])
+        f = lib().mr_allgather_param_contig_shards
+        args = (ptrs, W, G, sp, len(splits), dt, out.data_ptr(), _stream_handle(stream))
+
+    def call() -> None:
+        st = f(*args)
+        if st != MR_OK:
+            raise MRError(st, "shard gather")
+
+    call.keepalive = (args, list(shards), out)
     return call
 
 

@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "mr_internal.h"
 
@@ -106,6 +107,122 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
   return MR_OK;
 }
 
+
+// ------------------------------------------------------------------------------------ reduce launch
+// Alias check, 16-byte layout of the call, and the one-shot or two-shot launch.  `ins` are already
+// validated non-null.
+mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype, char* out, mr_mode mode,
+                        hipStream_t st) {
+  const int es = mr::elem_size(dtype);
+  const size_t nbytes = n * static_cast<size_t>(es);
+  const uintptr_t po = reinterpret_cast<uintptr_t>(out);
+  mr::RankPtrs in{};
+  bool same_phase = (po % static_cast<uintptr_t>(es)) == 0;
+  for (int r = 0; r < W; ++r) {
+    const uintptr_t pr = reinterpret_cast<uintptr_t>(ins[r]);
+    if (pr != po && overlap(pr, nbytes, po, nbytes)) return MR_ERR_ALIAS;
+    if ((pr & 15u) != (po & 15u)) same_phase = false;
+    in.p[r] = ins[r];
+  }
+  mr::ReduceShape sh{};
+  sh.n = n;
+  sh.vec = same_phase ? 1 : 0;
+  if (sh.vec) {
+    const size_t V = 16 / static_cast<size_t>(es);
+    size_t head = ((16u - (po & 15u)) & 15u) / static_cast<size_t>(es);
+    if (head > n) head = n;
+    sh.head = head;
+    sh.npacks = (n - head) / V;
+  }
+  hipError_t e;
+  if (mode == MR_ONESHOT) {
+    if (g_trace)
+      std::fprintf(stderr, "[mr] allreduce oneshot W=%d n=%zu dtype=%d vec=%d head=%zu packs=%zu\n", W, n,
+                   static_cast<int>(dtype), sh.vec, sh.head, sh.npacks);
+    e = mr::launch_oneshot(in, W, dtype, out, sh, st);
+  } else {
+    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, g_twoshot_sync.load(), g_spin_limit.load());
+    const uint64_t grid = static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
+    if (grid >= (1ull << 24)) return MR_ERR_INVALID_ARG;
+    const size_t flags_needed = static_cast<size_t>(pl.chunks) * pl.t1;
+    Workspace ws;
+    mr_status s = get_workspace(st, n, es, flags_needed, &ws);
+    if (s != MR_OK) return s;
+    // the stage shares out's 16-byte phase so that its body is 16-byte aligned too
+    char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (sh.vec ? (po & 15u) : 0);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws.base + mr::kCtrlBytes);
+    if (g_trace)
+      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu t1=%u t2=%u\n", W, n,
+                   static_cast<int>(dtype), sh.vec, pl.sync, pl.chunk_units, pl.t1, pl.t2);
+    e = mr::launch_twoshot(in, W, dtype, out, stage, reinterpret_cast<mr::Ctrl*>(ws.base), flags, sh, pl, st);
+  }
+  return e == hipSuccess ? MR_OK : hip_fail(e);
+}
+
+// ------------------------------------------------------------------------------------ gather launches
+// Splits are validated and cut into launch groups of up to kMaxParams parameters before anything is
+// enqueued; the entry points then fill in the pointers of every group and launch them in order.
+struct GatherPlan {
+  uint64_t T = 0;
+  uint64_t es = 0;
+  std::vector<mr::GatherArgs> groups;
+};
+
+mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, GatherPlan* gp) {
+  if (G < 1 || W % G != 0) return MR_ERR_INVALID_ARG;
+  if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
+  const uint64_t es = static_cast<uint64_t>(mr::elem_size(dtype));
+  uint64_t T = 0;
+  for (int s = 0; s < P; ++s) {
+    if (splits[s] > (1ull << 56) || T > (1ull << 56)) return MR_ERR_INVALID_ARG;
+    T += splits[s];
+  }
+  if (T > (1ull << 56) / (static_cast<uint64_t>(W) * es)) return MR_ERR_INVALID_ARG;
+  gp->T = T;
+  gp->es = es;
+  if (T == 0) return MR_OK;
+  uint64_t base = 0;  // shard offset of the first parameter of a group
+  for (int s0 = 0; s0 < P; s0 += mr::kMaxParams) {
+    const int np = (P - s0) < mr::kMaxParams ? (P - s0) : mr::kMaxParams;
+    mr::GatherArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.T = T;
+    a.P = static_cast<uint32_t>(np);
+    a.W = static_cast<uint32_t>(W);
+    a.G = static_cast<uint32_t>(G);
+    a.elem = static_cast<uint32_t>(es);
+    uint64_t tiles = 0;
+    for (int i = 0; i < np; ++i) {
+      a.O[i] = base;
+      a.tile_prefix[i] = static_cast<uint32_t>(tiles);
+      const uint64_t E = splits[s0 + i];
+      tiles += static_cast<uint64_t>(G) * mr::gather_tiles_per_segment(E, static_cast<uint32_t>(es));
+      base += E;
+      if (tiles >= (1ull << 31)) return MR_ERR_INVALID_ARG;
+    }
+    a.O[np] = base;
+    a.tile_prefix[np] = static_cast<uint32_t>(tiles);
+    a.tiles_per_block = static_cast<uint32_t>(tiles);
+    const uint64_t total = tiles * static_cast<uint64_t>(W / G);
+    if (total >= (1ull << 32)) return MR_ERR_INVALID_ARG;
+    a.total_tiles = static_cast<uint32_t>(total);
+    gp->groups.push_back(a);
+  }
+  return MR_OK;
+}
+
+mr_status gather_launch(const GatherPlan& gp, hipStream_t st) {
+  for (const mr::GatherArgs& a : gp.groups) {
+    if (g_trace)
+      std::fprintf(stderr, "[mr] gather W=%u G=%u params=%u T=%llu tiles=%u src_table=%u dst_table=%u\n", a.W, a.G,
+                   a.P, static_cast<unsigned long long>(a.T), a.total_tiles, a.src_table, a.dst_table);
+    const hipError_t e = mr::launch_param_contig(a, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return MR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,109 +284,115 @@ mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dt
   if (!bufs || !out) return MR_ERR_INVALID_ARG;
   const int es = mr::elem_size(dtype);
   if (n > (SIZE_MAX / 2 - mr::kCtrlBytes) / static_cast<size_t>(es)) return MR_ERR_INVALID_ARG;
-  const size_t nbytes = n * static_cast<size_t>(es);
-  const uintptr_t po = reinterpret_cast<uintptr_t>(out);
-  mr::RankPtrs in{};
-  bool same_phase = (po % static_cast<uintptr_t>(es)) == 0;
+  const char* ins[MR_MAX_W];
   for (int r = 0; r < W; ++r) {
     if (!bufs[r]) return MR_ERR_INVALID_ARG;
-    const uintptr_t pr = reinterpret_cast<uintptr_t>(bufs[r]);
-    if (pr != po && overlap(pr, nbytes, po, nbytes)) return MR_ERR_ALIAS;
-    if ((pr & 15u) != (po & 15u)) same_phase = false;
-    in.p[r] = static_cast<const char*>(bufs[r]);
+    ins[r] = static_cast<const char*>(bufs[r]);
   }
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return reduce_launch(ins, W, n, dtype, static_cast<char*>(out), mode, reinterpret_cast<hipStream_t>(stream));
+}
 
-  mr::ReduceShape sh{};
-  sh.n = n;
-  sh.vec = same_phase ? 1 : 0;
-  if (sh.vec) {
-    const size_t V = 16 / static_cast<size_t>(es);
-    size_t head = ((16u - (po & 15u)) & 15u) / static_cast<size_t>(es);
-    if (head > n) head = n;
-    sh.head = head;
-    sh.npacks = (n - head) / V;
-  }
+mr_status mr_reduce_scatter_chunk(size_t n, int W, mr_dtype dtype, int rank, size_t* offset, size_t* count) {
+  if (W < 1 || W > MR_MAX_W || rank < 0 || rank >= W || !offset || !count) return MR_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
+  if (!is_float(dtype)) return MR_ERR_DTYPE;
+  const size_t V = 16 / static_cast<size_t>(mr::elem_size(dtype));
+  if (n > SIZE_MAX / 2) return MR_ERR_INVALID_ARG;
+  const size_t per = (n + W - 1) / W;
+  const size_t C = (per + V - 1) / V * V;
+  const size_t start = static_cast<size_t>(rank) * C < n ? static_cast<size_t>(rank) * C : n;
+  *offset = start;
+  *count = (start + C < n ? start + C : n) - start;
+  return MR_OK;
+}
 
-  hipError_t e;
-  if (mode == MR_ONESHOT) {
-    if (g_trace)
-      std::fprintf(stderr, "[mr] allreduce oneshot W=%d n=%zu dtype=%d vec=%d head=%zu packs=%zu\n", W, n,
-                   static_cast<int>(dtype), sh.vec, sh.head, sh.npacks);
-    e = mr::launch_oneshot(in, W, dtype, static_cast<char*>(out), sh, st);
-  } else {
-    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, g_twoshot_sync.load(), g_spin_limit.load());
-    const uint64_t grid = static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
-    if (grid >= (1ull << 24)) return MR_ERR_INVALID_ARG;
-    const size_t flags_needed = static_cast<size_t>(pl.chunks) * pl.t1;
-    Workspace ws;
-    mr_status s = get_workspace(st, n, es, flags_needed, &ws);
-    if (s != MR_OK) return s;
-    // the stage shares out's 16-byte phase so that its body is 16-byte aligned too
-    char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (sh.vec ? (po & 15u) : 0);
-    uint32_t* flags = reinterpret_cast<uint32_t*>(ws.base + mr::kCtrlBytes);
-    if (g_trace)
-      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu t1=%u t2=%u\n", W, n,
-                   static_cast<int>(dtype), sh.vec, pl.sync, pl.chunk_units, pl.t1, pl.t2);
-    e = mr::launch_twoshot(in, W, dtype, static_cast<char*>(out), stage, reinterpret_cast<mr::Ctrl*>(ws.base), flags,
-                           sh, pl, st);
+mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dtype dtype, int rank, void* out,
+                                mr_stream stream) {
+  size_t off = 0, cnt = 0;
+  mr_status s = mr_reduce_scatter_chunk(n, W, dtype, rank, &off, &cnt);
+  if (s != MR_OK) return s;
+  if (cnt == 0) return MR_OK;
+  if (!bufs || !out) return MR_ERR_INVALID_ARG;
+  const size_t es = static_cast<size_t>(mr::elem_size(dtype));
+  const char* ins[MR_MAX_W];
+  for (int r = 0; r < W; ++r) {
+    if (!bufs[r]) return MR_ERR_INVALID_ARG;
+    ins[r] = static_cast<const char*>(bufs[r]) + off * es;  // this rank's chunk of every rank buffer
   }
-  return e == hipSuccess ? MR_OK : hip_fail(e);
+  return reduce_launch(ins, W, cnt, dtype, static_cast<char*>(out), MR_ONESHOT, reinterpret_cast<hipStream_t>(stream));
 }
 
 mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_t* splits, int P, mr_dtype dtype,
                                     void* out, mr_stream stream) {
-  if (W < 1 || W > 65535 || G < 1 || W % G != 0) return MR_ERR_INVALID_ARG;
-  if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
-  if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
-  const uint64_t es = static_cast<uint64_t>(mr::elem_size(dtype));
-  uint64_t T = 0;
-  for (int s = 0; s < P; ++s) {
-    if (splits[s] > (1ull << 56) || T > (1ull << 56)) return MR_ERR_INVALID_ARG;
-    T += splits[s];
-  }
-  if (T > (1ull << 56) / (static_cast<uint64_t>(W) * es)) return MR_ERR_INVALID_ARG;
-  if (T == 0) return MR_OK;
+  if (W < 1 || W > 65535) return MR_ERR_INVALID_ARG;
+  GatherPlan gp;
+  mr_status s = gather_plan(W, G, splits, P, dtype, &gp);
+  if (s != MR_OK || gp.T == 0) return s;
   if (!src || !out) return MR_ERR_INVALID_ARG;
-  const uint64_t total_bytes = static_cast<uint64_t>(W) * T * es;
+  const uint64_t total_bytes = static_cast<uint64_t>(W) * gp.T * gp.es;
   if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
     return MR_ERR_ALIAS;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-
-  uint64_t base = 0;  // shard offset of the first parameter of this launch
-  for (int s0 = 0; s0 < P; s0 += mr::kMaxParams) {
-    const int np = (P - s0) < mr::kMaxParams ? (P - s0) : mr::kMaxParams;
-    mr::GatherArgs a;
-    std::memset(&a, 0, sizeof(a));
+  for (mr::GatherArgs& a : gp.groups) {
     a.src = static_cast<const char*>(src);
     a.out = static_cast<char*>(out);
-    a.T = T;
-    a.P = static_cast<uint32_t>(np);
-    a.W = static_cast<uint32_t>(W);
-    a.G = static_cast<uint32_t>(G);
-    a.elem = static_cast<uint32_t>(es);
-    uint64_t tiles = 0;
-    for (int i = 0; i < np; ++i) {
-      a.O[i] = base;
-      a.tile_prefix[i] = static_cast<uint32_t>(tiles);
-      const uint64_t E = splits[s0 + i];
-      tiles += static_cast<uint64_t>(G) * mr::gather_tiles_per_segment(E, static_cast<uint32_t>(es));
-      base += E;
-      if (tiles >= (1ull << 31)) return MR_ERR_INVALID_ARG;
-    }
-    a.O[np] = base;
-    a.tile_prefix[np] = static_cast<uint32_t>(tiles);
-    a.tiles_per_block = static_cast<uint32_t>(tiles);
-    const uint64_t total = tiles * static_cast<uint64_t>(W / G);
-    if (total >= (1ull << 32)) return MR_ERR_INVALID_ARG;
-    a.total_tiles = static_cast<uint32_t>(total);
-    if (g_trace)
-      std::fprintf(stderr, "[mr] param_contig W=%d G=%d params=[%d,%d) T=%llu tiles=%u\n", W, G, s0, s0 + np,
-                   static_cast<unsigned long long>(T), a.total_tiles);
-    const hipError_t e = mr::launch_param_contig(a, st);
-    if (e != hipSuccess) return hip_fail(e);
   }
-  return MR_OK;
+  return gather_launch(gp, reinterpret_cast<hipStream_t>(stream));
+}
+
+mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int G, const uint64_t* splits, int P,
+                                           mr_dtype dtype, void* out, mr_stream stream) {
+  if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
+  GatherPlan gp;
+  mr_status s = gather_plan(W, G, splits, P, dtype, &gp);
+  if (s != MR_OK || gp.T == 0) return s;
+  if (!shards || !out) return MR_ERR_INVALID_ARG;
+  const uint64_t shard_bytes = gp.T * gp.es, out_bytes = static_cast<uint64_t>(W) * shard_bytes;
+  for (int r = 0; r < W; ++r) {
+    if (!shards[r]) return MR_ERR_INVALID_ARG;
+    if (overlap(reinterpret_cast<uintptr_t>(shards[r]), shard_bytes, reinterpret_cast<uintptr_t>(out), out_bytes))
+      return MR_ERR_ALIAS;
+  }
+  for (mr::GatherArgs& a : gp.groups) {
+    a.src_table = 1;
+    for (int r = 0; r < W; ++r) a.src_tab[r] = static_cast<const char*>(shards[r]);
+    a.out = static_cast<char*>(out);
+  }
+  return gather_launch(gp, reinterpret_cast<hipStream_t>(stream));
+}
+
+mr_status mr_allgather_into_tensor(const void* const* shards, int W, size_t T, mr_dtype dtype, void* out,
+                                   mr_stream stream) {
+  if (W < 1) return MR_ERR_INVALID_ARG;
+  const uint64_t split = T;
+  return mr_allgather_param_contig_shards(shards, W, W, &split, 1, dtype, out, stream);
+}
+
+mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype dtype, void* const* outs,
+                            mr_stream stream) {
+  if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
+  const uint64_t split = T;
+  GatherPlan gp;
+  mr_status s = gather_plan(W, W, &split, 1, dtype, &gp);
+  if (s != MR_OK || gp.T == 0) return s;
+  if (!shards || !outs) return MR_ERR_INVALID_ARG;
+  const uint64_t bytes = gp.T * gp.es;
+  for (int i = 0; i < W; ++i) {
+    if (!shards[i] || !outs[i]) return MR_ERR_INVALID_ARG;
+    for (int j = 0; j < W; ++j) {
+      const uintptr_t oi = reinterpret_cast<uintptr_t>(outs[i]);
+      if (overlap(oi, bytes, reinterpret_cast<uintptr_t>(shards[j]), bytes)) return MR_ERR_ALIAS;
+      if (j != i && overlap(oi, bytes, reinterpret_cast<uintptr_t>(outs[j]), bytes)) return MR_ERR_ALIAS;
+    }
+  }
+  for (mr::GatherArgs& a : gp.groups) {
+    a.src_table = 1;
+    a.dst_table = 1;
+    for (int r = 0; r < W; ++r) {
+      a.src_tab[r] = static_cast<const char*>(shards[r]);
+      a.dst_tab[r] = static_cast<char*>(outs[r]);
+    }
+  }
+  return gather_launch(gp, reinterpret_cast<hipStream_t>(stream));
 }
 
 mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {

@@ -86,10 +86,10 @@ __global__ __launch_bounds__(kGB) void param_contig(GatherArgs a) {
     const uint64_t r = static_cast<uint64_t>(m) * a.G + g;
     const uint64_t dst_block = Os * a.W + static_cast<uint64_t>(m) * a.G * Es;  // node-block m of param s
     const uint64_t dst_elem = dst_block + static_cast<uint64_t>(g) * Es;         // slot g, stride E_s
-    const uint64_t src_elem = r * a.T + Os;
-
-    const char* sp = a.src + src_elem * S;
-    char* dp = a.out + dst_elem * S;
+    // source: rank r's shard, inside the rank-major buffer or from the shard table
+    const char* sp = a.src_table ? a.src_tab[r] + Os * S : a.src + (r * a.T + Os) * S;
+    // destination: the [param][rank] slot, or rank r's own output (list-output all-gather)
+    char* dp = a.dst_table ? a.dst_tab[r] + Os * S : a.out + dst_elem * S;
     // tiles of the segment end on 256-byte lines of the destination: tile k spans [k*TILE - lead,
     // (k+1)*TILE - lead) with lead = the destination's offset into its line, clipped to the segment
     const uint64_t seg = Es * S;

@@ -96,9 +96,14 @@ constexpr uint32_t kGatherTileBytes = MR_GATHER_TILE;  // bytes per tile (one wo
 constexpr int kGatherBlock = MR_GATHER_BLOCK;          // lanes per gather workgroup
 constexpr uint32_t kGatherLine = MR_GATHER_LINE;       // tile boundaries fall on destination lines of this size (1: off)
 
+constexpr int kMaxTable = MR_MAX_TABLE_W;  // rank pointer tables in the kernel arguments
+
 struct GatherArgs {
-  const char* src;
-  char* out;
+  const char* src;                       // rank-major source (src_tab unused)
+  char* out;                             // param-major destination (dst_tab unused)
+  const char* src_tab[kMaxTable];        // with src_table: rank r's shard (T elements)
+  char* dst_tab[kMaxTable];              // with dst_table: rank r's own output (T elements)
+  uint32_t src_table, dst_table;
   uint64_t T;                            // elements per rank shard
   uint64_t O[kMaxParams + 1];            // O[s]: element offset of parameter s inside a shard; O[P] = its end
   uint32_t tile_prefix[kMaxParams + 1];  // node-block-local tile prefix: G * sum of tiles of params < s

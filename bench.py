@@ -201,6 +201,17 @@ def main():
         ms_w = time_steps(one[:1], K, args.warmup, stream)
         paths["oneshot_cache_resident"] = {"us": ms_w / K * 1e3, "GBps_algorithmic": algo / (ms_w / K * 1e-3) / 1e9,
                                            "note": "one buffer set reused; served partly from cache, not HBM"}
+        # reduce-scatter: rank 0's 1/W share, rotating sets
+        off, cnt = mr.reduce_scatter_chunk(n, W, dtype, 0)
+        rs_out = [torch.empty(cnt, dtype=torch.bfloat16, device=dev) for _ in sets]
+        rs = [mr.prepare_reduce_scatter(b, 0, o) for (b, _), o in zip(sets, rs_out)]
+        ms_rs = time_steps(rs, K, args.warmup, stream)
+        t_rs = ms_rs / K * 1e-3
+        rs_bytes = (W + 1) * cnt * s
+        paths["reduce_scatter_rank0"] = {"us": t_rs * 1e6, "GBps": rs_bytes / t_rs / 1e9, "bytes": rs_bytes,
+                                         "elements": cnt}
+        log(f"[bench] reduce_scatter (rank 0 share, {cnt} elements): {t_rs * 1e6:.2f} us/launch, "
+            f"{rs_bytes / t_rs / 1e9:.1f} GB/s")
         # two-shot, rotating sets, under each phase hand-off
         two = [mr.prepare_allreduce(b, o, "twoshot") for b, o in sets]
         actual2 = (W + 3) * n * s
@@ -231,7 +242,19 @@ def main():
         paths["param_contig"] = {"us": tg * 1e6, "GBps": gbytes / tg / 1e9, "bytes": gbytes, "W": c4["W"],
                                  "G": c4["G"], "P": c4["P"], "T": T, "dtype": "bf16"}
         log(f"[bench] param_contig: {tg * 1e6:.1f} us/launch, {gbytes / tg / 1e9:.1f} GB/s ({gbytes} B)")
-        del gsets
+        # the same gathers written straight from W separate shard buffers
+        shard_sets = []
+        for k in range(2):
+            shards = [torch.randint(-32768, 32767, (T,), dtype=torch.int16, device=dev).view(torch.bfloat16)
+                      for _ in range(c4["W"])]
+            shard_sets.append((shards, torch.empty(c4["W"] * T, dtype=torch.bfloat16, device=dev)))
+        for name, kw in (("allgather_into_tensor", {}), ("param_contig_shards", {"G": c4["G"], "splits": splits})):
+            calls = [mr.prepare_allgather_shards(sh, o, **kw) for sh, o in shard_sets]
+            msx = time_steps(calls, Kg, max(2, args.warmup // 10), stream)
+            tx = msx / Kg * 1e-3
+            paths[name] = {"us": tx * 1e6, "GBps": gbytes / tx / 1e9, "bytes": gbytes, "W": c4["W"], "T": T}
+            log(f"[bench] {name}: {tx * 1e6:.1f} us/launch, {gbytes / tx / 1e9:.1f} GB/s")
+        del gsets, shard_sets
         torch.cuda.empty_cache()
         paths["contention_fp32_512MiB"] = contention_leg(mr, torch, dev, stream)
 

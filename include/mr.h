@@ -43,6 +43,7 @@ typedef enum mr_mode { MR_ONESHOT = 0, MR_TWOSHOT = 1 } mr_mode;
 
 #define MR_MAX_W 16
 #define MR_MAX_PARAMS_PER_LAUNCH 128
+#define MR_MAX_TABLE_W 64 /* ranks in the shard-list gathers (pointer tables ride in the launch arguments) */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mr_status_string(mr_status status);
@@ -98,13 +99,56 @@ mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dt
  *  W       1 .. 65535;  G >= 1 with W % G == 0 (G == W: one node-block).
  *  splits  host array of P element counts (splits[s] == 0 allowed).  Read during the call only.
  *  P       >= 1.  Up to MR_MAX_PARAMS_PER_LAUNCH parameters go in one kernel launch; more are split
- *          into independent launches of up to that many parameters each.
+ *          into independent launches of up to that many parameters each (all validated before the
+ *          first is enqueued).
  *  dtype   any mr_dtype (element size 2 or 4 bytes).
  *  out     device pointer, W*T elements.  Any overlap with src -> MR_ERR_ALIAS.
  *  All offsets are 64-bit; buffers beyond 2^31 bytes are supported.
  */
 mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, const uint64_t* splits,
                                     int P, mr_dtype dtype, void* out, mr_stream stream);
+
+/*
+ * mr_reduce_scatter_chunk / mr_reduce_scatter_sum -- one rank's share of a sum reduce-scatter.
+ *
+ * Two-shot's first phase hands chunk c of the message to owner c (page "Question and suggestions
+ * about custom allreduce", the two-shot reduce-scatter; page "triton_multimem_all_reduce.py", each
+ * rank's slice of cdiv(numel/8, W) 128-bit packs); it is also the gradient half of FSDP sharding.
+ * Chunk c is elements [c*C, min((c+1)*C, n)) with C = ceil(n/W) rounded up to a whole 16 bytes
+ * (8 bf16/fp16 or 4 fp32 elements), so trailing chunks may be short or empty.
+ *
+ * mr_reduce_scatter_chunk: host-only; writes chunk `rank`'s first element and length.
+ * mr_reduce_scatter_sum:   out[j] = the mr_allreduce_sum formula at element offset+j, for j < count,
+ *                          reading only that chunk of each rank buffer.  bufs/W/n/dtype as for
+ *                          mr_allreduce_sum; 0 <= rank < W; out is a device buffer of `count`
+ *                          elements; out may equal bufs[k] + offset exactly (in place), any other
+ *                          overlap with a read chunk -> MR_ERR_ALIAS.  count == 0 is a no-op.
+ */
+mr_status mr_reduce_scatter_chunk(size_t n, int W, mr_dtype dtype, int rank, size_t* offset, size_t* count);
+mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dtype dtype, int rank, void* out,
+                                mr_stream stream);
+
+/*
+ * All-gathers from W separate rank shards (each a device buffer of T elements), one launch each.
+ * Bit copies of any dtype; 1 <= W <= MR_MAX_TABLE_W; shards may not overlap any output (MR_ERR_ALIAS).
+ *
+ * mr_allgather_into_tensor:  rank-major gather (torch.distributed.all_gather_into_tensor's layout):
+ *                            out[r*T + j] = shards[r][j]; out holds W*T elements.
+ * mr_allgather_list:         list-output gather (torch.distributed.all_gather's layout, page "ccl:
+ *                            hierarchical cross-node AllGather ...", the commit adding the list-output
+ *                            all_gather): outs[r][j] = shards[r][j]; outs is a host array of W device
+ *                            buffers of T elements that may not overlap one another.
+ * mr_allgather_param_contig_shards: the param-contiguous placement of mr_allgather_param_contig
+ *                            written straight from the W shards, with no rank-major intermediate (the
+ *                            zero-copy push of enqueue_param_contiguous on the same page):
+ *                            out[O_s*W + r*splits[s] + j] = shards[r][O_s + j].
+ */
+mr_status mr_allgather_into_tensor(const void* const* shards, int W, size_t T, mr_dtype dtype, void* out,
+                                   mr_stream stream);
+mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype dtype, void* const* outs,
+                            mr_stream stream);
+mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int G, const uint64_t* splits, int P,
+                                           mr_dtype dtype, void* out, mr_stream stream);
 
 /*
  * Two-shot workspace.

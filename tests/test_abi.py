@@ -180,3 +180,52 @@ def test_header_is_plain_c_and_links(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "c abi ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_reduce_scatter_chunk_matches_the_oracle_definition(L):
+    import oracle
+
+    off, cnt = ctypes.c_size_t(), ctypes.c_size_t()
+    for dt, name in ((0, "bf16"), (1, "fp16"), (2, "fp32")):
+        for n in (0, 1, 7, 8, 9, 63, 64, 65, 1000, 8_388_608, 8_388_611, 123_457):
+            for W in (1, 2, 3, 8, 16):
+                for rank in range(W):
+                    assert L.mr_reduce_scatter_chunk(n, W, dt, rank, ctypes.byref(off), ctypes.byref(cnt)) == OK
+                    a, b = oracle.reduce_scatter_chunk(n, W, name, rank)
+                    assert (off.value, cnt.value) == (a, b - a), (name, n, W, rank)
+
+
+def test_reduce_scatter_argument_errors(L):
+    off, cnt = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.mr_reduce_scatter_chunk(100, 4, 0, 4, ctypes.byref(off), ctypes.byref(cnt)) == EINVAL
+    assert L.mr_reduce_scatter_chunk(100, 4, 0, -1, ctypes.byref(off), ctypes.byref(cnt)) == EINVAL
+    assert L.mr_reduce_scatter_chunk(100, 4, 3, 0, ctypes.byref(off), ctypes.byref(cnt)) == EDTYPE
+    assert L.mr_reduce_scatter_chunk(100, 17, 0, 0, ctypes.byref(off), ctypes.byref(cnt)) == EINVAL
+    assert L.mr_reduce_scatter_chunk(100, 4, 0, 0, None, ctypes.byref(cnt)) == EINVAL
+    p = _ptrs(0x100000, 0x200000)
+    assert L.mr_reduce_scatter_sum(p, 2, 64, 0, 2, 0x900000, None) == EINVAL
+    assert L.mr_reduce_scatter_sum(p, 2, 64, 3, 0, 0x900000, None) == EDTYPE
+    assert L.mr_reduce_scatter_sum(None, 2, 64, 0, 0, 0x900000, None) == EINVAL
+    # rank 1's chunk of 64 bf16 is elements [32, 64): out 2 bytes into it overlaps without being equal
+    assert L.mr_reduce_scatter_sum(p, 2, 64, 0, 1, 0x100000 + 66, None) == EALIAS
+    assert L.mr_reduce_scatter_sum(p, 2, 0, 0, 1, None, None) == OK     # empty chunk: no-op
+    assert L.mr_reduce_scatter_sum(p, 16, 8, 0, 15, None, None) == OK   # a trailing empty chunk
+
+
+def test_shard_gather_argument_errors(L):
+    sh = _ptrs(0x100000, 0x200000, 0x300000, 0x400000)
+    outs = _ptrs(0x1100000, 0x1200000, 0x1300000, 0x1400000)
+    sp = (ctypes.c_uint64 * 2)(8, 24)
+    big = _ptrs(*[0x100000 * (i + 1) for i in range(65)])
+    assert L.mr_allgather_into_tensor(big, 65, 32, 0, 0x9000000, None) == EINVAL          # over the table size
+    assert L.mr_allgather_into_tensor(sh, 4, 32, 5, 0x9000000, None) == EINVAL             # unknown dtype
+    assert L.mr_allgather_into_tensor(_ptrs(0x100000, None, 0x300000, 0x400000), 4, 32, 0, 0x9000000, None) == EINVAL
+    assert L.mr_allgather_into_tensor(sh, 4, 32, 0, 0x300000 + 2, None) == EALIAS          # out over a shard
+    assert L.mr_allgather_into_tensor(None, 4, 0, 0, None, None) == OK                      # T == 0
+    assert L.mr_allgather_list(sh, 4, 32, 3, _ptrs(0x1100000, 0x1100000 + 64, 0x1300000, 0x1400000), None) == EALIAS
+    assert L.mr_allgather_list(sh, 4, 32, 2, _ptrs(0x1100000, 0x200000 + 4, 0x1300000, 0x1400000), None) == EALIAS
+    assert L.mr_allgather_list(sh, 4, 32, 2, None, None) == EINVAL
+    assert L.mr_allgather_param_contig_shards(sh, 4, 3, sp, 2, 0, 0x9000000, None) == EINVAL  # G does not divide W
+    assert L.mr_allgather_param_contig_shards(sh, 4, 2, sp, 0, 0, 0x9000000, None) == EINVAL  # no params
+    assert L.mr_allgather_param_contig_shards(sh, 4, 2, sp, 2, 0, 0x400000 - 10, None) == EALIAS
+    assert outs is not None

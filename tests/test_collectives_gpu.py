@@ -1,0 +1,86 @@
+"""GPU parity of the reduce-scatter share and the shard-list all-gathers against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import all_gather_amd as mr
+import oracle
+import workloads
+from gpu_util import TORCH_DT, assert_reduce_equal, device, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,W,n", [("bf16", 8, 8_388_608), ("bf16", 3, 100_003), ("fp16", 5, 65_541),
+                                       ("fp32", 16, 1_000_001), ("fp32", 8, 7)])
+def test_reduce_scatter_every_rank(dtype, W, n):
+    bufs = workloads.rank_buffers(70 + W, W, n, dtype, "normal")
+    dbufs = [to_dev(b, dtype) for b in bufs]
+    for rank in range(W):
+        off, cnt = mr.reduce_scatter_chunk(n, W, dtype, rank)
+        assert (off, off + cnt) == oracle.reduce_scatter_chunk(n, W, dtype, rank)
+        if cnt == 0:
+            continue
+        out = torch.empty(cnt, dtype=TORCH_DT[dtype], device=device())
+        mr.reduce_scatter_sum(dbufs, rank, out)
+        torch.cuda.synchronize()
+        assert_reduce_equal(to_bits(out), oracle.reduce_scatter_sum_ref(bufs, dtype, rank), dtype, f"rank {rank}")
+
+
+def test_reduce_scatter_in_place_into_own_chunk():
+    W, n = 4, 40_000
+    bufs = workloads.rank_buffers(75, W, n, "bf16", "uniform")
+    dbufs = [to_dev(b, "bf16") for b in bufs]
+    rank = 2
+    off, cnt = mr.reduce_scatter_chunk(n, W, "bf16", rank)
+    out = dbufs[rank][off:off + cnt]
+    mr.reduce_scatter_sum(dbufs, rank, out)
+    torch.cuda.synchronize()
+    assert_reduce_equal(to_bits(out), oracle.reduce_scatter_sum_ref(bufs, "bf16", rank), "bf16", "in place")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32", "int32"])
+def test_allgather_into_tensor_and_list(dtype):
+    W, T = 8, 3_000_017
+    shards = [workloads.random_bits(76, r, T, dtype) for r in range(W)]
+    dshards = [to_dev(x, dtype) for x in shards]
+    out = torch.empty(W * T, dtype=TORCH_DT[dtype], device=device())
+    mr.allgather_into_tensor(dshards, out)
+    outs = [torch.empty(T, dtype=TORCH_DT[dtype], device=device()) for _ in range(W)]
+    mr.allgather_list(dshards, outs)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), oracle.allgather_into_tensor_ref(shards))
+    for o, want in zip(outs, oracle.allgather_list_ref(shards)):
+        assert np.array_equal(to_bits(o), want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_param_contig_from_shards_config4(dtype):
+    c = workloads.CONFIG4
+    W, G = c["W"], c["G"]
+    splits = [int(x) for x in workloads.log_uniform_splits(c["cfg"], c["P"])]
+    T = sum(splits)
+    shards = [workloads.random_bits(c["cfg"], r, T, dtype) for r in range(W)]
+    dshards = [to_dev(x, dtype) for x in shards]
+    out = torch.empty(W * T, dtype=TORCH_DT[dtype], device=device())
+    mr.allgather_param_contig_shards(dshards, G, splits, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), oracle.allgather_param_contig_shards_ref(shards, G, splits))
+    # and it equals the rank-major path's output
+    src = torch.cat(dshards)
+    out2 = torch.empty_like(out)
+    mr.allgather_param_contig(src, W, G, splits, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+
+
+def test_param_contig_from_shards_ragged_and_many_params():
+    W, G = 6, 2
+    splits = [int(x) for x in workloads.log_uniform_splits(77, 200, lo=1, hi=5000, mult=1)] + [0, 3]
+    T = sum(splits)
+    shards = [workloads.random_bits(77, r, T, "bf16") for r in range(W)]
+    dshards = [to_dev(x, "bf16") for x in shards]
+    out = torch.empty(W * T, dtype=torch.bfloat16, device=device())
+    mr.allgather_param_contig_shards(dshards, G, splits, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), oracle.allgather_param_contig_shards_ref(shards, G, splits))
