@@ -1,0 +1,94 @@
+"""The entry points captured into a HIP graph replay correctly, again and again.
+
+Each op is captured once on a stream that already ran it (so the two-shot workspace exists and no
+allocation happens under capture), then the graph is replayed several times with fresh inputs copied
+into the captured buffers between replays, eager work and synchronisations in between; every replay is
+checked against the CPU oracle.  The two-shot barrier words and flags re-arm themselves inside each
+launch, which is what lets a captured two-shot replay without host-side resets."""
+import numpy as np
+import pytest
+import torch
+
+import all_gather_amd as mr
+import oracle
+import workloads
+from gpu_util import assert_reduce_equal, device, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture(fn, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    return g
+
+
+@pytest.mark.parametrize("mode", ["oneshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid"])
+def test_allreduce_graph_replays(mode):
+    W, n = 8, 2_000_003
+    kind, _, sync = mode.partition(":")
+    s = torch.cuda.Stream()
+    dbufs = [torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(W)]
+    out = torch.empty(n, dtype=torch.bfloat16, device=device())
+    if sync:
+        mr.set_option("twoshot_sync", sync)
+    try:
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            mr.allreduce_sum(dbufs, out, mode=kind)  # warm: creates this stream's workspace
+        torch.cuda.synchronize()
+        g = _capture(lambda: mr.allreduce_sum(dbufs, out, mode=kind), s)
+        for rep in range(5):
+            bufs = workloads.rank_buffers(80 + rep, W, n, "bf16", "normal")
+            for d, b in zip(dbufs, bufs):
+                d.copy_(to_dev(b, "bf16"))
+            out.fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert_reduce_equal(to_bits(out), oracle.allreduce_sum_ref(bufs, "bf16"), "bf16", f"{mode} replay {rep}")
+        if kind == "twoshot":
+            assert mr.workspace_check(s) == 0
+    finally:
+        mr.set_option("twoshot_sync", "tile")
+
+
+def test_gathers_and_reduce_scatter_graph_replays():
+    W, G = 8, 4
+    splits = [8, 4096, 100_000, 24, 777_776]
+    T = sum(splits)
+    s = torch.cuda.Stream()
+    src = torch.empty(W * T, dtype=torch.float16, device=device())
+    shards = [torch.empty(T, dtype=torch.float16, device=device()) for _ in range(W)]
+    out_pc = torch.empty_like(src)
+    out_sh = torch.empty_like(src)
+    outs_list = [torch.empty(T, dtype=torch.float16, device=device()) for _ in range(W)]
+    rs_bufs = [torch.empty(T, dtype=torch.float16, device=device()) for _ in range(W)]
+    off, cnt = mr.reduce_scatter_chunk(T, W, "fp16", 5)
+    rs_out = torch.empty(cnt, dtype=torch.float16, device=device())
+
+    def ops():
+        mr.allgather_param_contig(src, W, G, splits, out_pc)
+        mr.allgather_param_contig_shards(shards, G, splits, out_sh)
+        mr.allgather_list(shards, outs_list)
+        mr.reduce_scatter_sum(rs_bufs, 5, rs_out)
+
+    g = _capture(ops, s)
+    for rep in range(4):
+        hsrc = workloads.gather_source(90 + rep, W, T, "fp16")
+        hsh = [workloads.random_bits(95 + rep, r, T, "fp16") for r in range(W)]
+        hrs = workloads.rank_buffers(99 + rep, W, T, "fp16", "uniform")
+        src.copy_(to_dev(hsrc, "fp16"))
+        for d, h in zip(shards, hsh):
+            d.copy_(to_dev(h, "fp16"))
+        for d, h in zip(rs_bufs, hrs):
+            d.copy_(to_dev(h, "fp16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(out_pc), oracle.allgather_param_contig_ref(hsrc, W, G, splits)), rep
+        assert np.array_equal(to_bits(out_sh), oracle.allgather_param_contig_shards_ref(hsh, G, splits)), rep
+        for o, h in zip(outs_list, hsh):
+            assert np.array_equal(to_bits(o), h), rep
+        assert_reduce_equal(to_bits(rs_out), oracle.reduce_scatter_sum_ref(hrs, "fp16", 5), "fp16", f"rs {rep}")
