@@ -10,7 +10,6 @@
 namespace mr {
 
 constexpr int kBlock = 256;    // element-wise and gather workgroups (4 wave64s)
-constexpr int kRBlock = 1024;  // vector reduce workgroups (16 wave64s): fewer, larger groups ramp up faster
 
 inline int elem_size(mr_dtype d) { return (d == MR_BF16 || d == MR_FP16) ? 2 : 4; }
 

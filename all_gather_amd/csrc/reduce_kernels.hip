@@ -31,8 +31,8 @@ __device__ void raw_buffer_store_v4(i32x4 data, i32x4 rsrc, int voffset, int sof
 #ifndef MR_TS_LOAD_AUX
 #define MR_TS_LOAD_AUX (1 << 4)
 #endif
-#ifndef MR_TS_U1
-#define MR_TS_U1 1
+#ifndef MR_TS_BLOCK
+#define MR_TS_BLOCK 1024
 #endif
 #ifndef MR_TS_RATIO
 #define MR_TS_RATIO 4
@@ -160,33 +160,45 @@ __device__ __forceinline__ void reduce_elem(const RankPtrs& in, char* dst, size_
   store_bits<D::kSize, Dev>(dst + off, D::narrow1(acc));
 }
 
-// U packs per lane (pack i = first + u*kRBlock + lane, i < end), all W*U loads issued before the
-// first add, each result stored through `st(u, pack)`.
-template <typename D, int W, int U, typename Store>
-__device__ __forceinline__ void reduce_packs(const RankPtrs& in, size_t hb, size_t first, size_t end, Store st) {
-  u32x4 v[U][W];
+// Wave-contiguous tile layout: a workgroup of B lanes owns B*P consecutive 16-byte packs starting at
+// `first`; wave w owns P*64 of them and lane l's u-th pack is first + w*64*P + u*64 + l, so each wave
+// instruction covers 1 KiB and a wave's P instructions for one rank cover P KiB contiguous.
+template <int B, int P>
+__device__ __forceinline__ size_t wc_pack(size_t first, int u) {
+  return first + static_cast<size_t>(threadIdx.x >> 6) * (64 * P) + static_cast<size_t>(u) * 64 + (threadIdx.x & 63);
+}
+
+// Reduce a wave-contiguous tile of B*P packs (i < end), PC packs at a time: all W*PC loads in flight,
+// rank by rank, before the adds; each result goes to st(u, pack).
+template <typename D, int W, int B, int P, typename Store>
+__device__ __forceinline__ void reduce_tile(const RankPtrs& in, size_t hb, size_t first, size_t end, Store st) {
+  constexpr int PC = (W <= 8 || P == 1) ? P : 2;  // wide W: fewer packs in flight per lane
+  static_assert(P % PC == 0, "pack groups");
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const size_t i = first + static_cast<size_t>(u) * kRBlock + threadIdx.x;
-    if (i < end) {
+  for (int u0 = 0; u0 < P; u0 += PC) {
+    u32x4 v[PC][W];
 #pragma unroll
-      for (int r = 0; r < W; ++r) v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
-    }
-  }
+    for (int r = 0; r < W; ++r)
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const size_t i = first + static_cast<size_t>(u) * kRBlock + threadIdx.x;
-    if (i < end) {
-      float acc[D::V];
-      D::widen(v[u][0], acc);
-#pragma unroll
-      for (int r = 1; r < W; ++r) {
-        float t[D::V];
-        D::widen(v[u][r], t);
-#pragma unroll
-        for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
+      for (int u = 0; u < PC; ++u) {
+        const size_t i = wc_pack<B, P>(first, u0 + u);
+        if (i < end) v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
       }
-      st(u, D::narrow(acc));
+#pragma unroll
+    for (int u = 0; u < PC; ++u) {
+      const size_t i = wc_pack<B, P>(first, u0 + u);
+      if (i < end) {
+        float acc[D::V];
+        D::widen(v[u][0], acc);
+#pragma unroll
+        for (int r = 1; r < W; ++r) {
+          float t[D::V];
+          D::widen(v[u][r], t);
+#pragma unroll
+          for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
+        }
+        st(u0 + u, i, D::narrow(acc));
+      }
     }
   }
 }
@@ -392,11 +404,16 @@ __device__ __forceinline__ void finish_phase2(Ctrl* ctrl, const TwoShotPlan& pl,
 
 constexpr uint32_t kRatio = MR_TS_RATIO;  // phase-1 tiles per phase-2 tile
 static_assert(kRatio >= 1 && kRatio <= 64, "one lane of the first wave waits for each producer flag");
-// packs per lane in a phase-1 tile: 16-byte loads of W ranks stay in registers, so wide W takes one
-template <int W> struct PhaseOneU { static constexpr int value = W <= 8 ? MR_TS_U1 : 1; };
+// lanes per two-shot workgroup: same-GPU A/B at W=8 bf16, 16 MiB per rank, per-tile flags:
+// 1024 lanes x 1 pack 35.4 us, 512 x 2 39.2 us, 256 x 4 39.8 us (each publish waits for its stores)
+constexpr int kTBlock = MR_TS_BLOCK;
+constexpr int kTile1 = 1024;               // 16-byte packs per phase-1 tile
+constexpr int kP1 = kTile1 / kTBlock;      // packs per lane, phase 1
+constexpr int kP2 = kP1 * kRatio;          // packs per lane, phase 2
+static_assert(kP1 * kTBlock == kTile1, "phase-1 tile is a whole number of packs per lane");
 
 template <typename D, int W>
-__global__ __launch_bounds__(kRBlock) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
+__global__ __launch_bounds__(kTBlock) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
                                                        uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
   uint32_t c, k;
   take_ticket(ctrl, pl, c, k);
@@ -405,29 +422,27 @@ __global__ __launch_bounds__(kRBlock) void twoshot_vec(RankPtrs in, char* out, c
   const size_t cend = c0 + pl.chunk_units < sh.npacks ? c0 + pl.chunk_units : sh.npacks;
   char* stage_body = stage + hb;
   if (k < pl.t1) {
-    constexpr int kU1 = PhaseOneU<W>::value;
-    const size_t first = c0 + static_cast<size_t>(k) * (kRBlock * kU1);
-    const i32x4 rs = make_rsrc(stage_body + first * 16, kRBlock * kU1 * 16);
-    reduce_packs<D, W, kU1>(in, hb, first, cend, [&](int u, const u32x4& o) {
-      raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), rs, (u * kRBlock + threadIdx.x) * 16, 0, kStageStoreAux);
+    const size_t first = c0 + static_cast<size_t>(k) * kTile1;
+    const i32x4 rs = make_rsrc(stage_body + first * 16, kTile1 * 16);
+    reduce_tile<D, W, kTBlock, kP1>(in, hb, first, cend, [&](int, size_t i, const u32x4& o) {
+      raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), rs, static_cast<int>((i - first) * 16), 0, kStageStoreAux);
     });
     if (c == 0 && k == 0) reduce_edges<D, W, true>(in, stage, sh);
     publish_phase1(ctrl, flags, pl, c, k);
   } else {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
-    constexpr uint32_t kU = kRatio * PhaseOneU<W>::value;
-    const size_t first = c0 + static_cast<size_t>(q) * (kRBlock * kU);
-    const i32x4 rs = make_rsrc(stage_body + first * 16, kRBlock * kU * 16);
-    u32x4 v[kU];
+    const size_t first = c0 + static_cast<size_t>(q) * (kTile1 * kRatio);
+    const i32x4 rs = make_rsrc(stage_body + first * 16, kTile1 * kRatio * 16);
+    u32x4 v[kP2];
 #pragma unroll
-    for (uint32_t u = 0; u < kU; ++u) {
-      const size_t i = first + u * kRBlock + threadIdx.x;
-      if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, (u * kRBlock + threadIdx.x) * 16, 0, kStageLoadAux));
+    for (int u = 0; u < kP2; ++u) {
+      const size_t i = wc_pack<kTBlock, kP2>(first, u);
+      if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, static_cast<int>((i - first) * 16), 0, kStageLoadAux));
     }
 #pragma unroll
-    for (uint32_t u = 0; u < kU; ++u) {
-      const size_t i = first + u * kRBlock + threadIdx.x;
+    for (int u = 0; u < kP2; ++u) {
+      const size_t i = wc_pack<kTBlock, kP2>(first, u);
       if (i < cend) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + hb) + i);
     }
     if (c == 0 && q == 0) copy_edges_from_stage<D>(stage, out, sh);
@@ -494,7 +509,7 @@ hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uin
                      const TwoShotPlan& pl, hipStream_t st) {
   const unsigned grid = pl.chunks * (pl.t1 + pl.t2);
   if (sh.vec)
-    hipLaunchKernelGGL((twoshot_vec<D, W>), dim3(grid), dim3(kRBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
+    hipLaunchKernelGGL((twoshot_vec<D, W>), dim3(grid), dim3(kTBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
   else
     hipLaunchKernelGGL((twoshot_elem<D, W>), dim3(grid), dim3(kBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
   return hipGetLastError();
@@ -564,10 +579,7 @@ TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t s
   pl.chunks = static_cast<uint32_t>(W);
   const size_t units = sh.vec ? sh.npacks : sh.n;
   pl.chunk_units = (units + W - 1) / W;
-  static const int kU1[MR_MAX_W + 1] = {1, PhaseOneU<1>::value, PhaseOneU<2>::value, PhaseOneU<3>::value,
-                                        PhaseOneU<4>::value, PhaseOneU<5>::value, PhaseOneU<6>::value,
-                                        PhaseOneU<7>::value, PhaseOneU<8>::value, 1, 1, 1, 1, 1, 1, 1, 1};
-  pl.unit1 = sh.vec ? kRBlock * kU1[W] : kBlock;
+  pl.unit1 = sh.vec ? kTile1 : kBlock;
   pl.ratio = kRatio;
   pl.unit2 = pl.unit1 * kRatio;
   size_t t1 = (pl.chunk_units + pl.unit1 - 1) / pl.unit1;
