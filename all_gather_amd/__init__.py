@@ -26,7 +26,7 @@ STATUS = {
 DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2, "int32": 3}
 MODE_CODE = {"oneshot": 0, "twoshot": 1}
 OPTION_CODE = {"twoshot_sync": 0, "spin_limit": 1}
-TWOSHOT_SYNC = {"tile": 0, "chunk": 1, "grid": 2}
+TWOSHOT_SYNC = {"tile": 0, "chunk": 1, "grid": 2, "last": 3}
 MAX_W = 16
 MAX_PARAMS_PER_LAUNCH = 128
 MAX_TABLE_W = 64
@@ -231,7 +231,7 @@ def workspace_check(stream=None) -> int:
 
 
 def set_option(name: str, value) -> None:
-    """Set a process-wide option: ``twoshot_sync`` ("tile", "chunk", "grid") or ``spin_limit`` (int)."""
+    """Set a process-wide option: ``twoshot_sync`` ("tile", "chunk", "grid", "last") or ``spin_limit`` (int)."""
     if name == "twoshot_sync" and isinstance(value, str):
         value = TWOSHOT_SYNC[value]
     _check(lib().mr_set_option(OPTION_CODE[name], int(value)), "mr_set_option")

@@ -253,7 +253,7 @@ size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
 mr_status mr_set_option(mr_option opt, int64_t value) {
   switch (opt) {
     case MR_OPT_TWOSHOT_SYNC:
-      if (value < MR_TWOSHOT_SYNC_TILE || value > MR_TWOSHOT_SYNC_GRID) return MR_ERR_INVALID_ARG;
+      if (value < MR_TWOSHOT_SYNC_TILE || value > MR_TWOSHOT_SYNC_LAST) return MR_ERR_INVALID_ARG;
       g_twoshot_sync.store(static_cast<uint32_t>(value));
       return MR_OK;
     case MR_OPT_SPIN_LIMIT:

@@ -24,10 +24,9 @@ constexpr size_t kCtrlBytes = 16384;
 
 struct Ctrl {
   uint32_t claim[MR_MAX_W][64];  // per-chunk ticket counters (start order of that chunk's workgroups)
-  uint32_t done1[MR_MAX_W][64];  // per-chunk phase-1 completions (chunk barrier)
+  uint32_t done1[MR_MAX_W][64];  // per-chunk phase-1 completions (chunk and grid barriers)
   uint32_t done2[MR_MAX_W][64];  // per-chunk phase-2 completions (resets the chunk words)
   uint32_t gclaim[64];           // grid ticket counter (grid barrier)
-  uint32_t gdone1[64];           // grid phase-1 completions
   uint32_t gdone2[64];           // grid phase-2 completions
   uint32_t err[64];              // bit 0: a wait gave up after the spin limit
 };
@@ -43,6 +42,7 @@ enum TwoShotSync : uint32_t {
   kSyncTile = 0,   // per-tile producer flags: a phase-2 tile waits for the phase-1 tiles it copies
   kSyncChunk = 1,  // per-chunk barrier: waits for every phase-1 tile of its chunk
   kSyncGrid = 2,   // grid barrier: waits for every phase-1 tile of every chunk
+  kSyncLast = 3,   // no waits: the workgroup that completes a group of phase-1 tiles copies that group
 };
 
 struct RankPtrs {

@@ -169,7 +169,7 @@ __device__ __forceinline__ size_t wc_pack(size_t first, int u) {
 }
 
 // Reduce a wave-contiguous tile of B*P packs (i < end), PC packs at a time: all W*PC loads in flight,
-// rank by rank, before the adds; each result goes to st(u, pack).
+// rank by rank, before the adds; each result goes to st(u, i, pack).
 template <typename D, int W, int B, int P, typename Store>
 __device__ __forceinline__ void reduce_tile(const RankPtrs& in, size_t hb, size_t first, size_t end, Store st) {
   constexpr int PC = (W <= 8 || P == 1) ? P : 2;  // wide W: fewer packs in flight per lane
@@ -224,19 +224,15 @@ __device__ __forceinline__ void copy_edges_from_stage(const char* stage, char* d
 
 // ---------------------------------------------------------------------------------------- one-shot
 
-// One-shot tile: kOneShotBlock lanes x U packs.  Wave w of the workgroup owns U*64 consecutive packs
-// and loads them rank by rank (the U loads of one rank are adjacent 1 KiB pieces), so each wave reads
-// U KiB contiguous per rank buffer at a time.  Same-GPU A/B at W=8 bf16, 16 MiB per rank: 256 lanes x
-// 4 packs wave-contiguous 26.2 us; 512 x 1 interleaved 26.3; 512 x 2 interleaved 26.5; 1024 x 2
+// One-shot tile: kOneShotBlock lanes x U packs in the wave-contiguous layout, so each wave reads U KiB
+// contiguous per rank buffer at a time.  Same-GPU A/B at W=8 bf16, 16 MiB per rank: 256 lanes x 4 packs
+// wave-contiguous 26.2 us; 512 x 1 lane-interleaved 26.3; 512 x 2 interleaved 26.5; 1024 x 2
 // wave-contiguous 26.9; 512 x 2 wave-contiguous 27.0; 1024 x 1 interleaved 27.5.
 #ifndef MR_OS_BLOCK
 #define MR_OS_BLOCK 256
 #endif
 #ifndef MR_OS_U
 #define MR_OS_U 4
-#endif
-#ifndef MR_OS_WAVE_CONTIG
-#define MR_OS_WAVE_CONTIG 1
 #endif
 constexpr int kOneShotBlock = MR_OS_BLOCK;
 template <int W> struct OneShotU { static constexpr int value = W <= 8 ? MR_OS_U : 1; };
@@ -245,36 +241,10 @@ template <typename D, int W>
 __global__ __launch_bounds__(kOneShotBlock) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
   constexpr int U = OneShotU<W>::value;
   const size_t hb = sh.head * D::kSize;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    // pack of (lane, u): wave-contiguous first + u*64, or lane-interleaved first + u*kOneShotBlock
-    constexpr size_t kStep = MR_OS_WAVE_CONTIG ? 64 : kOneShotBlock;
-    const size_t first = t * (kOneShotBlock * U) + (MR_OS_WAVE_CONTIG ? static_cast<size_t>(wave) * (64 * U) + lane : threadIdx.x);
-    u32x4 v[U][W];
-#pragma unroll
-    for (int r = 0; r < W; ++r)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const size_t i = first + u * kStep;
-        if (i < sh.npacks) v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t i = first + u * kStep;
-      if (i < sh.npacks) {
-        float acc[D::V];
-        D::widen(v[u][0], acc);
-#pragma unroll
-        for (int r = 1; r < W; ++r) {
-          float tv[D::V];
-          D::widen(v[u][r], tv);
-#pragma unroll
-          for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + tv[k];
-        }
-        __builtin_nontemporal_store(D::narrow(acc), reinterpret_cast<u32x4*>(out + hb) + i);
-      }
-    }
-  }
+  u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
+  for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x)
+    reduce_tile<D, W, kOneShotBlock, U>(in, hb, t * (kOneShotBlock * U), sh.npacks,
+                                        [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); });
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
 
@@ -311,7 +281,10 @@ __global__ __launch_bounds__(kBlock) void oneshot_elem(RankPtrs in, char* out, s
 //   tile  -- phase-2 tile q of chunk c waits for the flags of phase-1 tiles [q*ratio, (q+1)*ratio) of
 //            chunk c and clears them; the claim counter is cleared by the holder of the last ticket.
 //   chunk -- waits until done1[c] counts all t1 phase-1 tiles of chunk c.
-//   grid  -- waits until gdone1 counts every phase-1 tile of every chunk (one ticket counter).
+//   grid  -- waits until done1[x] counts all t1 phase-1 tiles of every chunk x (one ticket counter
+//            orders every workgroup; lanes 0..W-1 of the first wave wait for one chunk each).
+//   last  -- no phase-2 workgroups and no waiting: flags[c*t2 + q] counts the releases of group q of
+//            chunk c, and the workgroup whose release completes the group re-arms it and copies it.
 // In every mode the words return to zero by the end of the launch, so back-to-back launches on one
 // stream need no host reset.
 
@@ -347,13 +320,11 @@ __device__ __forceinline__ void take_ticket(Ctrl* ctrl, const TwoShotPlan& pl, u
 __device__ __forceinline__ void publish_phase1(Ctrl* ctrl, uint32_t* flags, const TwoShotPlan& pl, uint32_t c, uint32_t k) {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's write-through stage stores are acknowledged
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && pl.sync != kSyncLast) {
     if (pl.sync == kSyncTile)
       __hip_atomic_store(&flags[static_cast<size_t>(c) * pl.t1 + k], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else if (pl.sync == kSyncChunk)
+    else  // chunk and grid barriers count per chunk (W words instead of one contended word)
       __hip_atomic_fetch_add(&ctrl->done1[c][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      __hip_atomic_fetch_add(&ctrl->gdone1[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -377,10 +348,13 @@ __device__ __forceinline__ void wait_phase1(Ctrl* ctrl, uint32_t* flags, const T
         __hip_atomic_fetch_or(&ctrl->err[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // consumed: re-arm
     }
-  } else if (threadIdx.x == 0) {
-    const bool ok = pl.sync == kSyncChunk ? wait_at_least(&ctrl->done1[c][0], pl.t1, pl.spin_limit)
-                                          : wait_at_least(&ctrl->gdone1[0], pl.chunks * pl.t1, pl.spin_limit);
-    if (!ok) __hip_atomic_fetch_or(&ctrl->err[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (pl.sync == kSyncChunk) {
+    if (threadIdx.x == 0 && !wait_at_least(&ctrl->done1[c][0], pl.t1, pl.spin_limit))
+      __hip_atomic_fetch_or(&ctrl->err[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (threadIdx.x < pl.chunks) {
+    // grid barrier: lane x of the first wave waits for chunk x, so the W waits overlap
+    if (!wait_at_least(&ctrl->done1[threadIdx.x][0], pl.t1, pl.spin_limit))
+      __hip_atomic_fetch_or(&ctrl->err[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
@@ -396,7 +370,8 @@ __device__ __forceinline__ void finish_phase2(Ctrl* ctrl, const TwoShotPlan& pl,
   } else {
     const uint32_t d = __hip_atomic_fetch_add(&ctrl->gdone2[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == pl.chunks * pl.t2 - 1) {
-      __hip_atomic_store(&ctrl->gdone1[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t x = 0; x < pl.chunks; ++x)
+        __hip_atomic_store(&ctrl->done1[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&ctrl->gdone2[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -412,68 +387,113 @@ constexpr int kP1 = kTile1 / kTBlock;      // packs per lane, phase 1
 constexpr int kP2 = kP1 * kRatio;          // packs per lane, phase 2
 static_assert(kP1 * kTBlock == kTile1, "phase-1 tile is a whole number of packs per lane");
 
+// Phase 2 of one group: copy phase-2 tile q of chunk c (ratio phase-1 tiles) from the stage to out with
+// device-scope stage loads.
+template <typename D>
+__device__ __forceinline__ void copy_group(char* out, char* stage, const ReduceShape& sh, size_t first, size_t cend,
+                                           bool with_edges) {
+  const size_t hb = sh.head * D::kSize;
+  const i32x4 rs = make_rsrc(stage + hb + first * 16, kTile1 * kRatio * 16);
+  u32x4 v[kP2];
+#pragma unroll
+  for (int u = 0; u < kP2; ++u) {
+    const size_t i = wc_pack<kTBlock, kP2>(first, u);
+    if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, static_cast<int>((i - first) * 16), 0, kStageLoadAux));
+  }
+#pragma unroll
+  for (int u = 0; u < kP2; ++u) {
+    const size_t i = wc_pack<kTBlock, kP2>(first, u);
+    if (i < cend) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + hb) + i);
+  }
+  if (with_edges) copy_edges_from_stage<D>(stage, out, sh);
+}
+
+// Last-arriver hand-off: after publishing its tile, the workgroup bumps the arrival count of its group
+// of `ratio` tiles; the one that completes the group (it has seen every other member's release in the
+// atomic's order) re-arms the count and copies the group.  Nobody waits.
+__device__ __forceinline__ bool arrive_last(uint32_t* counts, const TwoShotPlan& pl, uint32_t c, uint32_t k) {
+  __shared__ uint32_t s_last;
+  if (threadIdx.x == 0) {
+    const uint32_t q = k / pl.ratio;
+    const uint32_t members = (q + 1) * pl.ratio <= pl.t1 ? pl.ratio : pl.t1 - q * pl.ratio;
+    uint32_t* cnt = &counts[static_cast<size_t>(c) * pl.t2 + q];
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == members - 1;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  return s_last != 0;
+}
+
 template <typename D, int W>
 __global__ __launch_bounds__(kTBlock) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
                                                        uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
   uint32_t c, k;
-  take_ticket(ctrl, pl, c, k);
+  if (pl.sync == kSyncLast) {  // phase-1 workgroups only; consecutive workgroups take one chunk's tiles
+    c = blockIdx.x / pl.t1;
+    k = blockIdx.x % pl.t1;
+  } else {
+    take_ticket(ctrl, pl, c, k);
+  }
   const size_t hb = sh.head * D::kSize;
   const size_t c0 = static_cast<size_t>(c) * pl.chunk_units;
   const size_t cend = c0 + pl.chunk_units < sh.npacks ? c0 + pl.chunk_units : sh.npacks;
-  char* stage_body = stage + hb;
   if (k < pl.t1) {
     const size_t first = c0 + static_cast<size_t>(k) * kTile1;
-    const i32x4 rs = make_rsrc(stage_body + first * 16, kTile1 * 16);
+    const i32x4 rs = make_rsrc(stage + hb + first * 16, kTile1 * 16);
     reduce_tile<D, W, kTBlock, kP1>(in, hb, first, cend, [&](int, size_t i, const u32x4& o) {
       raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), rs, static_cast<int>((i - first) * 16), 0, kStageStoreAux);
     });
     if (c == 0 && k == 0) reduce_edges<D, W, true>(in, stage, sh);
     publish_phase1(ctrl, flags, pl, c, k);
+    if (pl.sync == kSyncLast && arrive_last(flags, pl, c, k)) {
+      const uint32_t q = k / pl.ratio;
+      copy_group<D>(out, stage, sh, c0 + static_cast<size_t>(q) * (kTile1 * kRatio), cend, c == 0 && q == 0);
+    }
   } else {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
-    const size_t first = c0 + static_cast<size_t>(q) * (kTile1 * kRatio);
-    const i32x4 rs = make_rsrc(stage_body + first * 16, kTile1 * kRatio * 16);
-    u32x4 v[kP2];
-#pragma unroll
-    for (int u = 0; u < kP2; ++u) {
-      const size_t i = wc_pack<kTBlock, kP2>(first, u);
-      if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, static_cast<int>((i - first) * 16), 0, kStageLoadAux));
-    }
-#pragma unroll
-    for (int u = 0; u < kP2; ++u) {
-      const size_t i = wc_pack<kTBlock, kP2>(first, u);
-      if (i < cend) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + hb) + i);
-    }
-    if (c == 0 && q == 0) copy_edges_from_stage<D>(stage, out, sh);
+    copy_group<D>(out, stage, sh, c0 + static_cast<size_t>(q) * (kTile1 * kRatio), cend, c == 0 && q == 0);
     finish_phase2(ctrl, pl, c);
   }
 }
 
 // Element-wise two-shot for pointers that do not share one 16-byte alignment (one element per unit).
+template <typename D>
+__device__ __forceinline__ void copy_group_elem(char* out, const char* stage, size_t first, size_t cend) {
+#pragma unroll
+  for (uint32_t u = 0; u < kRatio; ++u) {
+    const size_t e = first + u * kBlock + threadIdx.x;
+    if (e < cend) {
+      const size_t off = e * D::kSize;
+      store_bits<D::kSize, false>(out + off, load_bits<D::kSize, true>(stage + off));
+    }
+  }
+}
+
 template <typename D, int W>
 __global__ __launch_bounds__(kBlock) void twoshot_elem(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
                                                        uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
   uint32_t c, k;
-  take_ticket(ctrl, pl, c, k);
+  if (pl.sync == kSyncLast) {
+    c = blockIdx.x / pl.t1;
+    k = blockIdx.x % pl.t1;
+  } else {
+    take_ticket(ctrl, pl, c, k);
+  }
   const size_t c0 = static_cast<size_t>(c) * pl.chunk_units;
   const size_t cend = c0 + pl.chunk_units < sh.n ? c0 + pl.chunk_units : sh.n;
   if (k < pl.t1) {
     const size_t e = c0 + static_cast<size_t>(k) * kBlock + threadIdx.x;
     if (e < cend) reduce_elem<D, W, true>(in, stage, e);
     publish_phase1(ctrl, flags, pl, c, k);
+    if (pl.sync == kSyncLast && arrive_last(flags, pl, c, k))
+      copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(k / pl.ratio) * (kBlock * kRatio), cend);
   } else {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
-    const size_t first = c0 + static_cast<size_t>(q) * (kBlock * kRatio);
-#pragma unroll
-    for (uint32_t u = 0; u < kRatio; ++u) {
-      const size_t e = first + u * kBlock + threadIdx.x;
-      if (e < cend) {
-        const size_t off = e * D::kSize;
-        store_bits<D::kSize, false>(out + off, load_bits<D::kSize, true>(stage + off));
-      }
-    }
+    copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(q) * (kBlock * kRatio), cend);
     finish_phase2(ctrl, pl, c);
   }
 }
@@ -507,7 +527,7 @@ hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, hipSt
 template <typename D, int W>
 hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uint32_t* flags, const ReduceShape& sh,
                      const TwoShotPlan& pl, hipStream_t st) {
-  const unsigned grid = pl.chunks * (pl.t1 + pl.t2);
+  const unsigned grid = pl.chunks * (pl.sync == kSyncLast ? pl.t1 : pl.t1 + pl.t2);
   if (sh.vec)
     hipLaunchKernelGGL((twoshot_vec<D, W>), dim3(grid), dim3(kTBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
   else

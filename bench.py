@@ -215,7 +215,7 @@ def main():
         # two-shot, rotating sets, under each phase hand-off
         two = [mr.prepare_allreduce(b, o, "twoshot") for b, o in sets]
         actual2 = (W + 3) * n * s
-        for sync in ("tile", "chunk", "grid"):
+        for sync in ("tile", "chunk", "grid", "last"):
             mr.set_option("twoshot_sync", sync)
             two[0]()
             torch.cuda.synchronize()

@@ -183,7 +183,9 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  *                         phase-1 tiles it copies (the per-block flag hand-off of the custom
  *                         allreduce page's block_barrier, applied to the two phases);
  *   MR_TWOSHOT_SYNC_CHUNK per-chunk barrier: waits for every phase-1 tile of its 1/W chunk;
- *   MR_TWOSHOT_SYNC_GRID  grid barrier: waits for every phase-1 tile of every chunk.
+ *   MR_TWOSHOT_SYNC_GRID  grid barrier: waits for every phase-1 tile of every chunk;
+ *   MR_TWOSHOT_SYNC_LAST  no waiting: each group of phase-1 tiles counts its releases, and the
+ *                         workgroup whose release completes the group copies it.
  * MR_OPT_SPIN_LIMIT    polls a waiting workgroup makes before it gives up and sets the workspace error
  *                      word (see mr_workspace_check); default 2^22.  A value of 0 makes every wait
  *                      that is not already satisfied give up at once (for testing error handling).
@@ -194,6 +196,7 @@ typedef enum mr_option { MR_OPT_TWOSHOT_SYNC = 0, MR_OPT_SPIN_LIMIT = 1 } mr_opt
 #define MR_TWOSHOT_SYNC_TILE 0
 #define MR_TWOSHOT_SYNC_CHUNK 1
 #define MR_TWOSHOT_SYNC_GRID 2
+#define MR_TWOSHOT_SYNC_LAST 3
 mr_status mr_set_option(mr_option opt, int64_t value);
 mr_status mr_get_option(mr_option opt, int64_t* value);
 

@@ -135,11 +135,11 @@ def test_options_validate_and_round_trip(L):
     v = ctypes.c_int64(-7)
     assert L.mr_get_option(0, ctypes.byref(v)) == OK and v.value == 0          # tile flags by default
     assert L.mr_get_option(1, ctypes.byref(v)) == OK and v.value == 1 << 22
-    assert L.mr_set_option(0, 3) == EINVAL and L.mr_set_option(0, -1) == EINVAL
+    assert L.mr_set_option(0, 4) == EINVAL and L.mr_set_option(0, -1) == EINVAL
     assert L.mr_set_option(1, -1) == EINVAL and L.mr_set_option(1, 2 ** 32) == EINVAL
     assert L.mr_set_option(9, 0) == EINVAL and L.mr_get_option(9, ctypes.byref(v)) == EINVAL
     assert L.mr_get_option(0, None) == EINVAL
-    for sync in ("chunk", "grid", "tile"):
+    for sync in ("chunk", "grid", "last", "tile"):
         mr.set_option("twoshot_sync", sync)
         assert mr.get_option("twoshot_sync") == sync
     mr.set_option("spin_limit", 1000)

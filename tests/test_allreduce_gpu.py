@@ -11,8 +11,10 @@ import workloads
 from gpu_util import TORCH_DT, assert_reduce_equal, device, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
-# one-shot, and two-shot under each phase hand-off (per-tile flags, per-chunk barrier, grid barrier)
-MODES = ("oneshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid")
+# one-shot, and two-shot under each phase hand-off (per-tile flags, per-chunk barrier, grid barrier,
+# last arriver of each tile group)
+MODES = ("oneshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid", "twoshot:last")
+TWOSHOT_MODES = MODES[1:]
 
 
 def _call(dbufs, out, mode):
@@ -146,7 +148,7 @@ def test_oneshot_equals_twoshot_and_is_deterministic():
     assert mr.workspace_check() == 0
 
 
-@pytest.mark.parametrize("sync", ["tile", "chunk", "grid"])
+@pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last"])
 def test_twoshot_stale_stage_is_never_read(sync):
     """Two input sets alternate on one caller-owned workspace, so when a call starts its stage still
     holds the previous call's (different) sums: a phase-2 copy that ran ahead of its phase-1 producer
@@ -232,7 +234,7 @@ def test_twoshot_on_two_streams_concurrently():
     for rep in range(30):
         for k in range(2):
             with torch.cuda.stream(streams[k]):
-                _call(dsets[k], outs[k], MODES[1 + rep % 3])
+                _call(dsets[k], outs[k], TWOSHOT_MODES[rep % len(TWOSHOT_MODES)])
     torch.cuda.synchronize()
     for k in range(2):
         assert_reduce_equal(to_bits(outs[k]), wants[k], "bf16", f"stream {k}")

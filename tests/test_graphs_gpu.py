@@ -24,7 +24,7 @@ def _capture(fn, stream):
     return g
 
 
-@pytest.mark.parametrize("mode", ["oneshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid"])
+@pytest.mark.parametrize("mode", ["oneshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid", "twoshot:last"])
 def test_allreduce_graph_replays(mode):
     W, n = 8, 2_000_003
     kind, _, sync = mode.partition(":")
