@@ -25,8 +25,9 @@ STATUS = {
 }
 DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2, "int32": 3}
 MODE_CODE = {"oneshot": 0, "twoshot": 1}
-OPTION_CODE = {"twoshot_sync": 0, "spin_limit": 1}
-TWOSHOT_SYNC = {"tile": 0, "chunk": 1, "grid": 2, "last": 3}
+OPTION_CODE = {"twoshot_sync": 0, "spin_limit": 1, "tile_shape": 2}
+TWOSHOT_SYNC = {"tile": 0, "chunk": 1, "grid": 2, "last": 3, "auto": 4}
+TILE_SHAPE = {"auto": 0, "wide": 1, "medium": 2, "narrow": 3}
 MAX_W = 16
 MAX_PARAMS_PER_LAUNCH = 128
 MAX_TABLE_W = 64
@@ -231,9 +232,12 @@ def workspace_check(stream=None) -> int:
 
 
 def set_option(name: str, value) -> None:
-    """Set a process-wide option: ``twoshot_sync`` ("tile", "chunk", "grid", "last") or ``spin_limit`` (int)."""
+    """Set a process-wide option: ``twoshot_sync`` ("auto", "tile", "chunk", "grid", "last"), ``spin_limit`` (int)
+    or ``tile_shape`` ("auto", "wide", "medium", "narrow")."""
     if name == "twoshot_sync" and isinstance(value, str):
         value = TWOSHOT_SYNC[value]
+    if name == "tile_shape" and isinstance(value, str):
+        value = TILE_SHAPE[value]
     _check(lib().mr_set_option(OPTION_CODE[name], int(value)), "mr_set_option")
 
 
@@ -242,6 +246,8 @@ def get_option(name: str):
     _check(lib().mr_get_option(OPTION_CODE[name], ctypes.byref(v)), "mr_get_option")
     if name == "twoshot_sync":
         return {c: k for k, c in TWOSHOT_SYNC.items()}[v.value]
+    if name == "tile_shape":
+        return {c: k for k, c in TILE_SHAPE.items()}[v.value]
     return int(v.value)
 
 

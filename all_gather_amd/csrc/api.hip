@@ -27,7 +27,8 @@ uint32_t env_u32(const char* name, uint32_t dflt) {
 
 // Process-wide options (mr_set_option); defaults may be overridden by the environment at load.
 std::atomic<uint32_t> g_spin_limit{env_u32("MR_SPIN_LIMIT", 1u << 22)};
-std::atomic<uint32_t> g_twoshot_sync{env_u32("MR_TWOSHOT_SYNC", mr::kSyncTile)};
+std::atomic<uint32_t> g_twoshot_sync{env_u32("MR_TWOSHOT_SYNC", mr::kSyncAuto)};
+std::atomic<uint32_t> g_tile_shape{env_u32("MR_TILE_SHAPE", mr::kShapeAuto)};
 const bool g_trace = env_u32("MR_TRACE", 0) != 0;
 
 mr_status hip_fail(hipError_t e) {
@@ -136,12 +137,14 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
   }
   hipError_t e;
   if (mode == MR_ONESHOT) {
+    const uint32_t shape = mr::oneshot_shape(sh.npacks, es, g_tile_shape.load());
     if (g_trace)
-      std::fprintf(stderr, "[mr] allreduce oneshot W=%d n=%zu dtype=%d vec=%d head=%zu packs=%zu\n", W, n,
-                   static_cast<int>(dtype), sh.vec, sh.head, sh.npacks);
-    e = mr::launch_oneshot(in, W, dtype, out, sh, st);
+      std::fprintf(stderr, "[mr] allreduce oneshot W=%d n=%zu dtype=%d vec=%d head=%zu packs=%zu shape=%u\n", W, n,
+                   static_cast<int>(dtype), sh.vec, sh.head, sh.npacks, shape);
+    e = mr::launch_oneshot(in, W, dtype, out, sh, shape, st);
   } else {
-    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, g_twoshot_sync.load(), g_spin_limit.load());
+    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, mr::twoshot_sync_for(n * static_cast<size_t>(es), g_twoshot_sync.load()),
+                                                 g_spin_limit.load(), g_tile_shape.load());
     const uint64_t grid = static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
     if (grid >= (1ull << 24)) return MR_ERR_INVALID_ARG;
     const size_t flags_needed = static_cast<size_t>(pl.chunks) * pl.t1;
@@ -152,8 +155,8 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
     char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (sh.vec ? (po & 15u) : 0);
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws.base + mr::kCtrlBytes);
     if (g_trace)
-      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu t1=%u t2=%u\n", W, n,
-                   static_cast<int>(dtype), sh.vec, pl.sync, pl.chunk_units, pl.t1, pl.t2);
+      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu tile=%zu t1=%u t2=%u\n",
+                   W, n, static_cast<int>(dtype), sh.vec, pl.sync, pl.chunk_units, pl.unit1, pl.t1, pl.t2);
     e = mr::launch_twoshot(in, W, dtype, out, stage, reinterpret_cast<mr::Ctrl*>(ws.base), flags, sh, pl, st);
   }
   return e == hipSuccess ? MR_OK : hip_fail(e);
@@ -253,12 +256,16 @@ size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
 mr_status mr_set_option(mr_option opt, int64_t value) {
   switch (opt) {
     case MR_OPT_TWOSHOT_SYNC:
-      if (value < MR_TWOSHOT_SYNC_TILE || value > MR_TWOSHOT_SYNC_LAST) return MR_ERR_INVALID_ARG;
+      if (value < MR_TWOSHOT_SYNC_TILE || value > MR_TWOSHOT_SYNC_AUTO) return MR_ERR_INVALID_ARG;
       g_twoshot_sync.store(static_cast<uint32_t>(value));
       return MR_OK;
     case MR_OPT_SPIN_LIMIT:
       if (value < 0 || value > 0xffffffffll) return MR_ERR_INVALID_ARG;
       g_spin_limit.store(static_cast<uint32_t>(value));
+      return MR_OK;
+    case MR_OPT_TILE_SHAPE:
+      if (value < MR_TILE_AUTO || value > MR_TILE_NARROW) return MR_ERR_INVALID_ARG;
+      g_tile_shape.store(static_cast<uint32_t>(value));
       return MR_OK;
     default:
       return MR_ERR_INVALID_ARG;
@@ -270,6 +277,7 @@ mr_status mr_get_option(mr_option opt, int64_t* value) {
   switch (opt) {
     case MR_OPT_TWOSHOT_SYNC: *value = g_twoshot_sync.load(); return MR_OK;
     case MR_OPT_SPIN_LIMIT: *value = g_spin_limit.load(); return MR_OK;
+    case MR_OPT_TILE_SHAPE: *value = g_tile_shape.load(); return MR_OK;
     default: return MR_ERR_INVALID_ARG;
   }
 }

@@ -43,7 +43,42 @@ enum TwoShotSync : uint32_t {
   kSyncChunk = 1,  // per-chunk barrier: waits for every phase-1 tile of its chunk
   kSyncGrid = 2,   // grid barrier: waits for every phase-1 tile of every chunk
   kSyncLast = 3,   // no waits: the workgroup that completes a group of phase-1 tiles copies that group
+  kSyncAuto = 4,   // chosen from the message size (twoshot_sync_for)
 };
+
+// Tile shape of the reduce kernels (MR_OPT_TILE_SHAPE).  Wide tiles suit large messages; small ones
+// need narrower tiles so that the grid still holds enough workgroups to keep every CU busy.
+enum TileShape : uint32_t { kShapeAuto = 0, kShapeWide = 1, kShapeMedium = 2, kShapeNarrow = 3 };
+
+// Auto choices, from graph-replayed sweeps at W=8 over 64 KiB .. 64 MiB per rank (bf16 and fp32):
+// the narrow one-shot tile halves the time of messages below 1 MiB against the wide one (3.0 vs
+// 5.4 us at 64 KiB), the medium one leads from 1 to 2-4 MiB, and the wide one from 4 MiB (fp32) or
+// 8 MiB (bf16) up.  For two-shot, 256-pack tiles lead below 2 MiB and 1024-pack tiles above.
+inline uint32_t oneshot_shape(size_t npacks, int elem_size, uint32_t forced) {
+  if (forced != kShapeAuto) return forced;
+  const size_t wide_from = elem_size == 4 ? (size_t(1) << 18) : (size_t(1) << 19);
+  if (npacks >= wide_from) return kShapeWide;          // 256 lanes x 4 packs
+  if (npacks >= (size_t(1) << 16)) return kShapeMedium;  // 256 lanes x 1 pack
+  return kShapeNarrow;                                   // 64 lanes x 1 pack
+}
+// Two-shot phase-1 tile (lanes = packs per tile) for a message of `npacks` packs.  The grid barrier
+// orders every workgroup through one ticket counter (about 11.6 ns per same-address atomic), so it
+// keeps the tile count low: 256-pack tiles only below 64 Ki packs, never 64-pack ones.
+inline uint32_t twoshot_tile_packs(size_t npacks, uint32_t sync, uint32_t forced) {
+  const bool grid = sync == kSyncGrid;
+  const uint32_t shape = forced != kShapeAuto                              ? forced
+                         : npacks >= (size_t(1) << (grid ? 16 : 17))      ? kShapeWide
+                         : grid || npacks >= (size_t(1) << 13)            ? kShapeMedium
+                                                                          : kShapeNarrow;
+  return shape == kShapeNarrow ? 64u : shape == kShapeMedium ? 256u : 1024u;
+}
+// Two-shot hand-off under MR_TWOSHOT_SYNC_AUTO: the last-arriver hand-off leads below 16 MiB per rank
+// (12.3 vs 16.4 us for per-tile flags at 4 MiB, W=8 bf16), per-tile flags above (125 vs 149 us at
+// 64 MiB).
+inline uint32_t twoshot_sync_for(size_t bytes, uint32_t sync) {
+  if (sync != kSyncAuto) return sync;
+  return bytes < (size_t(16) << 20) ? kSyncLast : kSyncTile;
+}
 
 struct RankPtrs {
   const char* p[MR_MAX_W];
@@ -74,10 +109,10 @@ struct TwoShotPlan {
 };
 
 hipError_t launch_oneshot(const RankPtrs& in, int W, mr_dtype dt, char* out, const ReduceShape& sh,
-                          hipStream_t st);
+                          uint32_t shape, hipStream_t st);  // shape: TileShape, already resolved
 hipError_t launch_twoshot(const RankPtrs& in, int W, mr_dtype dt, char* out, char* stage, Ctrl* ctrl,
                           uint32_t* flags, const ReduceShape& sh, const TwoShotPlan& pl, hipStream_t st);
-TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit);
+TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit, uint32_t shape);
 hipError_t launch_zero_words(void* p, size_t words, hipStream_t st);
 
 // ---------------------------------------------------------------------------------- param-contiguous

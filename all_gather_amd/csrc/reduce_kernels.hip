@@ -224,10 +224,11 @@ __device__ __forceinline__ void copy_edges_from_stage(const char* stage, char* d
 
 // ---------------------------------------------------------------------------------------- one-shot
 
-// One-shot tile: kOneShotBlock lanes x U packs in the wave-contiguous layout, so each wave reads U KiB
-// contiguous per rank buffer at a time.  Same-GPU A/B at W=8 bf16, 16 MiB per rank: 256 lanes x 4 packs
-// wave-contiguous 26.2 us; 512 x 1 lane-interleaved 26.3; 512 x 2 interleaved 26.5; 1024 x 2
-// wave-contiguous 26.9; 512 x 2 wave-contiguous 27.0; 1024 x 1 interleaved 27.5.
+// One-shot tile shapes (lanes x packs per lane, wave-contiguous).  The wide tile is the large-message
+// shape: same-GPU A/B at W=8 bf16, 16 MiB per rank: 256 lanes x 4 packs wave-contiguous 26.2 us; 512 x 1
+// lane-interleaved 26.3; 512 x 2 interleaved 26.5; 1024 x 2 wave-contiguous 26.9; 512 x 2
+// wave-contiguous 27.0; 1024 x 1 interleaved 27.5.  Smaller messages take the medium (256 x 1) or
+// narrow (64 x 1) tile so that the grid still has enough workgroups to keep every CU's loads in flight.
 #ifndef MR_OS_BLOCK
 #define MR_OS_BLOCK 256
 #endif
@@ -237,14 +238,13 @@ __device__ __forceinline__ void copy_edges_from_stage(const char* stage, char* d
 constexpr int kOneShotBlock = MR_OS_BLOCK;
 template <int W> struct OneShotU { static constexpr int value = W <= 8 ? MR_OS_U : 1; };
 
-template <typename D, int W>
-__global__ __launch_bounds__(kOneShotBlock) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
-  constexpr int U = OneShotU<W>::value;
+template <typename D, int W, int B, int U>
+__global__ __launch_bounds__(B) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
   const size_t hb = sh.head * D::kSize;
   u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
   for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x)
-    reduce_tile<D, W, kOneShotBlock, U>(in, hb, t * (kOneShotBlock * U), sh.npacks,
-                                        [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); });
+    reduce_tile<D, W, B, U>(in, hb, t * (B * U), sh.npacks,
+                            [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); });
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
 
@@ -379,30 +379,29 @@ __device__ __forceinline__ void finish_phase2(Ctrl* ctrl, const TwoShotPlan& pl,
 
 constexpr uint32_t kRatio = MR_TS_RATIO;  // phase-1 tiles per phase-2 tile
 static_assert(kRatio >= 1 && kRatio <= 64, "one lane of the first wave waits for each producer flag");
-// lanes per two-shot workgroup: same-GPU A/B at W=8 bf16, 16 MiB per rank, per-tile flags:
-// 1024 lanes x 1 pack 35.4 us, 512 x 2 39.2 us, 256 x 4 39.8 us (each publish waits for its stores)
+// Phase-1 tile = TB lanes x 1 pack; phase-2 tile = TB lanes x ratio packs.  Large messages use TB=1024
+// (same-GPU A/B at W=8 bf16, 16 MiB per rank, per-tile flags: 1024 lanes x 1 pack 35.4 us, 512 x 2
+// 39.2 us, 256 x 4 39.8 us; each publish waits for its stores); smaller ones TB=256 or 64, so that
+// each chunk still splits into enough tiles to fill the CUs.
 constexpr int kTBlock = MR_TS_BLOCK;
-constexpr int kTile1 = 1024;               // 16-byte packs per phase-1 tile
-constexpr int kP1 = kTile1 / kTBlock;      // packs per lane, phase 1
-constexpr int kP2 = kP1 * kRatio;          // packs per lane, phase 2
-static_assert(kP1 * kTBlock == kTile1, "phase-1 tile is a whole number of packs per lane");
+constexpr int kP2 = kRatio;  // packs per lane, phase 2
 
 // Phase 2 of one group: copy phase-2 tile q of chunk c (ratio phase-1 tiles) from the stage to out with
 // device-scope stage loads.
-template <typename D>
+template <typename D, int TB>
 __device__ __forceinline__ void copy_group(char* out, char* stage, const ReduceShape& sh, size_t first, size_t cend,
                                            bool with_edges) {
   const size_t hb = sh.head * D::kSize;
-  const i32x4 rs = make_rsrc(stage + hb + first * 16, kTile1 * kRatio * 16);
+  const i32x4 rs = make_rsrc(stage + hb + first * 16, TB * kP2 * 16);
   u32x4 v[kP2];
 #pragma unroll
   for (int u = 0; u < kP2; ++u) {
-    const size_t i = wc_pack<kTBlock, kP2>(first, u);
+    const size_t i = wc_pack<TB, kP2>(first, u);
     if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, static_cast<int>((i - first) * 16), 0, kStageLoadAux));
   }
 #pragma unroll
   for (int u = 0; u < kP2; ++u) {
-    const size_t i = wc_pack<kTBlock, kP2>(first, u);
+    const size_t i = wc_pack<TB, kP2>(first, u);
     if (i < cend) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + hb) + i);
   }
   if (with_edges) copy_edges_from_stage<D>(stage, out, sh);
@@ -426,9 +425,9 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counts, const TwoShotPlan&
   return s_last != 0;
 }
 
-template <typename D, int W>
-__global__ __launch_bounds__(kTBlock) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
-                                                       uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
+template <typename D, int W, int TB>
+__global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl, uint32_t* flags,
+                                                  ReduceShape sh, TwoShotPlan pl) {
   uint32_t c, k;
   if (pl.sync == kSyncLast) {  // phase-1 workgroups only; consecutive workgroups take one chunk's tiles
     c = blockIdx.x / pl.t1;
@@ -440,21 +439,21 @@ __global__ __launch_bounds__(kTBlock) void twoshot_vec(RankPtrs in, char* out, c
   const size_t c0 = static_cast<size_t>(c) * pl.chunk_units;
   const size_t cend = c0 + pl.chunk_units < sh.npacks ? c0 + pl.chunk_units : sh.npacks;
   if (k < pl.t1) {
-    const size_t first = c0 + static_cast<size_t>(k) * kTile1;
-    const i32x4 rs = make_rsrc(stage + hb + first * 16, kTile1 * 16);
-    reduce_tile<D, W, kTBlock, kP1>(in, hb, first, cend, [&](int, size_t i, const u32x4& o) {
+    const size_t first = c0 + static_cast<size_t>(k) * TB;
+    const i32x4 rs = make_rsrc(stage + hb + first * 16, TB * 16);
+    reduce_tile<D, W, TB, 1>(in, hb, first, cend, [&](int, size_t i, const u32x4& o) {
       raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), rs, static_cast<int>((i - first) * 16), 0, kStageStoreAux);
     });
     if (c == 0 && k == 0) reduce_edges<D, W, true>(in, stage, sh);
     publish_phase1(ctrl, flags, pl, c, k);
     if (pl.sync == kSyncLast && arrive_last(flags, pl, c, k)) {
       const uint32_t q = k / pl.ratio;
-      copy_group<D>(out, stage, sh, c0 + static_cast<size_t>(q) * (kTile1 * kRatio), cend, c == 0 && q == 0);
+      copy_group<D, TB>(out, stage, sh, c0 + static_cast<size_t>(q) * (TB * kRatio), cend, c == 0 && q == 0);
     }
   } else {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
-    copy_group<D>(out, stage, sh, c0 + static_cast<size_t>(q) * (kTile1 * kRatio), cend, c == 0 && q == 0);
+    copy_group<D, TB>(out, stage, sh, c0 + static_cast<size_t>(q) * (TB * kRatio), cend, c == 0 && q == 0);
     finish_phase2(ctrl, pl, c);
   }
 }
@@ -508,19 +507,28 @@ __global__ void zero_words(uint32_t* p, size_t words) {
 
 constexpr size_t kMaxGrid = size_t(1) << 20;  // workgroups; beyond this the one-shot kernels grid-stride
 
+template <typename D, int W, int B, int U>
+hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
+  constexpr size_t tile = static_cast<size_t>(B) * U;
+  const size_t ntiles = (sh.npacks + tile - 1) / tile;
+  size_t grid = ntiles < kMaxGrid ? ntiles : kMaxGrid;
+  if (grid == 0) grid = 1;  // edges only
+  hipLaunchKernelGGL((oneshot_vec<D, W, B, U>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh, ntiles);
+  return hipGetLastError();
+}
+
 template <typename D, int W>
-hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
+hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, uint32_t shape, hipStream_t st) {
   if (sh.vec) {
-    const size_t tile = static_cast<size_t>(kOneShotBlock) * OneShotU<W>::value;
-    const size_t ntiles = (sh.npacks + tile - 1) / tile;
-    size_t grid = ntiles < kMaxGrid ? ntiles : kMaxGrid;
-    if (grid == 0) grid = 1;  // edges only
-    hipLaunchKernelGGL((oneshot_vec<D, W>), dim3(static_cast<unsigned>(grid)), dim3(kOneShotBlock), 0, st, in, out, sh, ntiles);
-  } else {
-    const size_t need = (sh.n + kBlock - 1) / kBlock;
-    const size_t grid = need < kMaxGrid ? need : kMaxGrid;
-    hipLaunchKernelGGL((oneshot_elem<D, W>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, st, in, out, sh.n);
+    switch (shape) {
+      case kShapeNarrow: return oneshot_vec_launch<D, W, 64, 1>(in, out, sh, st);
+      case kShapeMedium: return oneshot_vec_launch<D, W, 256, 1>(in, out, sh, st);
+      default: return oneshot_vec_launch<D, W, kOneShotBlock, OneShotU<W>::value>(in, out, sh, st);
+    }
   }
+  const size_t need = (sh.n + kBlock - 1) / kBlock;
+  const size_t grid = need < kMaxGrid ? need : kMaxGrid;
+  hipLaunchKernelGGL((oneshot_elem<D, W>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, st, in, out, sh.n);
   return hipGetLastError();
 }
 
@@ -528,8 +536,12 @@ template <typename D, int W>
 hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uint32_t* flags, const ReduceShape& sh,
                      const TwoShotPlan& pl, hipStream_t st) {
   const unsigned grid = pl.chunks * (pl.sync == kSyncLast ? pl.t1 : pl.t1 + pl.t2);
-  if (sh.vec)
-    hipLaunchKernelGGL((twoshot_vec<D, W>), dim3(grid), dim3(kTBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
+  if (sh.vec && pl.unit1 == 64)
+    hipLaunchKernelGGL((twoshot_vec<D, W, 64>), dim3(grid), dim3(64), 0, st, in, out, stage, ctrl, flags, sh, pl);
+  else if (sh.vec && pl.unit1 == 256)
+    hipLaunchKernelGGL((twoshot_vec<D, W, 256>), dim3(grid), dim3(256), 0, st, in, out, stage, ctrl, flags, sh, pl);
+  else if (sh.vec)
+    hipLaunchKernelGGL((twoshot_vec<D, W, kTBlock>), dim3(grid), dim3(kTBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
   else
     hipLaunchKernelGGL((twoshot_elem<D, W>), dim3(grid), dim3(kBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
   return hipGetLastError();
@@ -557,8 +569,8 @@ hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uin
   }
 
 template <typename D>
-hipError_t oneshot_d(const RankPtrs& in, int W, char* out, const ReduceShape& sh, hipStream_t st) {
-  MR_W_CASES(oneshot_w, D, in, out, sh, st)
+hipError_t oneshot_d(const RankPtrs& in, int W, char* out, const ReduceShape& sh, uint32_t shape, hipStream_t st) {
+  MR_W_CASES(oneshot_w, D, in, out, sh, shape, st)
 }
 
 template <typename D>
@@ -570,11 +582,11 @@ hipError_t twoshot_d(const RankPtrs& in, int W, char* out, char* stage, Ctrl* ct
 }  // namespace
 
 hipError_t launch_oneshot(const RankPtrs& in, int W, mr_dtype dt, char* out, const ReduceShape& sh,
-                          hipStream_t st) {
+                          uint32_t shape, hipStream_t st) {
   switch (dt) {
-    case MR_BF16: return oneshot_d<Bf16>(in, W, out, sh, st);
-    case MR_FP16: return oneshot_d<Fp16>(in, W, out, sh, st);
-    case MR_FP32: return oneshot_d<Fp32>(in, W, out, sh, st);
+    case MR_BF16: return oneshot_d<Bf16>(in, W, out, sh, shape, st);
+    case MR_FP16: return oneshot_d<Fp16>(in, W, out, sh, shape, st);
+    case MR_FP32: return oneshot_d<Fp32>(in, W, out, sh, shape, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -594,12 +606,12 @@ hipError_t launch_twoshot(const RankPtrs& in, int W, mr_dtype dt, char* out, cha
 // with C = ceil(n/W) rounded up to a whole pack, so every chunk boundary is 16-byte aligned; the last
 // chunks may be short or empty.  The few elements outside the body (an unaligned head, a tail shorter
 // than a pack) ride with phase-1 tile 0 and phase-2 tile 0 of chunk 0.
-TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit) {
+TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit, uint32_t shape) {
   TwoShotPlan pl{};
   pl.chunks = static_cast<uint32_t>(W);
   const size_t units = sh.vec ? sh.npacks : sh.n;
   pl.chunk_units = (units + W - 1) / W;
-  pl.unit1 = sh.vec ? kTile1 : kBlock;
+  pl.unit1 = sh.vec ? twoshot_tile_packs(sh.npacks, sync, shape) : kBlock;
   pl.ratio = kRatio;
   pl.unit2 = pl.unit1 * kRatio;
   size_t t1 = (pl.chunk_units + pl.unit1 - 1) / pl.unit1;

@@ -8,8 +8,9 @@ before timing starts and the caches do not hold them: the steps rotate over seve
 sets whose total (>= 864 MiB) is far beyond the 256 MB last-level cache, so every step streams from
 HBM.  Timing: HIP events on the stream the kernels are launched on, around exactly K steps, with a
 device synchronisation on both sides.  The same run also times two-shot (both byte counts), the
-param-contiguous scatter on the FSDP-style split workload, the cache-resident one-shot, and the CPU
-oracle on the host cores; one JSON line goes to stdout, progress to stderr.
+param-contiguous scatter on the FSDP-style split workload, the cache-resident one-shot, a size sweep of
+256 KiB .. 256 MiB per rank, and the CPU oracle on the host cores; one JSON line goes to stdout,
+progress to stderr.
 """
 from __future__ import annotations
 
@@ -26,7 +27,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0  # MI355X HBM3E, 8.0e12 B/s
 PROFILE_PMC = os.path.join(ROOT, "profiles", "oneshot_vec_bf16_w8_16MiB_pmc.txt")
-KERNEL_SRC = os.path.join(ROOT, "all_gather_amd", "csrc", "reduce_kernels.hip")
+# the reduce kernels and the header that picks their launch shapes
+KERNEL_SRC = (os.path.join(ROOT, "all_gather_amd", "csrc", "reduce_kernels.hip"),
+              os.path.join(ROOT, "all_gather_amd", "csrc", "mr_internal.h"))
 
 
 def log(*a):
@@ -34,8 +37,11 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(algo_bytes: int):
@@ -125,6 +131,92 @@ def contention_leg(mr, torch, dev, stream, R=20, G=24):
     return res
 
 
+SWEEP_KIB = (256, 1024, 4096, 16384, 65536, 262144)  # bytes per rank buffer, 256 KiB .. 256 MiB
+SWEEP_MODES = ("oneshot", "twoshot", "twoshot:grid")  # two-shot under its default hand-off and the grid barrier
+
+
+def sweep_leg(mr, torch, dev):
+    """W=8 sum-reduce over per-rank sizes 256 KiB .. 256 MiB, bf16 and fp32, uniform[-1,1) inputs:
+    one-shot, and two-shot under its default (size-chosen) hand-off and with the grid barrier.  Each size rotates over
+    enough disjoint buffer sets to keep >= 512 MiB in flight (twice the last-level cache); sizes up to
+    1 MiB per rank are timed as HIP-graph replays so that launch cost does not hide the kernel."""
+    W = 8
+    side = torch.cuda.Stream()
+    rows = []
+    for dtype, tdt, s in (("bf16", torch.bfloat16, 2), ("fp32", torch.float32, 4)):
+        for kib in SWEEP_KIB:
+            n = kib * 1024 // s
+            per_set = (W + 1) * n * s
+            S = max(1, min(256, -(-(512 << 20) // per_set)))
+            g = torch.Generator(device=dev)
+            g.manual_seed(3000 + kib)
+            inp = (torch.rand(S * W * n, device=dev, generator=g) * 2 - 1).to(tdt)
+            outs = torch.empty(S * n, dtype=tdt, device=dev)
+            sets = [([inp[(k * W + r) * n:(k * W + r + 1) * n] for r in range(W)], outs[k * n:(k + 1) * n])
+                    for k in range(S)]
+            launches = max(20, min(2000, (4 << 30) // per_set))
+            use_graph = kib <= 1024
+            row = {"dtype": dtype, "KiB_per_rank": kib, "n": n, "bytes": per_set, "buffer_sets": S,
+                   "timing": "hip graph replay" if use_graph else "eager launches"}
+            for mode in SWEEP_MODES:
+                kind, _, sync = mode.partition(":")
+                mr.set_option("twoshot_sync", sync or "auto")
+                calls = [mr.prepare_allreduce(b, o, kind, stream=side) for b, o in sets]
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    for c in calls:  # warm: also sizes this stream's two-shot workspace
+                        c()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                if use_graph:
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(graph, stream=side):
+                        for c in calls:
+                            c()
+                    reps = max(1, launches // S)
+                    with torch.cuda.stream(side):  # replay() launches on the current stream
+                        graph.replay()
+                        torch.cuda.synchronize()
+                        e0.record(side)
+                        for _ in range(reps):
+                            graph.replay()
+                        e1.record(side)
+                    torch.cuda.synchronize()
+                    count = reps * S
+                    del graph
+                else:
+                    e0.record(side)
+                    for i in range(launches):
+                        calls[i % S]()
+                    e1.record(side)
+                    torch.cuda.synchronize()
+                    count = launches
+                t = e0.elapsed_time(e1) / count * 1e-3
+                row[mode] = {"us": round(t * 1e6, 3), "GBps": round(per_set / t / 1e9, 1),
+                             "frac": round(per_set / t / 1e9 / PEAK_GBS, 4), "launches": count}
+                if kind == "twoshot":
+                    row[mode]["GBps_actual_bytes"] = round((W + 3) * n * s / t / 1e9, 1)
+                    row[mode]["barrier_error_word"] = mr.workspace_check(side)
+            mr.set_option("twoshot_sync", "auto")
+            rows.append(row)
+            log(f"[bench] sweep {dtype} {kib:>6d} KiB/rank ({row['timing']}): " + ", ".join(
+                f"{m} {row[m]['us']:.2f} us {row[m]['GBps']:.0f} GB/s" for m in SWEEP_MODES))
+            del sets, inp, outs
+            torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +225,7 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="disjoint buffer sets rotated through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip the secondary paths")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 256 KiB .. 256 MiB size sweep")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (reference for counter scaling)")
     args = ap.parse_args()
@@ -226,7 +319,7 @@ def main():
                                         "barrier_error_word": mr.workspace_check()}
             log(f"[bench] twoshot ({sync}): {t2 * 1e6:.2f} us/launch, {algo / t2 / 1e9:.1f} GB/s (metric bytes), "
                 f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")
-        mr.set_option("twoshot_sync", "tile")
+        mr.set_option("twoshot_sync", "auto")
         # param-contiguous scatter: W=8, G=4, P=64 log-uniform splits, bf16 random bits
         c4 = workloads.CONFIG4
         splits = [int(x) for x in workloads.log_uniform_splits(c4["cfg"], c4["P"])]
@@ -257,6 +350,8 @@ def main():
         del gsets, shard_sets
         torch.cuda.empty_cache()
         paths["contention_fp32_512MiB"] = contention_leg(mr, torch, dev, stream)
+        if not args.no_sweep:
+            paths["sweep_w8"] = sweep_leg(mr, torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -268,10 +363,23 @@ def main():
             times.append(time.perf_counter() - t0)
             reps += 1
         med = float(np.median(times))
+        # the same oracle over disjoint index ranges on several threads (bits unchanged); the pool is
+        # held to this process's share of the host, at most 16 threads
+        nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+        ttimes = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.allreduce_sum_ref_threaded(host, dtype, nthr)
+            ttimes.append(time.perf_counter() - t0)
+        tmed = float(np.median(ttimes))
         cpu = {"value": algo / med / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"the full workload (W=8 x 8,388,608 bf16), {reps} runs, median {med:.3f} s, "
-                         f"numpy single-threaded on {os.cpu_count()} host CPUs"}
-        log(f"[bench] cpu oracle: {med:.3f} s per call, {algo / med / 1e9:.2f} GB/s")
+                         f"numpy single-threaded on {os.cpu_count()} host CPUs",
+               "cpu_model": cpu_model(),
+               "threaded": {"value": algo / tmed / 1e9, "unit": "GB/s", "cores": nthr, "seconds": tmed,
+                            "sample": "the same workload split over disjoint index ranges, median of 3"}}
+        log(f"[bench] cpu oracle: {med:.3f} s per call, {algo / med / 1e9:.2f} GB/s; "
+            f"{nthr} threads: {tmed:.3f} s, {algo / tmed / 1e9:.2f} GB/s ({cpu['cpu_model']})")
 
     rec = {
         "metric": "achieved HBM GB/s (and % of peak) for W=8 bf16 all-reduce at 16 MB/rank, 1 GPU",

@@ -179,7 +179,8 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  * Process-wide options (thread-safe; they apply to calls made after the change).
  *
  * MR_OPT_TWOSHOT_SYNC  how a two-shot phase-2 tile waits for phase 1 (all give identical results):
- *   MR_TWOSHOT_SYNC_TILE  (default) per-tile producer flags: a phase-2 tile waits only for the
+ *   MR_TWOSHOT_SYNC_AUTO  (default) LAST below 16 MiB per rank buffer, TILE from 16 MiB up;
+ *   MR_TWOSHOT_SYNC_TILE  per-tile producer flags: a phase-2 tile waits only for the
  *                         phase-1 tiles it copies (the per-block flag hand-off of the custom
  *                         allreduce page's block_barrier, applied to the two phases);
  *   MR_TWOSHOT_SYNC_CHUNK per-chunk barrier: waits for every phase-1 tile of its 1/W chunk;
@@ -189,14 +190,27 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  * MR_OPT_SPIN_LIMIT    polls a waiting workgroup makes before it gives up and sets the workspace error
  *                      word (see mr_workspace_check); default 2^22.  A value of 0 makes every wait
  *                      that is not already satisfied give up at once (for testing error handling).
+ * MR_OPT_TILE_SHAPE    tile shape of the sum-reduce kernels (results are identical for every shape):
+ *   MR_TILE_AUTO   (default) chosen from the message size and dtype: narrow below 64 Ki packs
+ *                  of 16 B, medium below 256 Ki (fp32) or 512 Ki (16-bit types) packs, wide above;
+ *                  two-shot: 64-pack tiles below 8 Ki packs, 256 below 128 Ki, 1024 above;
+ *   MR_TILE_WIDE   one-shot 256 lanes x 4 packs of 16 B (256 x 1 for W > 8), two-shot phase-1
+ *                  tiles of 1024 packs;
+ *   MR_TILE_MEDIUM one-shot 256 x 1, two-shot 256-pack tiles;
+ *   MR_TILE_NARROW one-shot 64 x 1, two-shot 64-pack tiles.
  * Unknown options or out-of-range values -> MR_ERR_INVALID_ARG.  Environment variables
- * MR_TWOSHOT_SYNC and MR_SPIN_LIMIT set the initial values when the library loads.
+ * MR_TWOSHOT_SYNC, MR_SPIN_LIMIT and MR_TILE_SHAPE set the initial values when the library loads.
  */
-typedef enum mr_option { MR_OPT_TWOSHOT_SYNC = 0, MR_OPT_SPIN_LIMIT = 1 } mr_option;
+typedef enum mr_option { MR_OPT_TWOSHOT_SYNC = 0, MR_OPT_SPIN_LIMIT = 1, MR_OPT_TILE_SHAPE = 2 } mr_option;
 #define MR_TWOSHOT_SYNC_TILE 0
 #define MR_TWOSHOT_SYNC_CHUNK 1
 #define MR_TWOSHOT_SYNC_GRID 2
 #define MR_TWOSHOT_SYNC_LAST 3
+#define MR_TWOSHOT_SYNC_AUTO 4
+#define MR_TILE_AUTO 0
+#define MR_TILE_WIDE 1
+#define MR_TILE_MEDIUM 2
+#define MR_TILE_NARROW 3
 mr_status mr_set_option(mr_option opt, int64_t value);
 mr_status mr_get_option(mr_option opt, int64_t* value);
 

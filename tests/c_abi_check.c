@@ -30,7 +30,7 @@ int main(void) {
   CHECK(mr_allgather_param_contig((const void*)0x100000, 8, 4, splits, 3, MR_FP16, (void*)0x1002FE, stream) ==
         MR_ERR_ALIAS);
   CHECK(mr_workspace_bytes(8, 1 << 20, MR_BF16) > (2u << 20));
-  CHECK(mr_get_option(MR_OPT_TWOSHOT_SYNC, &v) == MR_OK && v == MR_TWOSHOT_SYNC_TILE);
+  CHECK(mr_get_option(MR_OPT_TWOSHOT_SYNC, &v) == MR_OK && v == MR_TWOSHOT_SYNC_AUTO);
   CHECK(mr_set_option(MR_OPT_TWOSHOT_SYNC, 7) == MR_ERR_INVALID_ARG);
   CHECK(mr_last_hip_error() == 0);
   printf("c abi ok\n");

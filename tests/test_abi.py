@@ -133,18 +133,23 @@ def test_workspace_rule_covers_every_two_shot_plan(L, es, dt):
 
 def test_options_validate_and_round_trip(L):
     v = ctypes.c_int64(-7)
-    assert L.mr_get_option(0, ctypes.byref(v)) == OK and v.value == 0          # tile flags by default
+    assert L.mr_get_option(0, ctypes.byref(v)) == OK and v.value == 4          # size-chosen hand-off
     assert L.mr_get_option(1, ctypes.byref(v)) == OK and v.value == 1 << 22
-    assert L.mr_set_option(0, 4) == EINVAL and L.mr_set_option(0, -1) == EINVAL
+    assert L.mr_set_option(0, 5) == EINVAL and L.mr_set_option(0, -1) == EINVAL
     assert L.mr_set_option(1, -1) == EINVAL and L.mr_set_option(1, 2 ** 32) == EINVAL
     assert L.mr_set_option(9, 0) == EINVAL and L.mr_get_option(9, ctypes.byref(v)) == EINVAL
     assert L.mr_get_option(0, None) == EINVAL
-    for sync in ("chunk", "grid", "last", "tile"):
+    for sync in ("chunk", "grid", "last", "tile", "auto"):
         mr.set_option("twoshot_sync", sync)
         assert mr.get_option("twoshot_sync") == sync
     mr.set_option("spin_limit", 1000)
     assert mr.get_option("spin_limit") == 1000
     mr.set_option("spin_limit", 1 << 22)
+    assert L.mr_get_option(2, ctypes.byref(v)) == OK and v.value == 0          # tile shape: auto
+    assert L.mr_set_option(2, 4) == EINVAL and L.mr_set_option(2, -1) == EINVAL
+    for shape in ("wide", "medium", "narrow", "auto"):
+        mr.set_option("tile_shape", shape)
+        assert mr.get_option("tile_shape") == shape
 
 
 def test_binding_rejects_host_tensors():

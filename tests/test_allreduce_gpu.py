@@ -11,9 +11,9 @@ import workloads
 from gpu_util import TORCH_DT, assert_reduce_equal, device, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
-# one-shot, and two-shot under each phase hand-off (per-tile flags, per-chunk barrier, grid barrier,
-# last arriver of each tile group)
-MODES = ("oneshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid", "twoshot:last")
+# one-shot, and two-shot under the default (size-chosen) hand-off and each explicit one (per-tile
+# flags, per-chunk barrier, grid barrier, last arriver of each tile group)
+MODES = ("oneshot", "twoshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid", "twoshot:last")
 TWOSHOT_MODES = MODES[1:]
 
 
@@ -25,7 +25,7 @@ def _call(dbufs, out, mode):
         mr.allreduce_sum(dbufs, out, mode=kind)
     finally:
         if sync:
-            mr.set_option("twoshot_sync", "tile")
+            mr.set_option("twoshot_sync", "auto")
 
 
 def _run(dbufs, dtype, n, mode, out=None):
@@ -171,7 +171,7 @@ def test_twoshot_stale_stage_is_never_read(sync):
                 assert_reduce_equal(to_bits(outs[k]), wants[k], "bf16", f"{sync} launch {i}")
         assert mr.workspace_check() == 0
     finally:
-        mr.set_option("twoshot_sync", "tile")
+        mr.set_option("twoshot_sync", "auto")
         mr.set_workspace(None)
 
 
@@ -213,7 +213,7 @@ def test_bounded_wait_reports_and_recovers():
         flags = mr.workspace_check()
     finally:
         mr.set_option("spin_limit", 1 << 22)
-        mr.set_option("twoshot_sync", "tile")
+        mr.set_option("twoshot_sync", "auto")
     assert flags & 1, "a phase-2 wait should have given up"
     for mode in ("twoshot:tile", "twoshot:grid"):
         out.fill_(0)
@@ -365,3 +365,17 @@ def test_every_16bit_pattern_against_structured_partners(dtype):
     x2 = x1 ^ np.uint16(0x8000)
     for bufs in ([x0, x1], [x1, x0, x2]):
         _check_modes(bufs, dtype, f"16-bit sweep {dtype} W={len(bufs)}")
+
+
+@pytest.mark.parametrize("shape", ["wide", "medium", "narrow"])
+def test_every_tile_shape_in_every_mode(shape):
+    """Each forced tile shape (one-shot lanes x packs, two-shot phase-1 tile) gives the oracle's bits,
+    on sizes that leave partial tiles, partial chunks and unaligned edges."""
+    mr.set_option("tile_shape", shape)
+    try:
+        for dtype in ("bf16", "fp32"):
+            for W, n in ((8, 1_000_003), (3, 65_541), (16, 300_007), (8, 4_194_304 + 8)):
+                bufs = workloads.rank_buffers(60 + W, W, n, dtype, "uniform")
+                _check_modes(bufs, dtype, f"{shape} {dtype} W={W} n={n}")
+    finally:
+        mr.set_option("tile_shape", "auto")

@@ -24,7 +24,7 @@ def _capture(fn, stream):
     return g
 
 
-@pytest.mark.parametrize("mode", ["oneshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid", "twoshot:last"])
+@pytest.mark.parametrize("mode", ["oneshot", "twoshot", "twoshot:tile", "twoshot:chunk", "twoshot:grid", "twoshot:last"])
 def test_allreduce_graph_replays(mode):
     W, n = 8, 2_000_003
     kind, _, sync = mode.partition(":")
@@ -51,7 +51,7 @@ def test_allreduce_graph_replays(mode):
         if kind == "twoshot":
             assert mr.workspace_check(s) == 0
     finally:
-        mr.set_option("twoshot_sync", "tile")
+        mr.set_option("twoshot_sync", "auto")
 
 
 def test_gathers_and_reduce_scatter_graph_replays():
