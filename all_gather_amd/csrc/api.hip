@@ -215,8 +215,51 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
   return MR_OK;
 }
 
-mr_status gather_launch(const GatherPlan& gp, hipStream_t st) {
-  for (const mr::GatherArgs& a : gp.groups) {
+// Plans depend only on (W, G, P, dtype, splits).  FSDP issues the same few gathers every step, so each
+// thread keeps its last kPlanSlots plans: a repeated call neither recomputes the prefix sums and tile
+// tables nor allocates.  Failed plans are not kept.
+struct CachedPlan {
+  bool used = false;
+  int W = 0, G = 0, P = 0;
+  mr_dtype dtype = MR_BF16;
+  std::vector<uint64_t> splits;
+  GatherPlan plan;
+};
+constexpr int kPlanSlots = 8;
+thread_local CachedPlan t_plans[kPlanSlots];
+thread_local int t_plan_next = 0;
+
+mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, const GatherPlan** out) {
+  if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
+  const size_t key_bytes = static_cast<size_t>(P) * sizeof(uint64_t);
+  for (const CachedPlan& c : t_plans)
+    if (c.used && c.W == W && c.G == G && c.P == P && c.dtype == dtype &&
+        std::memcmp(c.splits.data(), splits, key_bytes) == 0) {
+      *out = &c.plan;
+      return MR_OK;
+    }
+  CachedPlan& c = t_plans[t_plan_next];
+  t_plan_next = (t_plan_next + 1) % kPlanSlots;
+  c.used = false;
+  c.plan.groups.clear();
+  const mr_status s = gather_plan(W, G, splits, P, dtype, &c.plan);
+  if (s != MR_OK) return s;
+  c.W = W;
+  c.G = G;
+  c.P = P;
+  c.dtype = dtype;
+  c.splits.assign(splits, splits + P);
+  c.used = true;
+  *out = &c.plan;
+  return MR_OK;
+}
+
+// Launch every group of a plan; `bind` fills in this call's pointers on a copy of the group's arguments.
+template <typename Bind>
+mr_status gather_launch(const GatherPlan& gp, Bind bind, hipStream_t st) {
+  for (const mr::GatherArgs& g : gp.groups) {
+    mr::GatherArgs a = g;
+    bind(a);
     if (g_trace)
       std::fprintf(stderr, "[mr] gather W=%u G=%u params=%u T=%llu tiles=%u src_table=%u dst_table=%u\n", a.W, a.G,
                    a.P, static_cast<unsigned long long>(a.T), a.total_tiles, a.src_table, a.dst_table);
@@ -333,39 +376,37 @@ mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dty
 mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_t* splits, int P, mr_dtype dtype,
                                     void* out, mr_stream stream) {
   if (W < 1 || W > 65535) return MR_ERR_INVALID_ARG;
-  GatherPlan gp;
-  mr_status s = gather_plan(W, G, splits, P, dtype, &gp);
-  if (s != MR_OK || gp.T == 0) return s;
+  const GatherPlan* gp = nullptr;
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, &gp);
+  if (s != MR_OK || gp->T == 0) return s;
   if (!src || !out) return MR_ERR_INVALID_ARG;
-  const uint64_t total_bytes = static_cast<uint64_t>(W) * gp.T * gp.es;
+  const uint64_t total_bytes = static_cast<uint64_t>(W) * gp->T * gp->es;
   if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
     return MR_ERR_ALIAS;
-  for (mr::GatherArgs& a : gp.groups) {
+  return gather_launch(*gp, [&](mr::GatherArgs& a) {
     a.src = static_cast<const char*>(src);
     a.out = static_cast<char*>(out);
-  }
-  return gather_launch(gp, reinterpret_cast<hipStream_t>(stream));
+  }, reinterpret_cast<hipStream_t>(stream));
 }
 
 mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int G, const uint64_t* splits, int P,
                                            mr_dtype dtype, void* out, mr_stream stream) {
   if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
-  GatherPlan gp;
-  mr_status s = gather_plan(W, G, splits, P, dtype, &gp);
-  if (s != MR_OK || gp.T == 0) return s;
+  const GatherPlan* gp = nullptr;
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, &gp);
+  if (s != MR_OK || gp->T == 0) return s;
   if (!shards || !out) return MR_ERR_INVALID_ARG;
-  const uint64_t shard_bytes = gp.T * gp.es, out_bytes = static_cast<uint64_t>(W) * shard_bytes;
+  const uint64_t shard_bytes = gp->T * gp->es, out_bytes = static_cast<uint64_t>(W) * shard_bytes;
   for (int r = 0; r < W; ++r) {
     if (!shards[r]) return MR_ERR_INVALID_ARG;
     if (overlap(reinterpret_cast<uintptr_t>(shards[r]), shard_bytes, reinterpret_cast<uintptr_t>(out), out_bytes))
       return MR_ERR_ALIAS;
   }
-  for (mr::GatherArgs& a : gp.groups) {
+  return gather_launch(*gp, [&](mr::GatherArgs& a) {
     a.src_table = 1;
     for (int r = 0; r < W; ++r) a.src_tab[r] = static_cast<const char*>(shards[r]);
     a.out = static_cast<char*>(out);
-  }
-  return gather_launch(gp, reinterpret_cast<hipStream_t>(stream));
+  }, reinterpret_cast<hipStream_t>(stream));
 }
 
 mr_status mr_allgather_into_tensor(const void* const* shards, int W, size_t T, mr_dtype dtype, void* out,
@@ -379,11 +420,11 @@ mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype
                             mr_stream stream) {
   if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
   const uint64_t split = T;
-  GatherPlan gp;
-  mr_status s = gather_plan(W, W, &split, 1, dtype, &gp);
-  if (s != MR_OK || gp.T == 0) return s;
+  const GatherPlan* gp = nullptr;
+  mr_status s = cached_gather_plan(W, W, &split, 1, dtype, &gp);
+  if (s != MR_OK || gp->T == 0) return s;
   if (!shards || !outs) return MR_ERR_INVALID_ARG;
-  const uint64_t bytes = gp.T * gp.es;
+  const uint64_t bytes = gp->T * gp->es;
   for (int i = 0; i < W; ++i) {
     if (!shards[i] || !outs[i]) return MR_ERR_INVALID_ARG;
     for (int j = 0; j < W; ++j) {
@@ -392,15 +433,14 @@ mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype
       if (j != i && overlap(oi, bytes, reinterpret_cast<uintptr_t>(outs[j]), bytes)) return MR_ERR_ALIAS;
     }
   }
-  for (mr::GatherArgs& a : gp.groups) {
+  return gather_launch(*gp, [&](mr::GatherArgs& a) {
     a.src_table = 1;
     a.dst_table = 1;
     for (int r = 0; r < W; ++r) {
       a.src_tab[r] = static_cast<const char*>(shards[r]);
       a.dst_tab[r] = static_cast<char*>(outs[r]);
     }
-  }
-  return gather_launch(gp, reinterpret_cast<hipStream_t>(stream));
+  }, reinterpret_cast<hipStream_t>(stream));
 }
 
 mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {

@@ -217,6 +217,26 @@ def test_reduce_scatter_argument_errors(L):
     assert L.mr_reduce_scatter_sum(p, 16, 8, 0, 15, None, None) == OK   # a trailing empty chunk
 
 
+def test_cached_gather_plans_keep_validation_and_alias_checks(L):
+    """Plans are cached per (W, G, P, dtype, splits); a cached plan must not let a call skip the checks
+    that depend on the call's own arguments (pointers) or on any key field, and more distinct split
+    sets than cache slots must keep working."""
+    src, out = 0x100000, 0x800000
+    for rep in range(2):  # miss, then hit
+        for k in range(12):
+            sp = (ctypes.c_uint64 * 3)(8 + k, 16, 24)
+            T = 48 + k
+            assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 0, None, None) == EINVAL, (rep, k)
+            assert L.mr_allgather_param_contig(None, 8, 4, sp, 3, 0, out, None) == EINVAL, (rep, k)
+            assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 0, src + 8 * T * 2 - 2, None) == EALIAS
+            assert L.mr_allgather_param_contig(src, 8, 3, sp, 3, 0, out, None) == EINVAL   # G differs
+            assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 9, out, None) == EINVAL   # dtype differs
+            assert L.mr_allgather_param_contig(src, 8, 4, sp, 2, 0, src + 8 * 24 * 2 - 2, None) == EALIAS
+    huge = (ctypes.c_uint64 * 3)(8, 2 ** 62, 2 ** 62)
+    assert L.mr_allgather_param_contig(src, 8, 4, huge, 3, 0, out, None) == EINVAL     # never cached
+    assert L.mr_allgather_param_contig(src, 8, 4, huge, 3, 0, out, None) == EINVAL
+
+
 def test_shard_gather_argument_errors(L):
     sh = _ptrs(0x100000, 0x200000, 0x300000, 0x400000)
     outs = _ptrs(0x1100000, 0x1200000, 0x1300000, 0x1400000)

@@ -127,3 +127,19 @@ def test_gather_on_side_stream_with_event_consumer():
         copy = out.clone()
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(copy), want), rep
+
+
+def test_more_split_sets_than_cached_plans():
+    """Twelve distinct split sets, each gathered twice from fresh buffers: the host keeps a few launch
+    plans per thread, and every call, hit or miss, must bind its own pointers."""
+    W, G = 8, 4
+    for rep in range(2):
+        for k in range(12):
+            splits = [1000 + 8 * k, 24 + k, 4096, 7 * k]
+            T = sum(splits)
+            print(f"[case] plan cache rep={rep} k={k} T={T}", flush=True)
+            src = workloads.gather_source(200 + 12 * rep + k, W, T, "bf16")
+            out = torch.empty(W * T, dtype=torch.bfloat16, device=device())
+            mr.allgather_param_contig(to_dev(src, "bf16"), W, G, splits, out)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(out), oracle.allgather_param_contig_ref(src, W, G, splits)), (rep, k)

@@ -175,6 +175,42 @@ def test_twoshot_stale_stage_is_never_read(sync):
         mr.set_workspace(None)
 
 
+@pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last"])
+def test_twoshot_poisoned_stage_stress(sync):
+    """Before every launch, a fill on the launch stream overwrites the whole stage (and out) with 0xFF
+    bytes, a NaN in every element; 80 launches per tile shape, at sizes whose grids differ, must all
+    match the oracle bit for bit.  A phase-2 copy that ran ahead of its producer, or a phase-1 tile
+    that was never written, would publish the poison."""
+    W = 8
+    cases = [("narrow", 30_011), ("medium", 1_000_003), ("wide", 4_194_304 + 8), ("auto", 2_500_001)]
+    n_max = max(n for _, n in cases)
+    ws = torch.empty(mr.workspace_bytes(W, n_max, "bf16"), dtype=torch.uint8, device=device())
+    flags_cap = ws.numel() >> 8
+    stage_off = 16384 + ((flags_cap * 4 + 255) // 256) * 256
+    mr.set_workspace(ws)
+    mr.set_option("twoshot_sync", sync)
+    try:
+        for shape, n in cases:
+            print(f"[case] poisoned stage {sync} {shape} n={n}", flush=True)
+            mr.set_option("tile_shape", shape)
+            bufs = workloads.rank_buffers(70 + n % 97, W, n, "bf16", "uniform")
+            want = torch.from_numpy(oracle.allreduce_sum_ref(bufs, "bf16").view(np.int16)).to(device())
+            dbufs = [to_dev(b, "bf16") for b in bufs]
+            out = torch.empty(n, dtype=torch.bfloat16, device=device())
+            bad = torch.zeros((), dtype=torch.int64, device=device())
+            for _ in range(80):
+                ws[stage_off:].fill_(0xFF)
+                out.view(torch.int16).fill_(-1)
+                mr.allreduce_sum(dbufs, out, mode="twoshot")
+                bad += (out.view(torch.int16) != want).sum()
+            assert int(bad) == 0, f"{sync} {shape} n={n}: {int(bad)} poisoned or wrong elements"
+            assert mr.workspace_check() == 0
+    finally:
+        mr.set_option("tile_shape", "auto")
+        mr.set_option("twoshot_sync", "auto")
+        mr.set_workspace(None)
+
+
 def test_caller_workspace_too_small():
     W, n = 8, 1_000_000
     bufs = [to_dev(b, "bf16") for b in workloads.rank_buffers(17, W, n, "bf16", "uniform")]
