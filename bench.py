@@ -74,24 +74,12 @@ def time_steps(calls, K, W_, stream):
     return e0.elapsed_time(e1)  # ms
 
 
-def contention_leg(mr, torch, dev, stream, R=20, G=24):
-    """W=8 fp32 one-shot at 512 MiB per rank, alone and while bf16 8192^3 GEMMs run on a second
-    stream (default priority): reduce GB/s and GEMM TFLOP/s alone and together."""
-    W, n = 8, 134_217_728
-    algo = (W + 1) * n * 4
-    g = torch.Generator(device=dev)
-    g.manual_seed(5)
-    bufs = [torch.rand(n, device=dev, generator=g) * 2 - 1 for _ in range(W)]
-    out = torch.empty(n, dtype=torch.float32, device=dev)
-    call = mr.prepare_allreduce(bufs, out, "oneshot")
-    a = (torch.randn(8192, 8192, device=dev, generator=g) * 0.02).to(torch.bfloat16)
-    b = (torch.randn(8192, 8192, device=dev, generator=g) * 0.02).to(torch.bfloat16)
-    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
-    side = torch.cuda.Stream()
-    flop = 2.0 * 8192 ** 3
+def _overlap(torch, stream, side, call, R, gemm, G):
+    """Time R calls alone on `stream`, G GEMMs alone on `side`, then both at once (the GEMM window is
+    opened first).  Returns seconds per call and per GEMM, alone and together."""
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def reduce_run():
+    def op_run():
         e0, e1 = ev(), ev()
         e0.record(stream)
         for _ in range(R):
@@ -104,28 +92,51 @@ def contention_leg(mr, torch, dev, stream, R=20, G=24):
         with torch.cuda.stream(side):
             e0.record(side)
             for _ in range(G):
-                torch.matmul(a, b, out=c)
+                gemm()
             e1.record(side)
         return e0, e1
 
-    call(); torch.matmul(a, b, out=c); torch.cuda.synchronize()
-    r0, r1 = reduce_run(); torch.cuda.synchronize()
-    t_red = r0.elapsed_time(r1) / R * 1e-3
+    call(); gemm(); torch.cuda.synchronize()
+    r0, r1 = op_run(); torch.cuda.synchronize()
+    t_op = r0.elapsed_time(r1) / R * 1e-3
     g0, g1 = gemm_run(); torch.cuda.synchronize()
     t_gemm = g0.elapsed_time(g1) / G * 1e-3
     side.wait_stream(stream)
     g0, g1 = gemm_run()
-    r0, r1 = reduce_run()
+    r0, r1 = op_run()
     torch.cuda.synchronize()
-    t_red_c = r0.elapsed_time(r1) / R * 1e-3
-    t_gemm_c = g0.elapsed_time(g1) / G * 1e-3
-    res = {"reduce_GBps_alone": algo / t_red / 1e9, "reduce_GBps_with_gemm": algo / t_red_c / 1e9,
-           "gemm_TFLOPs_alone": flop / t_gemm / 1e12, "gemm_TFLOPs_with_reduce": flop / t_gemm_c / 1e12,
-           "reduce_us_alone": t_red * 1e6, "reduce_us_with_gemm": t_red_c * 1e6, "bytes_per_reduce": algo,
-           "note": "reduce window overlaps the GEMM stream; GEMM figure averaged over its own window"}
-    log(f"[bench] contention fp32 512 MiB/rank: reduce {res['reduce_GBps_alone']:.1f} GB/s alone, "
-        f"{res['reduce_GBps_with_gemm']:.1f} GB/s beside GEMM; GEMM {res['gemm_TFLOPs_alone']:.0f} TFLOP/s alone, "
-        f"{res['gemm_TFLOPs_with_reduce']:.0f} TFLOP/s beside reduce")
+    return t_op, t_gemm, r0.elapsed_time(r1) / R * 1e-3, g0.elapsed_time(g1) / G * 1e-3
+
+
+def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes):
+    """Ops alone and beside bf16 8192^3 GEMMs on a second stream (default priority): W=8 fp32 one-shot
+    and two-shot at 512 MiB per rank, and the config-4 param-contiguous scatter.  GB/s of the op and
+    TFLOP/s of the GEMM, alone and together."""
+    W, n = 8, 134_217_728
+    algo = (W + 1) * n * 4
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    bufs = [torch.rand(n, device=dev, generator=g) * 2 - 1 for _ in range(W)]
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    a = (torch.randn(8192, 8192, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    b = (torch.randn(8192, 8192, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+    flop = 2.0 * 8192 ** 3
+    gemm = lambda: torch.matmul(a, b, out=c)
+    res = {"note": "op window overlaps the GEMM stream; GEMM figure averaged over its own window"}
+    legs = [("reduce_oneshot_fp32_512MiB", mr.prepare_allreduce(bufs, out, "oneshot"), algo, 20, 24),
+            ("reduce_twoshot_fp32_512MiB", mr.prepare_allreduce(bufs, out, "twoshot"), algo, 20, 24),
+            ("scatter_config4_bf16", gather_sets[0], gather_bytes, 100, 24)]
+    for name, call, nbytes, R, G in legs:
+        t_op, t_gemm, t_op_c, t_gemm_c = _overlap(torch, stream, side, call, R, gemm, G)
+        r = {"op_GBps_alone": nbytes / t_op / 1e9, "op_GBps_with_gemm": nbytes / t_op_c / 1e9,
+             "op_us_alone": t_op * 1e6, "op_us_with_gemm": t_op_c * 1e6, "bytes_per_op": nbytes,
+             "gemm_TFLOPs_alone": flop / t_gemm / 1e12, "gemm_TFLOPs_with_op": flop / t_gemm_c / 1e12}
+        res[name] = r
+        log(f"[bench] contention {name}: {r['op_us_alone']:.1f} us ({r['op_GBps_alone']:.0f} GB/s) alone, "
+            f"{r['op_us_with_gemm']:.1f} us ({r['op_GBps_with_gemm']:.0f} GB/s) beside GEMM; GEMM "
+            f"{r['gemm_TFLOPs_alone']:.0f} TFLOP/s alone, {r['gemm_TFLOPs_with_op']:.0f} beside")
     del bufs, out, a, b, c
     torch.cuda.empty_cache()
     return res
@@ -347,9 +358,11 @@ def main():
             tx = msx / Kg * 1e-3
             paths[name] = {"us": tx * 1e6, "GBps": gbytes / tx / 1e9, "bytes": gbytes, "W": c4["W"], "T": T}
             log(f"[bench] {name}: {tx * 1e6:.1f} us/launch, {gbytes / tx / 1e9:.1f} GB/s")
-        del gsets, shard_sets
+        del shard_sets
         torch.cuda.empty_cache()
-        paths["contention_fp32_512MiB"] = contention_leg(mr, torch, dev, stream)
+        paths["contention"] = contention_leg(mr, torch, dev, stream, gsets, gbytes)
+        del gsets
+        torch.cuda.empty_cache()
         if not args.no_sweep:
             paths["sweep_w8"] = sweep_leg(mr, torch, dev)
 

@@ -366,12 +366,16 @@ def test_config5_fp32_512MiB_alone_and_beside_a_gemm():
     with torch.cuda.stream(side):
         for _ in range(6):
             cgemm = torch.matmul(a, bm)
-    for mode in ("oneshot", "twoshot:tile"):
+    idx_dev = torch.from_numpy(idx).to(device())
+    for mode in MODES:  # every hand-off must make progress while GEMM workgroups hold the CUs
         out.zero_()
         _call(dbufs, out, mode)
+        got = to_bits(out.index_select(0, idx_dev))  # waits for this stream only; the GEMMs go on
+        assert_reduce_equal(got, want, "fp32", f"config5 {mode} under GEMM")
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                cgemm = torch.matmul(a, bm)
     torch.cuda.synchronize()
-    got = to_bits(out)
-    assert_reduce_equal(got[idx], want, "fp32", "config5 under GEMM")
     assert torch.isfinite(cgemm.float()).all()
     assert mr.workspace_check() == 0
     del dbufs, out, a, bm, cgemm
