@@ -109,6 +109,51 @@ def test_fp16_narrow_against_torch_and_exact():
         assert ie.same(ie.decode(int(g16), ie.FP16), want), hex(int(v))
 
 
+def _every_fp32_pattern(check, chunk_bits=23):
+    """Run check(u) over all 2^32 fp32 bit patterns in chunks, on the host's cores (numpy releases the
+    GIL inside its loops).  Returns the number of chunks checked."""
+    from concurrent.futures import ThreadPoolExecutor
+    step = 1 << chunk_bits
+
+    def one(k):
+        u = np.arange(k * step, (k + 1) * step, dtype=np.uint64).astype(np.uint32)
+        check(u)
+        return 1
+
+    threads = max(1, min(8, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(threads) as ex:
+        return sum(ex.map(one, range(1 << (32 - chunk_bits))))
+
+
+@pytest.mark.slow
+def test_bf16_narrow_every_fp32_pattern():
+    """All 2^32 fp32 patterns: the oracle's integer rounding against the nearest-neighbour formulation
+    (and torch's conversion on the non-NaN ones); NaNs stay NaN."""
+    def check(u):
+        got = oracle.narrow(u.view(np.float32), "bf16")
+        nan = _is_nan32(u)
+        ok = ~nan
+        assert np.array_equal(got[ok], _bf16_nearest(u[ok])), hex(int(u[0]))
+        tt = torch.from_numpy(u[ok].view(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got[ok], tt), hex(int(u[0]))
+        assert np.all(_is_nan16(got[nan], "bf16")), hex(int(u[0]))
+
+    assert _every_fp32_pattern(check) == 512
+
+
+@pytest.mark.slow
+def test_fp16_narrow_every_fp32_pattern():
+    """All 2^32 fp32 patterns: the oracle's fp16 narrowing against torch's CPU conversion; NaNs stay NaN."""
+    def check(u):
+        got = oracle.narrow(u.view(np.float32), "fp16")
+        nan = _is_nan32(u)
+        tt = torch.from_numpy(u.view(np.float32)).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got[~nan], tt[~nan]), hex(int(u[0]))
+        assert np.all(_is_nan16(got[nan], "fp16")), hex(int(u[0]))
+
+    assert _every_fp32_pattern(check) == 512
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_widen_is_exact_for_every_pattern(dtype):
     b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
