@@ -328,6 +328,46 @@ def test_reduce_matches_torch_cpu_loop(dtype, W):
     assert np.array_equal(out, ref.view(ibits).numpy().view(ub))
 
 
+def _structured_partners16(dtype: str) -> np.ndarray:
+    """4096 structured 16-bit partners: every exponent field with mantissas at 0 (powers of two), 1,
+    the half-way points and the top, plus random mantissas, in both signs (subnormals, inf and NaN
+    included)."""
+    g = np.random.default_rng(4096)
+    if dtype == "bf16":
+        eb, mb = 8, 7
+        fixed = [0, 1, 0x3F, 0x40, 0x41, 0x7F]
+    else:
+        eb, mb = 5, 10
+        fixed = [0, 1, 0x1FF, 0x200, 0x201, 0x3FF]
+    per_exp = 4096 // (2 << eb)
+    mants = []
+    for e in range(1 << eb):
+        m = fixed + list(g.integers(0, 1 << mb, size=per_exp - len(fixed)))
+        mants.append([(e << mb) | int(x) for x in m])
+    v = np.array(mants, dtype=np.uint32).ravel()
+    return np.concatenate([v, v | 0x8000]).astype(np.uint16)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_reduce_W2_every_pattern_against_structured_partners(dtype):
+    """W=2: each of the 65,536 patterns of x0 against 4,096 structured x1 (268M pairs) equals torch's
+    CPU widen, fp32 add and narrow; NaN results compare by NaN-ness."""
+    x0 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x1 = _structured_partners16(dtype)
+    assert len(x1) == 4096 and len(np.unique(x1)) > 3500
+    for k in range(0, 4096, 256):
+        a = np.repeat(x0, 256)
+        b = np.tile(x1[k:k + 256], 65536)
+        got = oracle.allreduce_sum_ref([a, b], dtype)
+        ta = torch.from_numpy(a.view(np.int16)).view(TORCH[dtype]).float()
+        tb = torch.from_numpy(b.view(np.int16)).view(TORCH[dtype]).float()
+        ref = (ta + tb).to(TORCH[dtype]).view(torch.int16).numpy().view(np.uint16)
+        rn = _is_nan16(ref, dtype)
+        assert np.array_equal(got[~rn], ref[~rn]), (dtype, k)
+        assert np.all(_is_nan16(got[rn], dtype)), (dtype, k)
+
+
 def test_reduce_rejects_int32():
     with pytest.raises(ValueError):
         oracle.allreduce_sum_ref([np.zeros(4, np.uint32)], "int32")
