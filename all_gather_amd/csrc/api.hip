@@ -52,6 +52,10 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Library-owned buffers that a larger workspace replaced.  Launches still in flight, and HIP graphs
+// that captured a two-shot call, may point at them, so they are freed only when the caller unbinds the
+// stream's workspace (mr_set_workspace).  Growth at least doubles, so they total less than the live one.
+std::map<std::pair<int, hipStream_t>, std::vector<char*>> g_retired;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -85,15 +89,11 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
     return MR_OK;
   }
   if (w.base && !w.owned) return MR_ERR_WORKSPACE;  // caller-owned and too small
-  if (w.base) {  // grow: earlier work on this stream may still use the old buffer
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e);
-    hipFree(w.base);
-    w = Workspace{};
-  }
-  void* p = nullptr;
-  const size_t bytes = round_up(ws_bytes_for(n, esize), size_t(1) << 20);
+  // Any size at or above the rule's also fits: the stage start moves by 1/64 of the extra bytes.
+  size_t bytes = round_up(ws_bytes_for(n, esize), size_t(1) << 20);
+  if (w.base && bytes < 2 * w.bytes) bytes = 2 * w.bytes;
   if (!ws_fits(bytes, n, esize, flags)) return MR_ERR_WORKSPACE;  // the sizing rule covers every plan
+  void* p = nullptr;
   e = hipMalloc(&p, bytes);
   if (e != hipSuccess) return hip_fail(e);
   e = ws_clear(static_cast<char*>(p), bytes, st);
@@ -101,6 +101,7 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
     hipFree(p);
     return hip_fail(e);
   }
+  if (w.base) g_retired[{dev, st}].push_back(w.base);  // grown: keep the old buffer alive (see g_retired)
   w.base = static_cast<char*>(p);
   w.bytes = bytes;
   w.owned = true;
@@ -452,10 +453,13 @@ mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {
   if (e != hipSuccess) return hip_fail(e);
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace& w = g_ws[{dev, st}];
-  if (w.base && w.owned) {
+  std::vector<char*>& old = g_retired[{dev, st}];
+  if ((w.base && w.owned) || !old.empty()) {  // free every library-owned buffer of this stream
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e);
-    hipFree(w.base);
+    if (w.base && w.owned) hipFree(w.base);
+    for (char* b : old) hipFree(b);
+    old.clear();
   }
   w = Workspace{};
   if (!dev_ptr) return MR_OK;

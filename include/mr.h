@@ -154,9 +154,12 @@ mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int
  * Two-shot workspace.
  *
  * By default the library allocates, on first two-shot use of a (device, stream) pair, a grow-only
- * workspace of mr_workspace_bytes() bytes holding the stage buffer and the barrier words; that first
- * call (and a call that grows it) allocates and is therefore not safe under graph capture.  One
- * workspace per (device, stream): two-shot calls on different streams never share barrier words.
+ * workspace of at least mr_workspace_bytes() bytes holding the stage buffer and the barrier words;
+ * that first call (and a call that grows it) allocates and is therefore not safe under graph capture.
+ * Growth at least doubles the size and keeps the replaced buffer alive, so launches in flight and HIP
+ * graphs that captured a two-shot call on the stream stay valid; replaced buffers are freed only by
+ * mr_set_workspace on that stream.  One workspace per (device, stream): two-shot calls on different
+ * streams never share barrier words.
  *
  * mr_workspace_bytes: bytes a caller-owned workspace needs for a two-shot call of this shape.
  * mr_set_workspace:   bind caller-owned device memory (256-byte aligned) as the workspace of `stream`
@@ -164,8 +167,10 @@ mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int
  *                     flags are cleared on `stream` here.  Memory too small to hold them plus some
  *                     stage -> MR_ERR_INVALID_ARG; a bound workspace too small for a later call makes
  *                     that call return MR_ERR_WORKSPACE.  dev_ptr == NULL unbinds (the library
- *                     allocates again on next use).  Not thread-safe against concurrent calls on that
- *                     stream.
+ *                     allocates again on next use).  Either way it synchronises `stream` and frees
+ *                     every library-owned workspace buffer of the stream, so a graph that captured a
+ *                     two-shot call on it must not be replayed afterwards.  Not thread-safe against
+ *                     concurrent calls on that stream.
  * mr_workspace_check: synchronises `stream`, then reads and clears the barrier error word of its
  *                     workspace.  *flags receives it (0 = no error; bit 0 = a phase-2 block gave up
  *                     waiting for phase 1, so that call's output is not valid).  Returns

@@ -92,3 +92,38 @@ def test_gathers_and_reduce_scatter_graph_replays():
         for o, h in zip(outs_list, hsh):
             assert np.array_equal(to_bits(o), h), rep
         assert_reduce_equal(to_bits(rs_out), oracle.reduce_scatter_sum_ref(hrs, "fp16", 5), "fp16", f"rs {rep}")
+
+
+def test_twoshot_graph_replays_after_the_workspace_grew():
+    """A graph captured with the stream's first (small) workspace is replayed after an eager call on the
+    same stream grew the workspace: the replaced buffer stays alive, so the replay still reads and
+    writes valid memory and gives the oracle's bits."""
+    W, n_small, n_big = 8, 300_001, 6_000_017
+    s = torch.cuda.Stream()
+    small = [torch.empty(n_small, dtype=torch.bfloat16, device=device()) for _ in range(W)]
+    out_small = torch.empty(n_small, dtype=torch.bfloat16, device=device())
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mr.allreduce_sum(small, out_small, mode="twoshot")  # first use: allocates the small workspace
+    torch.cuda.synchronize()
+    g = _capture(lambda: mr.allreduce_sum(small, out_small, mode="twoshot"), s)
+    big_host = workloads.rank_buffers(86, W, n_big, "bf16", "normal")
+    big = [to_dev(b, "bf16") for b in big_host]
+    out_big = torch.empty(n_big, dtype=torch.bfloat16, device=device())
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mr.allreduce_sum(big, out_big, mode="twoshot")  # grows this stream's workspace
+    torch.cuda.synchronize()
+    assert_reduce_equal(to_bits(out_big), oracle.allreduce_sum_ref(big_host, "bf16"), "bf16", "grown call")
+    for rep in range(3):
+        bufs = workloads.rank_buffers(87 + rep, W, n_small, "bf16", "normal")
+        for d, b in zip(small, bufs):
+            d.copy_(to_dev(b, "bf16"))
+        out_small.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_reduce_equal(to_bits(out_small), oracle.allreduce_sum_ref(bufs, "bf16"), "bf16", f"replay {rep}")
+    assert mr.workspace_check(s) == 0
+    del g
+    mr.set_workspace(None, stream=s)  # frees the live and the replaced buffers of this stream
