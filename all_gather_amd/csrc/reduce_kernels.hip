@@ -238,13 +238,28 @@ __device__ __forceinline__ void copy_edges_from_stage(const char* stage, char* d
 constexpr int kOneShotBlock = MR_OS_BLOCK;
 template <int W> struct OneShotU { static constexpr int value = W <= 8 ? MR_OS_U : 1; };
 
+// XCD-aware tile order.  Workgroups are handed to the 8 XCDs round-robin, so workgroup b runs on XCD
+// b % 8; xcd_tile is a bijection of [0, ntiles) that gives XCD x one contiguous run of tiles.  Whether
+// it pays depends on the grid (same-GPU A/B at W=8 bf16, three interleaved repeats, tile = b against
+// xcd_tile): it wins while the grid is small (256 KiB per rank, 256 tiles: 3.11 -> 2.41 us; 512 KiB:
+// 3.22 -> 2.73; 3 MiB, 768 tiles: 6.45 -> 6.23) and on the 1024 wide tiles of 16 MiB (26.8 -> 26.6),
+// and loses on larger grids (4 MiB as 1024 medium tiles: 8.0 -> 9.1; 32 MiB, 2048 tiles: 51.7 -> 52.8;
+// 64 MiB: 102 -> 109).  The host sets `xcd` from that (oneshot_vec_launch).
+__device__ __forceinline__ size_t xcd_tile(size_t b, size_t ntiles) {
+  constexpr size_t kXcds = 8;
+  const size_t q = ntiles / kXcds, rem = ntiles % kXcds, x = b % kXcds;
+  return x * q + (x < rem ? x : rem) + b / kXcds;
+}
+
 template <typename D, int W, int B, int U>
-__global__ __launch_bounds__(B) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
+__global__ __launch_bounds__(B) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles, int xcd) {
   const size_t hb = sh.head * D::kSize;
   u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
-  for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x)
+  for (size_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+    const size_t t = xcd ? xcd_tile(b, ntiles) : b;
     reduce_tile<D, W, B, U>(in, hb, t * (B * U), sh.npacks,
                             [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); });
+  }
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
 
@@ -513,7 +528,10 @@ hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& 
   const size_t ntiles = (sh.npacks + tile - 1) / tile;
   size_t grid = ntiles < kMaxGrid ? ntiles : kMaxGrid;
   if (grid == 0) grid = 1;  // edges only
-  hipLaunchKernelGGL((oneshot_vec<D, W, B, U>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh, ntiles);
+  // XCD-contiguous tile order on small grids and on the wide tiles up to 1024 of them (see xcd_tile)
+  const int xcd = grid == ntiles && (ntiles <= 512 || (tile == 1024 && ntiles <= 1024)) ? 1 : 0;
+  hipLaunchKernelGGL((oneshot_vec<D, W, B, U>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh, ntiles,
+                     xcd);
   return hipGetLastError();
 }
 
