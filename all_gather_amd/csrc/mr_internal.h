@@ -23,11 +23,10 @@ inline int elem_size(mr_dtype d) { return (d == MR_BF16 || d == MR_FP16) ? 2 : 4
 constexpr size_t kCtrlBytes = 16384;
 
 struct Ctrl {
-  uint32_t claim[MR_MAX_W][64];  // per-chunk ticket counters (start order of that chunk's workgroups)
+  uint32_t claim[MR_MAX_W][64];  // per-chunk ticket counters (grid barrier: phase-1 tile pools)
   uint32_t done1[MR_MAX_W][64];  // per-chunk phase-1 completions (chunk and grid barriers)
-  uint32_t done2[MR_MAX_W][64];  // per-chunk phase-2 completions (resets the chunk words)
-  uint32_t gclaim[64];           // grid ticket counter (grid barrier)
-  uint32_t gdone2[64];           // grid phase-2 completions
+  uint32_t done2[MR_MAX_W][64];  // per-chunk phase-2 completions (grid barrier: phase-2 group pools)
+  uint32_t gdone[64];            // workgroups finished (grid barrier)
   uint32_t err[64];              // bit 0: a wait gave up after the spin limit
 };
 static_assert(sizeof(Ctrl) <= kCtrlBytes, "ctrl layout");

@@ -296,28 +296,48 @@ __global__ __launch_bounds__(kBlock) void oneshot_elem(RankPtrs in, char* out, s
 //   tile  -- phase-2 tile q of chunk c waits for the flags of phase-1 tiles [q*ratio, (q+1)*ratio) of
 //            chunk c and clears them; the claim counter is cleared by the holder of the last ticket.
 //   chunk -- waits until done1[c] counts all t1 phase-1 tiles of chunk c.
-//   grid  -- waits until done1[x] counts all t1 phase-1 tiles of every chunk x (one ticket counter
-//            orders every workgroup; lanes 0..W-1 of the first wave wait for one chunk each).
+//   grid  -- waits until done1[x] counts all t1 phase-1 tiles of every chunk x (lanes 0..W-1 of the
+//            first wave wait for one chunk each).  Work comes from per-chunk pools (claim[c]: phase-1
+//            tiles, done2[c]: phase-2 groups): a workgroup tries its own chunk's pool first and the
+//            others after it, and takes phase-2 work only once it found every phase-1 pool empty, so
+//            every phase-1 tile has started before anyone waits.  The pools overshoot, so the last
+//            workgroup to finish (gdone counts all of them) clears every word.
 //   last  -- no phase-2 workgroups and no waiting: flags[c*t2 + q] counts the releases of group q of
 //            chunk c, and the workgroup whose release completes the group re-arms it and copies it.
 // In every mode the words return to zero by the end of the launch, so back-to-back launches on one
 // stream need no host reset.
+
+constexpr uint32_t kNoWork = 0xffffffffu;  // ticket of a workgroup that found no work (cannot happen:
+                                           // the grid holds exactly one workgroup per work item)
 
 __device__ __forceinline__ void take_ticket(Ctrl* ctrl, const TwoShotPlan& pl, uint32_t& c, uint32_t& k) {
   __shared__ uint32_t s_c, s_k;
   if (threadIdx.x == 0) {
     const uint32_t per = pl.t1 + pl.t2;
     if (pl.sync == kSyncGrid) {
-      const uint32_t g = __hip_atomic_fetch_add(&ctrl->gclaim[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (g == pl.chunks * per - 1) __hip_atomic_store(&ctrl->gclaim[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t n1 = pl.chunks * pl.t1;
-      if (g < n1) {
-        s_c = g / pl.t1;
-        s_k = g % pl.t1;
-      } else {  // phase-2 tiles take the chunks in reverse order
-        const uint32_t h = g - n1;
-        s_c = (pl.chunks - 1) - h / pl.t2;
-        s_k = pl.t1 + h % pl.t2;
+      // one fetch-and-add per pool tried; a pool is empty once its counter reached its size, and
+      // stays so (the counters only grow during a launch)
+      const uint32_t c0 = blockIdx.x % pl.chunks;
+      s_c = 0;
+      s_k = kNoWork;
+      bool got = false;
+      for (uint32_t i = 0; i < pl.chunks && !got; ++i) {
+        const uint32_t cc = c0 + i < pl.chunks ? c0 + i : c0 + i - pl.chunks;
+        const uint32_t t = __hip_atomic_fetch_add(&ctrl->claim[cc][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t < pl.t1) {
+          s_c = cc;
+          s_k = t;
+          got = true;
+        }
+      }
+      for (uint32_t i = 0; i < pl.chunks && !got; ++i) {
+        const uint32_t cc = c0 + i < pl.chunks ? c0 + i : c0 + i - pl.chunks;
+        const uint32_t t = __hip_atomic_fetch_add(&ctrl->done2[cc][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t < pl.t2) {
+          s_c = cc;
+          s_k = pl.t1 + t;
+          got = true;
+        }
       }
     } else {
       const uint32_t cc = blockIdx.x % pl.chunks;
@@ -374,20 +394,26 @@ __device__ __forceinline__ void wait_phase1(Ctrl* ctrl, uint32_t* flags, const T
   __syncthreads();
 }
 
-__device__ __forceinline__ void finish_phase2(Ctrl* ctrl, const TwoShotPlan& pl, uint32_t c) {
-  if (threadIdx.x != 0 || pl.sync == kSyncTile) return;
-  if (pl.sync == kSyncChunk) {
+// End of a workgroup's two-shot work (k = its ticket).  Chunk barrier: the last phase-2 tile of chunk c
+// clears that chunk's words.  Grid barrier: every workgroup counts itself out, and the last one clears
+// the pools and counters of every chunk (no workgroup can still be claiming work then).
+__device__ __forceinline__ void finish_twoshot(Ctrl* ctrl, const TwoShotPlan& pl, uint32_t c, uint32_t k) {
+  if (threadIdx.x != 0) return;
+  if (pl.sync == kSyncChunk && k >= pl.t1) {
     const uint32_t d = __hip_atomic_fetch_add(&ctrl->done2[c][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == pl.t2 - 1) {
       __hip_atomic_store(&ctrl->done1[c][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&ctrl->done2[c][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-  } else {
-    const uint32_t d = __hip_atomic_fetch_add(&ctrl->gdone2[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == pl.chunks * pl.t2 - 1) {
-      for (uint32_t x = 0; x < pl.chunks; ++x)
+  } else if (pl.sync == kSyncGrid) {
+    const uint32_t d = __hip_atomic_fetch_add(&ctrl->gdone[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == pl.chunks * (pl.t1 + pl.t2) - 1) {
+      for (uint32_t x = 0; x < pl.chunks; ++x) {
+        __hip_atomic_store(&ctrl->claim[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&ctrl->done1[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ctrl->gdone2[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctrl->done2[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(&ctrl->gdone[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -465,12 +491,12 @@ __global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* 
       const uint32_t q = k / pl.ratio;
       copy_group<D, TB>(out, stage, sh, c0 + static_cast<size_t>(q) * (TB * kRatio), cend, c == 0 && q == 0);
     }
-  } else {
+  } else if (k < pl.t1 + pl.t2) {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
     copy_group<D, TB>(out, stage, sh, c0 + static_cast<size_t>(q) * (TB * kRatio), cend, c == 0 && q == 0);
-    finish_phase2(ctrl, pl, c);
   }
+  finish_twoshot(ctrl, pl, c, k);
 }
 
 // Element-wise two-shot for pointers that do not share one 16-byte alignment (one element per unit).
@@ -504,12 +530,12 @@ __global__ __launch_bounds__(kBlock) void twoshot_elem(RankPtrs in, char* out, c
     publish_phase1(ctrl, flags, pl, c, k);
     if (pl.sync == kSyncLast && arrive_last(flags, pl, c, k))
       copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(k / pl.ratio) * (kBlock * kRatio), cend);
-  } else {
+  } else if (k < pl.t1 + pl.t2) {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
     copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(q) * (kBlock * kRatio), cend);
-    finish_phase2(ctrl, pl, c);
   }
+  finish_twoshot(ctrl, pl, c, k);
 }
 
 __global__ void zero_words(uint32_t* p, size_t words) {
