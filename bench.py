@@ -108,6 +108,28 @@ def _overlap(torch, stream, side, call, R, gemm, G):
     return t_op, t_gemm, r0.elapsed_time(r1) / R * 1e-3, g0.elapsed_time(g1) / G * 1e-3
 
 
+def copy_ceiling(mr, torch, dev, stream, reps=40):
+    """Secondary ceiling: GB/s (read + write bytes) of a plain 256 MiB device-to-device copy made by this
+    library's gather kernel (all_gather_into_tensor of one shard: 16-byte non-temporal loads and
+    stores), timed the same way on the same GPU.  The runtime's own blit copy is slower (about
+    5.3 TB/s), so it would understate the ceiling."""
+    a = torch.empty(1 << 26, dtype=torch.int32, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    call = mr.prepare_allgather_shards([a], b)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * (1 << 28) / t / 1e9
+
+
 def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes):
     """Ops alone and beside bf16 8192^3 GEMMs on a second stream (default priority): W=8 fp32 one-shot
     and two-shot at 512 MiB per rank, and the config-4 param-contiguous scatter.  GB/s of the op and
@@ -298,6 +320,8 @@ def main():
     gbs = algo / t_launch / 1e9
     log(f"[bench] oneshot: {ms / K * 1e3:.2f} us/launch, {gbs:.1f} GB/s ({gbs / PEAK_GBS:.1%} of peak)")
     traffic, traffic_src = traffic_from_profile(algo)
+    copy_gbs = copy_ceiling(mr, torch, dev, stream)
+    log(f"[bench] plain 256 MiB copy (gather kernel, one shard) on the same GPU: {copy_gbs:.1f} GB/s")
 
     paths = {}
     if not args.only_headline:
@@ -416,7 +440,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "oneshot_vec<Bf16, 8>", "bytes_per_launch": algo,
-                     "avg_launch_us": round(t_launch * 1e6, 3), "traffic_source": traffic_src},
+                     "avg_launch_us": round(t_launch * 1e6, 3), "traffic_source": traffic_src,
+                     "traffic_GBps": round(traffic / t_launch / 1e9, 1) if traffic else None,
+                     "copy_ceiling_GBps": round(copy_gbs, 1),
+                     "copy_ceiling_kernel": "param_contig<4>: all_gather_into_tensor of one 256 MiB shard",
+                     "frac_of_copy_ceiling": round(gbs / copy_gbs, 4)},
         "cpu_baseline": cpu,
         "paths": paths,
     }
