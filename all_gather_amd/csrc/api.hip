@@ -17,19 +17,21 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-uint32_t env_u32(const char* name, uint32_t dflt) {
+// An option's initial value from the environment: a whole number in [lo, hi], else the default (the
+// same ranges mr_set_option accepts).
+uint32_t env_u32(const char* name, uint32_t dflt, unsigned long lo, unsigned long hi) {
   const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
+  if (!v || !*v || *v == '-') return dflt;
   char* end = nullptr;
-  unsigned long x = std::strtoul(v, &end, 0);
-  return (end && *end == 0) ? static_cast<uint32_t>(x) : dflt;
+  const unsigned long x = std::strtoul(v, &end, 0);
+  return (end && *end == 0 && x >= lo && x <= hi) ? static_cast<uint32_t>(x) : dflt;
 }
 
 // Process-wide options (mr_set_option); defaults may be overridden by the environment at load.
-std::atomic<uint32_t> g_spin_limit{env_u32("MR_SPIN_LIMIT", 1u << 22)};
-std::atomic<uint32_t> g_twoshot_sync{env_u32("MR_TWOSHOT_SYNC", mr::kSyncAuto)};
-std::atomic<uint32_t> g_tile_shape{env_u32("MR_TILE_SHAPE", mr::kShapeAuto)};
-const bool g_trace = env_u32("MR_TRACE", 0) != 0;
+std::atomic<uint32_t> g_spin_limit{env_u32("MR_SPIN_LIMIT", 1u << 22, 0, 0xffffffffUL)};
+std::atomic<uint32_t> g_twoshot_sync{env_u32("MR_TWOSHOT_SYNC", mr::kSyncAuto, MR_TWOSHOT_SYNC_TILE, MR_TWOSHOT_SYNC_AUTO)};
+std::atomic<uint32_t> g_tile_shape{env_u32("MR_TILE_SHAPE", mr::kShapeAuto, MR_TILE_AUTO, MR_TILE_NARROW)};
+const bool g_trace = env_u32("MR_TRACE", 0, 0, 1) != 0;
 
 mr_status hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -288,7 +290,7 @@ const char* mr_status_string(mr_status s) {
 
 int mr_last_hip_error(void) { return g_last_hip_error; }
 
-int mr_version(void) { return 100; }
+int mr_version(void) { return 101; }
 
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
   if (W < 1 || W > MR_MAX_W || !is_float(dtype)) return 0;

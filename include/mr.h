@@ -204,7 +204,9 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  *   MR_TILE_MEDIUM one-shot 256 x 1, two-shot 256-pack tiles;
  *   MR_TILE_NARROW one-shot 64 x 1, two-shot 64-pack tiles.
  * Unknown options or out-of-range values -> MR_ERR_INVALID_ARG.  Environment variables
- * MR_TWOSHOT_SYNC, MR_SPIN_LIMIT and MR_TILE_SHAPE set the initial values when the library loads.
+ * MR_TWOSHOT_SYNC, MR_SPIN_LIMIT and MR_TILE_SHAPE set the initial values when the library loads; a
+ * value that is not a whole number in the option's range is ignored.  MR_TRACE=1 makes every launch
+ * print its plan (path, shape, grid) to stderr.
  */
 typedef enum mr_option { MR_OPT_TWOSHOT_SYNC = 0, MR_OPT_SPIN_LIMIT = 1, MR_OPT_TILE_SHAPE = 2 } mr_option;
 #define MR_TWOSHOT_SYNC_TILE 0
@@ -219,7 +221,8 @@ typedef enum mr_option { MR_OPT_TWOSHOT_SYNC = 0, MR_OPT_SPIN_LIMIT = 1, MR_OPT_
 mr_status mr_set_option(mr_option opt, int64_t value);
 mr_status mr_get_option(mr_option opt, int64_t* value);
 
-/* Library ABI version (major*100 + minor). */
+/* Library ABI version (major*100 + minor).  1.01 added MR_OPT_TILE_SHAPE, MR_TWOSHOT_SYNC_LAST and
+ * MR_TWOSHOT_SYNC_AUTO (the new default hand-off). */
 int mr_version(void);
 
 #ifdef __cplusplus

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mr_version() == 100
+    assert L.mr_version() == 101
     for code, name in mr.STATUS.items():
         assert L.mr_status_string(code).decode().startswith(name)
     assert b"unknown" in L.mr_status_string(-99)
@@ -150,6 +150,27 @@ def test_options_validate_and_round_trip(L):
     for shape in ("wide", "medium", "narrow", "auto"):
         mr.set_option("tile_shape", shape)
         assert mr.get_option("tile_shape") == shape
+
+
+def test_environment_sets_initial_options(tmp_path):
+    """MR_TWOSHOT_SYNC, MR_SPIN_LIMIT and MR_TILE_SHAPE give the options' values when the library loads
+    (in a fresh process; malformed values fall back to the defaults)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import all_gather_amd as mr; "
+            "print(mr.get_option('twoshot_sync'), mr.get_option('spin_limit'), mr.get_option('tile_shape'))"
+            % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    env = dict(os.environ, MR_TWOSHOT_SYNC="2", MR_SPIN_LIMIT="77", MR_TILE_SHAPE="3")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["grid", "77", "narrow"]
+    for bad in (dict(MR_TWOSHOT_SYNC="x", MR_SPIN_LIMIT="", MR_TILE_SHAPE="3z"),
+                dict(MR_TWOSHOT_SYNC="9", MR_SPIN_LIMIT="-1", MR_TILE_SHAPE="4"),
+                dict(MR_TWOSHOT_SYNC="-2", MR_SPIN_LIMIT="4294967296", MR_TILE_SHAPE="0x10")):
+        out = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, **bad), capture_output=True,
+                             text=True, timeout=120)
+        assert out.returncode == 0, out.stderr
+        assert out.stdout.split() == ["auto", str(1 << 22), "auto"], bad
 
 
 def test_binding_rejects_host_tensors():
