@@ -84,3 +84,27 @@ def test_param_contig_from_shards_ragged_and_many_params():
     mr.allgather_param_contig_shards(dshards, G, splits, out)
     torch.cuda.synchronize()
     assert np.array_equal(to_bits(out), oracle.allgather_param_contig_shards_ref(shards, G, splits))
+
+
+def test_empty_inputs_are_no_ops():
+    """n = 0 and T = 0 through every entry point: success, nothing written, the stream still works."""
+    W = 8
+    empty = [torch.empty(0, dtype=torch.bfloat16, device=device()) for _ in range(W)]
+    out0 = torch.empty(0, dtype=torch.bfloat16, device=device())
+    for mode in ("oneshot", "twoshot"):
+        mr.allreduce_sum(empty, out0, mode=mode)
+    mr.reduce_scatter_sum(empty, 3, out0)
+    mr.allgather_into_tensor(empty, out0)
+    mr.allgather_list(empty, [torch.empty(0, dtype=torch.bfloat16, device=device()) for _ in range(W)])
+    mr.allgather_param_contig_shards(empty, 4, [0, 0, 0], out0)
+    mr.allgather_param_contig(out0, W, 4, [0, 0], out0)
+    # a sentinel output next to the empty calls stays untouched, and real work still runs afterwards
+    sentinel = torch.full((64,), 7, dtype=torch.int32, device=device())
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7).all())
+    bufs = workloads.rank_buffers(303, W, 1000, "bf16", "uniform")
+    out = torch.empty(1000, dtype=torch.bfloat16, device=device())
+    mr.allreduce_sum([to_dev(b, "bf16") for b in bufs], out, mode="twoshot")
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), oracle.allreduce_sum_ref(bufs, "bf16"))
+    assert mr.workspace_check() == 0
