@@ -10,8 +10,9 @@
 // Tile boundaries fall on 256-byte lines of the destination, so two workgroups never write parts of
 // one line (a partial line costs a full one: aligning them cut the scatter's time by about 4%).
 // 512-lane workgroups moving 16 KiB (two 16-byte words per lane) measured best among 256..1024 lanes
-// and 8..128 KiB tiles.  The copy is a bit copy with 64-bit offsets; 16-byte
-// non-temporal loads and stores when source and destination share the same 16-byte phase.
+// and 8..128 KiB tiles.  The copy is a bit copy with 64-bit offsets; 16-byte non-temporal loads and
+// stores when source and destination share the same 16-byte phase, else 4-byte (or 2-byte) words with
+// the whole tile's loads in flight before its stores.
 
 #include "mr_internal.h"
 
@@ -28,6 +29,28 @@ template <int S>
 __device__ __forceinline__ void copy_elem(const char* src, char* dst, uint32_t o) {
   if (S == 2) *reinterpret_cast<uint16_t*>(dst + o) = *reinterpret_cast<const uint16_t*>(src + o);
   else *reinterpret_cast<uint32_t*>(dst + o) = *reinterpret_cast<const uint32_t*>(src + o);
+}
+
+// Copy `n` words of type Wd (src and dst both Wd-aligned), a whole tile's loads in flight before its
+// stores: the path for spans whose source and destination have different 16-byte phases.
+template <typename Wd>
+__device__ __forceinline__ void copy_words(const char* src, char* dst, uint32_t n) {
+  constexpr int U = kGatherTileBytes / (static_cast<int>(sizeof(Wd)) * kGB);  // words per lane per tile
+  const Wd* s = reinterpret_cast<const Wd*>(src);
+  Wd* d = reinterpret_cast<Wd*>(dst);
+  for (uint32_t w0 = 0; w0 < n; w0 += U * kGB) {
+    Wd v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = w0 + u * kGB + threadIdx.x;
+      if (i < n) v[u] = __builtin_nontemporal_load(s + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = w0 + u * kGB + threadIdx.x;
+      if (i < n) __builtin_nontemporal_store(v[u], d + i);
+    }
+  }
 }
 
 // Copy `len` (<= one tile) bytes of whole elements.
@@ -58,9 +81,18 @@ __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t l
     const uint32_t tail0 = head + body;
     const uint32_t edge = head + (len - tail0);
     for (uint32_t b = threadIdx.x * S; b < edge; b += kGB * S) copy_elem<S>(src, dst, b < head ? b : tail0 + (b - head));
+  } else if (((ps ^ pd) & 3u) == 0) {
+    // different 16-byte phases, same 4-byte phase (split sizes that are not a multiple of the pack):
+    // a 2-byte element up to 4-byte alignment, 4-byte words, a 2-byte element at the end
+    const uint32_t head = (S == 2 && (ps & 2u) && len >= 2) ? 2u : 0u;
+    if (head && threadIdx.x == 0) copy_elem<2>(src, dst, 0);
+    const uint32_t nw = (len - head) >> 2;
+    copy_words<uint32_t>(src + head, dst + head, nw);
+    const uint32_t tail0 = head + (nw << 2);
+    if (tail0 < len && threadIdx.x == 0) copy_elem<2>(src, dst, tail0);
   } else {
-    // different phases: element copies (odd split sizes with 2-byte elements)
-    for (uint32_t b = threadIdx.x * S; b < len; b += kGB * S) copy_elem<S>(src, dst, b);
+    // 2-byte elements whose 4-byte phases differ: 2-byte words
+    copy_words<uint16_t>(src, dst, len >> 1);
   }
 }
 

@@ -370,6 +370,21 @@ def main():
         paths["param_contig"] = {"us": tg * 1e6, "GBps": gbytes / tg / 1e9, "bytes": gbytes, "W": c4["W"],
                                  "G": c4["G"], "P": c4["P"], "T": T, "dtype": "bf16"}
         log(f"[bench] param_contig: {tg * 1e6:.1f} us/launch, {gbytes / tg / 1e9:.1f} GB/s ({gbytes} B)")
+        # the same splits in fp32 (4-byte elements: twice the bytes of the bf16 case)
+        fsets = []
+        for k in range(2):
+            src = torch.randint(-2 ** 31, 2 ** 31 - 1, (c4["W"] * T,), dtype=torch.int32, device=dev).view(torch.float32)
+            fsets.append(mr.prepare_allgather_param_contig(src, c4["W"], c4["G"], splits, torch.empty_like(src)))
+        fbytes = 2 * c4["W"] * T * 4
+        msf = time_steps(fsets, Kg, max(2, args.warmup // 10), stream)
+        tf = msf / Kg * 1e-3
+        paths["param_contig_fp32"] = {"us": tf * 1e6, "GBps": fbytes / tf / 1e9, "bytes": fbytes, "W": c4["W"],
+                                      "G": c4["G"], "P": c4["P"], "T": T, "dtype": "fp32",
+                                      "frac": fbytes / tf / 1e9 / PEAK_GBS}
+        log(f"[bench] param_contig fp32: {tf * 1e6:.1f} us/launch, {fbytes / tf / 1e9:.1f} GB/s "
+            f"({fbytes / tf / 1e9 / PEAK_GBS:.1%} of peak)")
+        del fsets
+        torch.cuda.empty_cache()
         # the same gathers written straight from W separate shard buffers
         shard_sets = []
         for k in range(2):

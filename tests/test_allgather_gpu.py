@@ -143,3 +143,18 @@ def test_more_split_sets_than_cached_plans():
             mr.allgather_param_contig(to_dev(src, "bf16"), W, G, splits, out)
             torch.cuda.synchronize()
             assert np.array_equal(to_bits(out), oracle.allgather_param_contig_ref(src, W, G, splits)), (rep, k)
+
+
+@pytest.mark.parametrize("dtype,E", [("fp32", 4099), ("fp32", 420_349), ("bf16", 4097), ("bf16", 262_147)])
+def test_equal_splits_with_unaligned_sizes(dtype, E):
+    """64 equal splits whose byte size is not a multiple of 16: segments take every combination of
+    source and destination 16-byte (and, for bf16, 4-byte) phase, so the word-copy paths run at scale."""
+    W, G, P = 8, 4, 64
+    splits = [E] * P
+    T = E * P
+    print(f"[case] equal unaligned splits {dtype} E={E}", flush=True)
+    src = workloads.gather_source(400 + E % 97, W, T, dtype)
+    out = torch.empty(W * T, dtype=TORCH_DT[dtype], device=device())
+    mr.allgather_param_contig(to_dev(src, dtype), W, G, splits, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), oracle.allgather_param_contig_ref(src, W, G, splits))
