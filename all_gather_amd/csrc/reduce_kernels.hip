@@ -431,6 +431,12 @@ static_assert(kRatio >= 1 && kRatio <= 64, "one lane of the first wave waits for
 // each chunk still splits into enough tiles to fill the CUs.
 constexpr int kTBlock = MR_TS_BLOCK;
 constexpr int kP2 = kRatio;  // packs per lane, phase 2
+// Element-wise path (pointers in different 16-byte phases): elements per lane per phase-1 tile.  Same-GPU
+// A/B, W=8 bf16, 16 MiB per rank, inputs at alternating 2-byte phases: one element per lane with the
+// loads issued one element at a time 92 us; with a lane's loads all in flight first, 1 / 2 / 4 / 8
+// elements per lane 88.5 / 94.7 / 86.5 / 137 us (eight ranks of eight elements outrun the 63
+// outstanding loads a wave can count).  The 16-byte path takes 35.6 us.
+constexpr int kElemPer = 4;
 
 // Phase 2 of one group: copy phase-2 tile q of chunk c (ratio phase-1 tiles) from the stage to out with
 // device-scope stage loads.
@@ -504,15 +510,44 @@ __global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* 
   finish_twoshot(ctrl, pl, c, k);
 }
 
-// Element-wise two-shot for pointers that do not share one 16-byte alignment (one element per unit).
+// Element-wise two-shot for pointers that do not share one 16-byte alignment (units are elements;
+// a phase-2 group copies ratio phase-1 tiles, kElemPer elements per lane each).
 template <typename D>
 __device__ __forceinline__ void copy_group_elem(char* out, const char* stage, size_t first, size_t cend) {
+  constexpr int N = kRatio * kElemPer;  // elements per lane
+  uint32_t v[N];
 #pragma unroll
-  for (uint32_t u = 0; u < kRatio; ++u) {
-    const size_t e = first + u * kBlock + threadIdx.x;
+  for (int u = 0; u < N; ++u) {
+    const size_t e = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
+    if (e < cend) v[u] = load_bits<D::kSize, true>(stage + e * D::kSize);
+  }
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const size_t e = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
+    if (e < cend) store_bits<D::kSize, false>(out + e * D::kSize, v[u]);
+  }
+}
+
+// Phase-1 tile of the element-wise path: kElemPer elements per lane at stride kBlock (each step
+// coalesced), every rank's loads in flight before the adds.
+template <typename D, int W>
+__device__ __forceinline__ void reduce_tile_elem(const RankPtrs& in, char* stage, size_t first, size_t cend) {
+  uint32_t v[kElemPer][W];
+#pragma unroll
+  for (int r = 0; r < W; ++r)
+#pragma unroll
+    for (int u = 0; u < kElemPer; ++u) {
+      const size_t e = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
+      if (e < cend) v[u][r] = load_bits<D::kSize, false>(in.p[r] + e * D::kSize);
+    }
+#pragma unroll
+  for (int u = 0; u < kElemPer; ++u) {
+    const size_t e = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
     if (e < cend) {
-      const size_t off = e * D::kSize;
-      store_bits<D::kSize, false>(out + off, load_bits<D::kSize, true>(stage + off));
+      float acc = D::widen1(v[u][0]);
+#pragma unroll
+      for (int r = 1; r < W; ++r) acc = acc + D::widen1(v[u][r]);
+      store_bits<D::kSize, true>(stage + e * D::kSize, D::narrow1(acc));
     }
   }
 }
@@ -527,18 +562,18 @@ __global__ __launch_bounds__(kBlock) void twoshot_elem(RankPtrs in, char* out, c
   } else {
     take_ticket(ctrl, pl, c, k);
   }
+  constexpr size_t kTileE = static_cast<size_t>(kBlock) * kElemPer;  // elements per phase-1 tile
   const size_t c0 = static_cast<size_t>(c) * pl.chunk_units;
   const size_t cend = c0 + pl.chunk_units < sh.n ? c0 + pl.chunk_units : sh.n;
   if (k < pl.t1) {
-    const size_t e = c0 + static_cast<size_t>(k) * kBlock + threadIdx.x;
-    if (e < cend) reduce_elem<D, W, true>(in, stage, e);
+    reduce_tile_elem<D, W>(in, stage, c0 + static_cast<size_t>(k) * kTileE, cend);
     publish_phase1(ctrl, flags, pl, c, k);
     if (pl.sync == kSyncLast && arrive_last(flags, pl, c, k))
-      copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(k / pl.ratio) * (kBlock * kRatio), cend);
+      copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(k / pl.ratio) * (kTileE * kRatio), cend);
   } else if (k < pl.t1 + pl.t2) {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
-    copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(q) * (kBlock * kRatio), cend);
+    copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(q) * (kTileE * kRatio), cend);
   }
   finish_twoshot(ctrl, pl, c, k);
 }
@@ -660,7 +695,7 @@ TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t s
   pl.chunks = static_cast<uint32_t>(W);
   const size_t units = sh.vec ? sh.npacks : sh.n;
   pl.chunk_units = (units + W - 1) / W;
-  pl.unit1 = sh.vec ? twoshot_tile_packs(sh.npacks, sync, shape) : kBlock;
+  pl.unit1 = sh.vec ? twoshot_tile_packs(sh.npacks, sync, shape) : kBlock * kElemPer;
   pl.ratio = kRatio;
   pl.unit2 = pl.unit1 * kRatio;
   size_t t1 = (pl.chunk_units + pl.unit1 - 1) / pl.unit1;
