@@ -174,7 +174,9 @@ struct GatherPlan {
   std::vector<mr::GatherArgs> groups;
 };
 
-mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, GatherPlan* gp) {
+// span: tiles cut per parameter over its W*E_s contiguous destination elements (every param-major
+// output); otherwise per (node-block, parameter, slot) segment (the list output's separate buffers).
+mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, bool span, GatherPlan* gp) {
   if (G < 1 || W % G != 0) return MR_ERR_INVALID_ARG;
   if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
@@ -198,19 +200,21 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
     a.W = static_cast<uint32_t>(W);
     a.G = static_cast<uint32_t>(G);
     a.elem = static_cast<uint32_t>(es);
+    a.span = span ? 1u : 0u;
     uint64_t tiles = 0;
     for (int i = 0; i < np; ++i) {
       a.O[i] = base;
       a.tile_prefix[i] = static_cast<uint32_t>(tiles);
       const uint64_t E = splits[s0 + i];
-      tiles += static_cast<uint64_t>(G) * mr::gather_tiles_per_segment(E, static_cast<uint32_t>(es));
+      tiles += span ? mr::gather_tiles_per_segment(E * static_cast<uint64_t>(W), static_cast<uint32_t>(es))
+                    : static_cast<uint64_t>(G) * mr::gather_tiles_per_segment(E, static_cast<uint32_t>(es));
       base += E;
       if (tiles >= (1ull << 31)) return MR_ERR_INVALID_ARG;
     }
     a.O[np] = base;
     a.tile_prefix[np] = static_cast<uint32_t>(tiles);
     a.tiles_per_block = static_cast<uint32_t>(tiles);
-    const uint64_t total = tiles * static_cast<uint64_t>(W / G);
+    const uint64_t total = span ? tiles : tiles * static_cast<uint64_t>(W / G);
     if (total >= (1ull << 32)) return MR_ERR_INVALID_ARG;
     a.total_tiles = static_cast<uint32_t>(total);
     gp->groups.push_back(a);
@@ -223,6 +227,7 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
 // tables nor allocates.  Failed plans are not kept.
 struct CachedPlan {
   bool used = false;
+  bool span = false;
   int W = 0, G = 0, P = 0;
   mr_dtype dtype = MR_BF16;
   std::vector<uint64_t> splits;
@@ -232,11 +237,12 @@ constexpr int kPlanSlots = 8;
 thread_local CachedPlan t_plans[kPlanSlots];
 thread_local int t_plan_next = 0;
 
-mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, const GatherPlan** out) {
+mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, bool span,
+                             const GatherPlan** out) {
   if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
   const size_t key_bytes = static_cast<size_t>(P) * sizeof(uint64_t);
   for (const CachedPlan& c : t_plans)
-    if (c.used && c.W == W && c.G == G && c.P == P && c.dtype == dtype &&
+    if (c.used && c.span == span && c.W == W && c.G == G && c.P == P && c.dtype == dtype &&
         std::memcmp(c.splits.data(), splits, key_bytes) == 0) {
       *out = &c.plan;
       return MR_OK;
@@ -245,8 +251,9 @@ mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dty
   t_plan_next = (t_plan_next + 1) % kPlanSlots;
   c.used = false;
   c.plan.groups.clear();
-  const mr_status s = gather_plan(W, G, splits, P, dtype, &c.plan);
+  const mr_status s = gather_plan(W, G, splits, P, dtype, span, &c.plan);
   if (s != MR_OK) return s;
+  c.span = span;
   c.W = W;
   c.G = G;
   c.P = P;
@@ -264,8 +271,8 @@ mr_status gather_launch(const GatherPlan& gp, Bind bind, hipStream_t st) {
     mr::GatherArgs a = g;
     bind(a);
     if (g_trace)
-      std::fprintf(stderr, "[mr] gather W=%u G=%u params=%u T=%llu tiles=%u src_table=%u dst_table=%u\n", a.W, a.G,
-                   a.P, static_cast<unsigned long long>(a.T), a.total_tiles, a.src_table, a.dst_table);
+      std::fprintf(stderr, "[mr] gather W=%u G=%u params=%u T=%llu tiles=%u span=%u src_table=%u dst_table=%u\n", a.W,
+                   a.G, a.P, static_cast<unsigned long long>(a.T), a.total_tiles, a.span, a.src_table, a.dst_table);
     const hipError_t e = mr::launch_param_contig(a, st);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -380,7 +387,7 @@ mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_
                                     void* out, mr_stream stream) {
   if (W < 1 || W > 65535) return MR_ERR_INVALID_ARG;
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, G, splits, P, dtype, &gp);
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, true, &gp);
   if (s != MR_OK || gp->T == 0) return s;
   if (!src || !out) return MR_ERR_INVALID_ARG;
   const uint64_t total_bytes = static_cast<uint64_t>(W) * gp->T * gp->es;
@@ -396,7 +403,7 @@ mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int
                                            mr_dtype dtype, void* out, mr_stream stream) {
   if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, G, splits, P, dtype, &gp);
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, true, &gp);
   if (s != MR_OK || gp->T == 0) return s;
   if (!shards || !out) return MR_ERR_INVALID_ARG;
   const uint64_t shard_bytes = gp->T * gp->es, out_bytes = static_cast<uint64_t>(W) * shard_bytes;
@@ -424,7 +431,7 @@ mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype
   if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
   const uint64_t split = T;
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, W, &split, 1, dtype, &gp);
+  mr_status s = cached_gather_plan(W, W, &split, 1, dtype, false, &gp);
   if (s != MR_OK || gp->T == 0) return s;
   if (!shards || !outs) return MR_ERR_INVALID_ARG;
   const uint64_t bytes = gp->T * gp->es;

@@ -137,14 +137,17 @@ struct GatherArgs {
   const char* src_tab[kMaxTable];        // with src_table: rank r's shard (T elements)
   char* dst_tab[kMaxTable];              // with dst_table: rank r's own output (T elements)
   uint32_t src_table, dst_table;
+  uint32_t span;                         // 1: tiles cut per parameter across its W ranks (param-major
+                                         // destination); 0: per (node-block, parameter, slot) segment
   uint64_t T;                            // elements per rank shard
   uint64_t O[kMaxParams + 1];            // O[s]: element offset of parameter s inside a shard; O[P] = its end
-  uint32_t tile_prefix[kMaxParams + 1];  // node-block-local tile prefix: G * sum of tiles of params < s
+  uint32_t tile_prefix[kMaxParams + 1];  // span: tiles of params < s; else node-block-local: G * tiles
+                                         // per segment of params < s
   uint32_t P;
   uint32_t W, G;
   uint32_t elem;                         // bytes per element
-  uint32_t tiles_per_block;              // tiles of one node-block (= tile_prefix[P])
-  uint32_t total_tiles;                  // W/G node-blocks * tiles_per_block
+  uint32_t tiles_per_block;              // tiles of one node-block (= tile_prefix[P]; span: all tiles)
+  uint32_t total_tiles;                  // span: tile_prefix[P]; else W/G node-blocks * tiles_per_block
 };
 
 hipError_t launch_param_contig(const GatherArgs& a, hipStream_t st);
