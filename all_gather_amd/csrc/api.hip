@@ -171,8 +171,16 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
 struct GatherPlan {
   uint64_t T = 0;
   uint64_t es = 0;
+  // Phase of every piece (parameter s, rank r) of a param-major output, as bit (dst_off - src_off) mod 16,
+  // where dst_off = (O_s*W + r*E_s)*es.  A launch may take the lean kernel build only if, for the call's
+  // base pointers, every piece's source and destination share a 16-byte phase.
+  uint16_t rm_mask = 0;              // source rank-major: src_off = (r*T + O_s)*es (period 16 in r)
+  std::vector<uint16_t> rank_mask;   // source from per-rank pointers: src_off = O_s*es, one mask per rank
   std::vector<mr::GatherArgs> groups;
 };
+
+// Does a bit other than bit d (the call's base-pointer difference mod 16) appear in the mask?
+bool needs_realign(uint16_t mask, uintptr_t d) { return (mask & ~(1u << (d & 15u))) != 0; }
 
 // span: tiles cut per parameter over its W*E_s contiguous destination elements (every param-major
 // output); otherwise per (node-block, parameter, slot) segment (the list output's separate buffers).
@@ -190,6 +198,20 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
   gp->T = T;
   gp->es = es;
   if (T == 0) return MR_OK;
+  gp->rank_mask.assign(W <= MR_MAX_TABLE_W ? static_cast<size_t>(W) : 0, 0);
+  {
+    uint64_t O = 0;
+    for (int s = 0; s < P; ++s) {
+      const uint64_t E = splits[s];
+      for (int r = 0; E && r < W; ++r) {
+        const uint64_t dst_off = (O * W + static_cast<uint64_t>(r) * E) * es;
+        if (r < 16) gp->rm_mask |= static_cast<uint16_t>(1u << ((dst_off - (static_cast<uint64_t>(r) * T + O) * es) & 15u));
+        if (r < static_cast<int>(gp->rank_mask.size()))
+          gp->rank_mask[r] |= static_cast<uint16_t>(1u << ((dst_off - O * es) & 15u));
+      }
+      O += E;
+    }
+  }
   uint64_t base = 0;  // shard offset of the first parameter of a group
   for (int s0 = 0; s0 < P; s0 += mr::kMaxParams) {
     const int np = (P - s0) < mr::kMaxParams ? (P - s0) : mr::kMaxParams;
@@ -264,16 +286,18 @@ mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dty
   return MR_OK;
 }
 
-// Launch every group of a plan; `bind` fills in this call's pointers on a copy of the group's arguments.
+// Launch every group of a plan; `bind` fills in this call's pointers on a copy of the group's arguments;
+// `realign` selects the kernel build that handles out-of-phase pieces.
 template <typename Bind>
-mr_status gather_launch(const GatherPlan& gp, Bind bind, hipStream_t st) {
+mr_status gather_launch(const GatherPlan& gp, Bind bind, bool realign, hipStream_t st) {
   for (const mr::GatherArgs& g : gp.groups) {
     mr::GatherArgs a = g;
     bind(a);
     if (g_trace)
-      std::fprintf(stderr, "[mr] gather W=%u G=%u params=%u T=%llu tiles=%u span=%u src_table=%u dst_table=%u\n", a.W,
-                   a.G, a.P, static_cast<unsigned long long>(a.T), a.total_tiles, a.span, a.src_table, a.dst_table);
-    const hipError_t e = mr::launch_param_contig(a, st);
+      std::fprintf(stderr, "[mr] gather W=%u G=%u params=%u T=%llu tiles=%u span=%u realign=%d src_table=%u dst_table=%u\n",
+                   a.W, a.G, a.P, static_cast<unsigned long long>(a.T), a.total_tiles, a.span, realign ? 1 : 0,
+                   a.src_table, a.dst_table);
+    const hipError_t e = mr::launch_param_contig(a, realign, st);
     if (e != hipSuccess) return hip_fail(e);
   }
   return MR_OK;
@@ -387,36 +411,43 @@ mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_
                                     void* out, mr_stream stream) {
   if (W < 1 || W > 65535) return MR_ERR_INVALID_ARG;
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, G, splits, P, dtype, true, &gp);
+  // tiles span a parameter's W slots when there are several parameters; one parameter (a plain
+  // rank-major copy) measured faster with per-slot tiles
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);
   if (s != MR_OK || gp->T == 0) return s;
   if (!src || !out) return MR_ERR_INVALID_ARG;
   const uint64_t total_bytes = static_cast<uint64_t>(W) * gp->T * gp->es;
   if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
     return MR_ERR_ALIAS;
+  const bool realign =
+      needs_realign(gp->rm_mask, reinterpret_cast<uintptr_t>(src) - reinterpret_cast<uintptr_t>(out));
   return gather_launch(*gp, [&](mr::GatherArgs& a) {
     a.src = static_cast<const char*>(src);
     a.out = static_cast<char*>(out);
-  }, reinterpret_cast<hipStream_t>(stream));
+  }, realign, reinterpret_cast<hipStream_t>(stream));
 }
 
 mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int G, const uint64_t* splits, int P,
                                            mr_dtype dtype, void* out, mr_stream stream) {
   if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, G, splits, P, dtype, true, &gp);
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);
   if (s != MR_OK || gp->T == 0) return s;
   if (!shards || !out) return MR_ERR_INVALID_ARG;
   const uint64_t shard_bytes = gp->T * gp->es, out_bytes = static_cast<uint64_t>(W) * shard_bytes;
+  bool realign = false;
   for (int r = 0; r < W; ++r) {
     if (!shards[r]) return MR_ERR_INVALID_ARG;
     if (overlap(reinterpret_cast<uintptr_t>(shards[r]), shard_bytes, reinterpret_cast<uintptr_t>(out), out_bytes))
       return MR_ERR_ALIAS;
+    realign = realign || needs_realign(gp->rank_mask[r], reinterpret_cast<uintptr_t>(shards[r]) -
+                                                             reinterpret_cast<uintptr_t>(out));
   }
   return gather_launch(*gp, [&](mr::GatherArgs& a) {
     a.src_table = 1;
     for (int r = 0; r < W; ++r) a.src_tab[r] = static_cast<const char*>(shards[r]);
     a.out = static_cast<char*>(out);
-  }, reinterpret_cast<hipStream_t>(stream));
+  }, realign, reinterpret_cast<hipStream_t>(stream));
 }
 
 mr_status mr_allgather_into_tensor(const void* const* shards, int W, size_t T, mr_dtype dtype, void* out,
@@ -435,8 +466,10 @@ mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype
   if (s != MR_OK || gp->T == 0) return s;
   if (!shards || !outs) return MR_ERR_INVALID_ARG;
   const uint64_t bytes = gp->T * gp->es;
+  bool realign = false;
   for (int i = 0; i < W; ++i) {
     if (!shards[i] || !outs[i]) return MR_ERR_INVALID_ARG;
+    realign = realign || ((reinterpret_cast<uintptr_t>(shards[i]) - reinterpret_cast<uintptr_t>(outs[i])) & 15u) != 0;
     for (int j = 0; j < W; ++j) {
       const uintptr_t oi = reinterpret_cast<uintptr_t>(outs[i]);
       if (overlap(oi, bytes, reinterpret_cast<uintptr_t>(shards[j]), bytes)) return MR_ERR_ALIAS;
@@ -450,7 +483,7 @@ mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype
       a.src_tab[r] = static_cast<const char*>(shards[r]);
       a.dst_tab[r] = static_cast<char*>(outs[r]);
     }
-  }, reinterpret_cast<hipStream_t>(stream));
+  }, realign, reinterpret_cast<hipStream_t>(stream));
 }
 
 mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {

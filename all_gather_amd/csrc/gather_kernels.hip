@@ -12,8 +12,8 @@
 // one line (a partial line costs a full one: aligning them cut the scatter's time by about 4%).
 // 512-lane workgroups moving 16 KiB (two 16-byte words per lane) measured best among 256..1024 lanes
 // and 8..128 KiB tiles.  The copy is a bit copy with 64-bit offsets; 16-byte non-temporal loads and
-// stores when source and destination share the same 16-byte phase, else 4-byte (or 2-byte) words with
-// the whole tile's loads in flight before its stores.
+// stores when source and destination share the same 16-byte phase, else the same packs realigned in
+// registers from the two source packs each destination pack straddles.
 
 #include "mr_internal.h"
 
@@ -32,30 +32,46 @@ __device__ __forceinline__ void copy_elem(const char* src, char* dst, uint32_t o
   else *reinterpret_cast<uint32_t*>(dst + o) = *reinterpret_cast<const uint32_t*>(src + o);
 }
 
-// Copy `n` words of type Wd (src and dst both Wd-aligned), a whole tile's loads in flight before its
-// stores: the path for spans whose source and destination have different 16-byte phases.
-template <typename Wd>
-__device__ __forceinline__ void copy_words(const char* src, char* dst, uint32_t n) {
-  constexpr int U = kGatherTileBytes / (static_cast<int>(sizeof(Wd)) * kGB);  // words per lane per tile
-  const Wd* s = reinterpret_cast<const Wd*>(src);
-  Wd* d = reinterpret_cast<Wd*>(dst);
-  for (uint32_t w0 = 0; w0 < n; w0 += U * kGB) {
-    Wd v[U];
+// Output dword i of a destination-aligned pack whose source starts M bytes into the aligned pair
+// (A, B): bytes M+4i .. M+4i+3 of A:B.
+template <int M>
+__device__ __forceinline__ u32x4 realign(const u32x4& A, const u32x4& B) {
+  const uint32_t w[8] = {A[0], A[1], A[2], A[3], B[0], B[1], B[2], B[3]};
+  constexpr int Q = M / 4, R = M % 4;
+  u32x4 o;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+  for (int i = 0; i < 4; ++i) o[i] = R == 0 ? w[Q + i] : __builtin_amdgcn_alignbyte(w[Q + i + 1], w[Q + i], R);
+  return o;
+}
+
+// 16-byte stores to a 16-byte-aligned destination from a source M (1..15, even) bytes past a 16-byte
+// boundary: each lane loads the two aligned source packs its output straddles and realigns them in
+// registers.  Every loaded pack holds at least one byte of the span, so no access leaves the pages the
+// source occupies.
+template <int M>
+__device__ __forceinline__ void copy_realigned(const u32x4* sa, u32x4* d4, uint32_t nw) {
+  for (uint32_t w0 = 0; w0 < nw; w0 += kCopyU * kGB) {
+    u32x4 a[kCopyU], b[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
       const uint32_t i = w0 + u * kGB + threadIdx.x;
-      if (i < n) v[u] = __builtin_nontemporal_load(s + i);
+      if (i < nw) {
+        a[u] = __builtin_nontemporal_load(sa + i);
+        b[u] = sa[i + 1];  // the next lane's pack: usually still in cache
+      }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kCopyU; ++u) {
       const uint32_t i = w0 + u * kGB + threadIdx.x;
-      if (i < n) __builtin_nontemporal_store(v[u], d + i);
+      if (i < nw) __builtin_nontemporal_store(realign<M>(a[u], b[u]), d4 + i);
     }
   }
 }
 
-// Copy `len` (<= one tile) bytes of whole elements.
-template <int S>
+// RA: the launch may hold spans whose source and destination 16-byte phases differ.  The kernel is
+// built twice because the realigning path, compiled in, slows the aligned one it never runs (same-GPU
+// A/B, config 4 bf16: 143 -> 146-149 us); the host picks the lean build whenever every span is in phase.
+template <int S, bool RA>
 __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t len) {
   const uintptr_t ps = reinterpret_cast<uintptr_t>(src), pd = reinterpret_cast<uintptr_t>(dst);
   if (((ps ^ pd) & 15u) == 0) {
@@ -82,28 +98,41 @@ __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t l
     const uint32_t tail0 = head + body;
     const uint32_t edge = head + (len - tail0);
     for (uint32_t b = threadIdx.x * S; b < edge; b += kGB * S) copy_elem<S>(src, dst, b < head ? b : tail0 + (b - head));
-  } else if (((ps ^ pd) & 3u) == 0) {
-    // different 16-byte phases, same 4-byte phase (split sizes that are not a multiple of the pack):
-    // a 2-byte element up to 4-byte alignment, 4-byte words, a 2-byte element at the end
-    const uint32_t head = (S == 2 && (ps & 2u) && len >= 2) ? 2u : 0u;
-    if (head && threadIdx.x == 0) copy_elem<2>(src, dst, 0);
-    const uint32_t nw = (len - head) >> 2;
-    copy_words<uint32_t>(src + head, dst + head, nw);
-    const uint32_t tail0 = head + (nw << 2);
-    if (tail0 < len && threadIdx.x == 0) copy_elem<2>(src, dst, tail0);
+  } else if (!RA) {
+    // not reached: the host launches this build only when every span is in phase
+    for (uint32_t b = threadIdx.x * S; b < len; b += kGB * S) copy_elem<S>(src, dst, b);
   } else {
-    // 2-byte elements whose 4-byte phases differ: 2-byte words
-    copy_words<uint16_t>(src, dst, len >> 1);
+    // different 16-byte phases (split sizes that are not a multiple of 16 bytes): elements up to the
+    // destination's 16-byte boundary, realigned 16-byte packs, elements at the end
+    uint32_t head = static_cast<uint32_t>((16u - (pd & 15u)) & 15u);
+    if (head > len) head = len;
+    const uint32_t nw = (len - head) >> 4;
+    const uint32_t m = static_cast<uint32_t>((ps + head) & 15u);  // source offset past its boundary
+    const u32x4* sa = reinterpret_cast<const u32x4*>(src + head - m);
+    u32x4* d4 = reinterpret_cast<u32x4*>(dst + head);
+    switch (m) {  // uniform per tile: one compile-time realignment per source offset
+      case 2: copy_realigned<2>(sa, d4, nw); break;
+      case 4: copy_realigned<4>(sa, d4, nw); break;
+      case 6: copy_realigned<6>(sa, d4, nw); break;
+      case 8: copy_realigned<8>(sa, d4, nw); break;
+      case 10: copy_realigned<10>(sa, d4, nw); break;
+      case 12: copy_realigned<12>(sa, d4, nw); break;
+      default: copy_realigned<14>(sa, d4, nw); break;
+    }
+    const uint32_t tail0 = head + (nw << 4);
+    const uint32_t edge = head + (len - tail0);
+    for (uint32_t b = threadIdx.x * S; b < edge; b += kGB * S) copy_elem<S>(src, dst, b < head ? b : tail0 + (b - head));
   }
 }
 
 // Param-major destination: the W slots of parameter s are contiguous in out (W*E_s elements from
 // O_s*W), so tiles are cut per parameter over that whole block and a tile crossing a rank boundary
-// switches source row mid-tile.  Same-GPU A/B against tiles cut per (node-block, parameter, slot)
-// segment, three interleaved repeats: config 4 (W=8, G=4, P=64 log-uniform) bf16 158 -> 154 us, fp32
-// 304 -> 298 us, from separate shards bf16 153 -> 150 us; equal fp32 splits at the same size, P=32
-// 300 -> 293 us, P=128 315 -> 303 us (W*P partial tiles become P).
-template <int S>
+// switches source row mid-tile (W*P partial tiles become P).  Same-GPU A/B of lean builds against
+// tiles cut per (node-block, parameter, slot) segment, three interleaved repeats: config 4 (W=8, G=4,
+// P=64 log-uniform) bf16 143.1-144.2 -> 142.1-142.7 us, fp32 282.7-283.6 -> 279.5-281.0 us, from
+// separate shards bf16 141.9-142.2 -> 140.1-140.4 us; but one parameter (a rank-major copy) fp32
+// 271-272.5 -> 277.6-278.8 us, so the host uses these tiles only when P > 1.
+template <int S, bool RA>
 __device__ __forceinline__ void param_block_tile(const GatherArgs& a, uint32_t t) {
   uint32_t lo = 0, hi = a.P;  // parameter s with tile_prefix[s] <= t < tile_prefix[s+1]
   while (hi - lo > 1) {
@@ -126,15 +155,15 @@ __device__ __forceinline__ void param_block_tile(const GatherArgs& a, uint32_t t
     const uint64_t r = x / ES;
     const uint64_t xe = (r + 1) * ES < b1 ? (r + 1) * ES : b1;
     const char* sp = a.src_table ? a.src_tab[r] + Os * S : a.src + (r * a.T + Os) * S;
-    copy_span<S>(sp + (x - r * ES), pd + x, static_cast<uint32_t>(xe - x));
+    copy_span<S, RA>(sp + (x - r * ES), pd + x, static_cast<uint32_t>(xe - x));
     x = xe;
   }
 }
 
-template <int S>
+template <int S, bool RA>
 __global__ __launch_bounds__(kGB) void param_contig(GatherArgs a) {
   if (a.span) {
-    for (uint32_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) param_block_tile<S>(a, t);
+    for (uint32_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) param_block_tile<S, RA>(a, t);
     return;
   }
   for (uint32_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
@@ -169,20 +198,24 @@ __global__ __launch_bounds__(kGB) void param_contig(GatherArgs a) {
     const uint64_t b0 = b0r > lead ? b0r - lead : 0;
     const uint64_t b1r = b0r + kGatherTileBytes - lead;
     const uint64_t b1 = b1r < seg ? b1r : seg;
-    if (b0 < b1) copy_span<S>(sp + b0, dp + b0, static_cast<uint32_t>(b1 - b0));
+    if (b0 < b1) copy_span<S, RA>(sp + b0, dp + b0, static_cast<uint32_t>(b1 - b0));
   }
 }
 
 }  // namespace
 
-hipError_t launch_param_contig(const GatherArgs& a, hipStream_t st) {
+hipError_t launch_param_contig(const GatherArgs& a, bool realign, hipStream_t st) {
   if (a.total_tiles == 0) return hipSuccess;
   const uint32_t kMaxGrid = 1u << 20;
   const uint32_t grid = a.total_tiles < kMaxGrid ? a.total_tiles : kMaxGrid;
-  if (a.elem == 2)
-    hipLaunchKernelGGL(param_contig<2>, dim3(grid), dim3(kGB), 0, st, a);
+  if (a.elem == 2 && realign)
+    hipLaunchKernelGGL((param_contig<2, true>), dim3(grid), dim3(kGB), 0, st, a);
+  else if (a.elem == 2)
+    hipLaunchKernelGGL((param_contig<2, false>), dim3(grid), dim3(kGB), 0, st, a);
+  else if (realign)
+    hipLaunchKernelGGL((param_contig<4, true>), dim3(grid), dim3(kGB), 0, st, a);
   else
-    hipLaunchKernelGGL(param_contig<4>, dim3(grid), dim3(kGB), 0, st, a);
+    hipLaunchKernelGGL((param_contig<4, false>), dim3(grid), dim3(kGB), 0, st, a);
   return hipGetLastError();
 }
 

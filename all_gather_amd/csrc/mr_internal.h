@@ -150,7 +150,8 @@ struct GatherArgs {
   uint32_t total_tiles;                  // span: tile_prefix[P]; else W/G node-blocks * tiles_per_block
 };
 
-hipError_t launch_param_contig(const GatherArgs& a, hipStream_t st);
+// realign: some span's source and destination differ in 16-byte phase (selects the kernel build)
+hipError_t launch_param_contig(const GatherArgs& a, bool realign, hipStream_t st);
 uint64_t gather_tiles_per_segment(uint64_t E, uint32_t elem);
 
 }  // namespace mr
