@@ -112,31 +112,49 @@ def _dev_tensor(t, what: str):
         raise ValueError(f"{what} must be a contiguous device tensor")
 
 
+def _splits_array(splits: Sequence[int]):
+    sp = [int(x) for x in splits]
+    if not sp or min(sp) < 0:
+        raise ValueError("splits must be a non-empty list of non-negative element counts")
+    return (ctypes.c_uint64 * len(sp))(*sp), sum(sp)
+
+
+def _same(tensors, ref, what: str, numel: int) -> None:
+    """Every tensor is a contiguous device tensor of ref's dtype holding exactly ``numel`` elements."""
+    for t in tensors:
+        _dev_tensor(t, what)
+        if t.dtype != ref.dtype or t.numel() != numel:
+            raise ValueError(f"{what} must hold {numel} elements of {ref.dtype}")
+
+
+def _prepared(name: str, f, args, keep):
+    def call() -> None:
+        st = f(*args)
+        if st != MR_OK:
+            raise MRError(st, name)
+
+    call.keepalive = keep
+    return call
+
+
+# Each prepare_* checks that every tensor is a contiguous device tensor of the sizes the call implies
+# (the library takes raw pointers and cannot check extents) and marshals the arguments once; the
+# returned no-argument callable enqueues that same call (tight timing loops, graph capture).  The
+# plain functions are one prepared call.
+
+def prepare_allreduce(bufs: Sequence, out, mode: str = "oneshot", stream=None):
+    """Pre-marshalled mr_allreduce_sum: out = elementwise fp32 sum (rank order) of the tensors ``bufs``."""
+    _dev_tensor(out, "out")
+    _same(bufs, out, "rank buffer", out.numel())
+    ptrs = (ctypes.c_void_p * max(len(bufs), 1))(*[b.data_ptr() for b in bufs])
+    args = (ptrs, len(bufs), out.numel(), DTYPE_CODE[dtype_name(out)], out.data_ptr(), MODE_CODE[mode],
+            _stream_handle(stream))
+    return _prepared("mr_allreduce_sum", lib().mr_allreduce_sum, args, (ptrs, list(bufs), out))
+
+
 def allreduce_sum(bufs: Sequence, out, mode: str = "oneshot", stream=None):
     """out = elementwise fp32 sum (rank order 0..W-1) of the W same-shape, same-dtype tensors ``bufs``."""
-    W = len(bufs)
-    for b in bufs:
-        _dev_tensor(b, "rank buffer")
-        if b.dtype != out.dtype or b.numel() != out.numel():
-            raise ValueError("rank buffers and out must share dtype and element count")
-    _dev_tensor(out, "out")
-    ptrs = (ctypes.c_void_p * max(W, 1))(*[b.data_ptr() for b in bufs])
-    st = lib().mr_allreduce_sum(ptrs, W, out.numel(), DTYPE_CODE[dtype_name(out)], out.data_ptr(),
-                                MODE_CODE[mode], _stream_handle(stream))
-    _check(st, "mr_allreduce_sum")
-    return out
-
-
-def allgather_param_contig(src, W: int, G: int, splits: Sequence[int], out, stream=None):
-    """Scatter the rank-major ``src`` ([W][T], T = sum(splits)) into [param][rank] order in ``out``."""
-    _dev_tensor(src, "src")
-    _dev_tensor(out, "out")
-    if src.dtype != out.dtype or src.numel() != out.numel():
-        raise ValueError("src and out must share dtype and element count")
-    sp = (ctypes.c_uint64 * max(len(splits), 1))(*[int(x) for x in splits])
-    st = lib().mr_allgather_param_contig(src.data_ptr(), W, G, sp, len(splits), DTYPE_CODE[dtype_name(src)],
-                                         out.data_ptr(), _stream_handle(stream))
-    _check(st, "mr_allgather_param_contig")
+    prepare_allreduce(bufs, out, mode, stream)()
     return out
 
 
@@ -148,41 +166,77 @@ def reduce_scatter_chunk(n: int, W: int, dtype: str, rank: int) -> tuple[int, in
     return int(off.value), int(cnt.value)
 
 
-def reduce_scatter_sum(bufs: Sequence, rank: int, out, stream=None):
-    """out = rank ``rank``'s chunk of the elementwise sum of the W same-shape tensors ``bufs``."""
-    W = len(bufs)
-    for b in bufs:
-        _dev_tensor(b, "rank buffer")
-        if b.dtype != out.dtype or b.numel() != bufs[0].numel():
-            raise ValueError("rank buffers must share dtype and element count with each other and out")
+def prepare_reduce_scatter(bufs: Sequence, rank: int, out, stream=None):
+    """Pre-marshalled mr_reduce_scatter_sum: out = rank ``rank``'s chunk of the sum of ``bufs``."""
     _dev_tensor(out, "out")
-    n = bufs[0].numel() if W else 0
-    _, cnt = reduce_scatter_chunk(n, W, dtype_name(out), rank)
+    n = bufs[0].numel() if len(bufs) else 0
+    _same(bufs, out, "rank buffer", n)
+    _, cnt = reduce_scatter_chunk(n, len(bufs), dtype_name(out), rank)
     if out.numel() != cnt:
         raise ValueError(f"out must hold the chunk's {cnt} elements")
-    ptrs = (ctypes.c_void_p * max(W, 1))(*[b.data_ptr() for b in bufs])
-    _check(lib().mr_reduce_scatter_sum(ptrs, W, n, DTYPE_CODE[dtype_name(out)], rank, out.data_ptr(),
-                                       _stream_handle(stream)), "mr_reduce_scatter_sum")
+    ptrs = (ctypes.c_void_p * max(len(bufs), 1))(*[b.data_ptr() for b in bufs])
+    args = (ptrs, len(bufs), n, DTYPE_CODE[dtype_name(out)], rank, out.data_ptr(), _stream_handle(stream))
+    return _prepared("mr_reduce_scatter_sum", lib().mr_reduce_scatter_sum, args, (ptrs, list(bufs), out))
+
+
+def reduce_scatter_sum(bufs: Sequence, rank: int, out, stream=None):
+    """out = rank ``rank``'s chunk of the elementwise sum of the W same-shape tensors ``bufs``."""
+    prepare_reduce_scatter(bufs, rank, out, stream)()
+    return out
+
+
+def prepare_allgather_param_contig(src, W: int, G: int, splits: Sequence[int], out, stream=None):
+    """Pre-marshalled mr_allgather_param_contig (src rank-major [W][T], T = sum(splits))."""
+    _dev_tensor(src, "src")
+    sp, T = _splits_array(splits)
+    if W < 1 or src.numel() != W * T:
+        raise ValueError(f"src must hold W*sum(splits) = {max(W, 0) * T} elements")
+    _same([out], src, "out", src.numel())
+    args = (src.data_ptr(), W, G, sp, len(sp), DTYPE_CODE[dtype_name(src)], out.data_ptr(), _stream_handle(stream))
+    return _prepared("mr_allgather_param_contig", lib().mr_allgather_param_contig, args, (sp, src, out))
+
+
+def allgather_param_contig(src, W: int, G: int, splits: Sequence[int], out, stream=None):
+    """Scatter the rank-major ``src`` ([W][T], T = sum(splits)) into [param][rank] order in ``out``."""
+    prepare_allgather_param_contig(src, W, G, splits, out, stream)()
     return out
 
 
 def _shard_ptrs(shards):
-    for t in shards:
-        _dev_tensor(t, "shard")
-        if t.dtype != shards[0].dtype or t.numel() != shards[0].numel():
-            raise ValueError("shards must share dtype and element count")
-    return (ctypes.c_void_p * max(len(shards), 1))(*[t.data_ptr() for t in shards])
+    if not len(shards):
+        raise ValueError("at least one shard")
+    _same(shards, shards[0], "shard", shards[0].numel())
+    return (ctypes.c_void_p * len(shards))(*[t.data_ptr() for t in shards])
+
+
+def prepare_allgather_shards(shards: Sequence, out, G: int | None = None, splits: Sequence[int] | None = None,
+                             stream=None):
+    """Pre-marshalled gather from W shards: rank-major into ``out`` (``splits`` None, mr_allgather_into_tensor)
+    or param-contiguous (mr_allgather_param_contig_shards, each shard sum(splits) elements)."""
+    ptrs = _shard_ptrs(shards)
+    W, T = len(shards), shards[0].numel()
+    _same([out], shards[0], "out", W * T)
+    dt = DTYPE_CODE[dtype_name(out)]
+    if splits is None:
+        name, args = "mr_allgather_into_tensor", (ptrs, W, T, dt, out.data_ptr(), _stream_handle(stream))
+    else:
+        sp, ST = _splits_array(splits)
+        if ST != T:
+            raise ValueError(f"each shard must hold sum(splits) = {ST} elements")
+        name = "mr_allgather_param_contig_shards"
+        args = (ptrs, W, W if G is None else G, sp, len(sp), dt, out.data_ptr(), _stream_handle(stream))
+    return _prepared(name, getattr(lib(), name), args, (args, list(shards), out))
 
 
 def allgather_into_tensor(shards: Sequence, out, stream=None):
     """out[r*T:(r+1)*T] = shards[r] (rank-major all-gather of W shards of T elements)."""
-    ptrs = _shard_ptrs(shards)
-    _dev_tensor(out, "out")
-    T = shards[0].numel()
-    if out.dtype != shards[0].dtype or out.numel() != len(shards) * T:
-        raise ValueError("out must hold W*T elements of the shards' dtype")
-    _check(lib().mr_allgather_into_tensor(ptrs, len(shards), T, DTYPE_CODE[dtype_name(out)], out.data_ptr(),
-                                          _stream_handle(stream)), "mr_allgather_into_tensor")
+    prepare_allgather_shards(shards, out, stream=stream)()
+    return out
+
+
+def allgather_param_contig_shards(shards: Sequence, G: int, splits: Sequence[int], out, stream=None):
+    """[param][rank] all-gather written straight from W shards (each sum(splits) elements)."""
+    prepare_allgather_shards(shards, out, G, splits, stream)()
     return out
 
 
@@ -191,27 +245,11 @@ def allgather_list(shards: Sequence, outs: Sequence, stream=None):
     ptrs = _shard_ptrs(shards)
     if len(outs) != len(shards):
         raise ValueError("one output per shard")
-    for o in outs:
-        _dev_tensor(o, "output")
-        if o.dtype != shards[0].dtype or o.numel() != shards[0].numel():
-            raise ValueError("outputs must match the shards")
-    optrs = (ctypes.c_void_p * max(len(outs), 1))(*[o.data_ptr() for o in outs])
+    _same(outs, shards[0], "output", shards[0].numel())
+    optrs = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
     _check(lib().mr_allgather_list(ptrs, len(shards), shards[0].numel(), DTYPE_CODE[dtype_name(shards[0])], optrs,
                                    _stream_handle(stream)), "mr_allgather_list")
     return outs
-
-
-def allgather_param_contig_shards(shards: Sequence, G: int, splits: Sequence[int], out, stream=None):
-    """[param][rank] all-gather written straight from W shards (each sum(splits) elements)."""
-    ptrs = _shard_ptrs(shards)
-    _dev_tensor(out, "out")
-    if out.dtype != shards[0].dtype or out.numel() != len(shards) * shards[0].numel():
-        raise ValueError("out must hold W*T elements of the shards' dtype")
-    sp = (ctypes.c_uint64 * max(len(splits), 1))(*[int(x) for x in splits])
-    _check(lib().mr_allgather_param_contig_shards(ptrs, len(shards), G, sp, len(splits),
-                                                  DTYPE_CODE[dtype_name(out)], out.data_ptr(),
-                                                  _stream_handle(stream)), "mr_allgather_param_contig_shards")
-    return out
 
 
 def workspace_bytes(W: int, n: int, dtype: str) -> int:
@@ -249,80 +287,3 @@ def get_option(name: str):
     if name == "tile_shape":
         return {c: k for k, c in TILE_SHAPE.items()}[v.value]
     return int(v.value)
-
-
-def prepare_allreduce(bufs: Sequence, out, mode: str = "oneshot", stream=None):
-    """Marshal the arguments of one mr_allreduce_sum call once; returns a no-argument callable that
-    enqueues that same call (for tight timing loops, where per-call marshalling would dominate)."""
-    W = len(bufs)
-    for b in bufs:
-        _dev_tensor(b, "rank buffer")
-    _dev_tensor(out, "out")
-    ptrs = (ctypes.c_void_p * max(W, 1))(*[b.data_ptr() for b in bufs])
-    f = lib().mr_allreduce_sum
-    args = (ptrs, W, out.numel(), DTYPE_CODE[dtype_name(out)], out.data_ptr(), MODE_CODE[mode],
-            _stream_handle(stream))
-
-    def call() -> None:
-        st = f(*args)
-        if st != MR_OK:
-            raise MRError(st, "mr_allreduce_sum")
-
-    call.keepalive = (ptrs, list(bufs), out)
-    return call
-
-
-def prepare_reduce_scatter(bufs: Sequence, rank: int, out, stream=None):
-    """Pre-marshalled mr_reduce_scatter_sum call (see prepare_allreduce)."""
-    W = len(bufs)
-    ptrs = (ctypes.c_void_p * max(W, 1))(*[b.data_ptr() for b in bufs])
-    f = lib().mr_reduce_scatter_sum
-    args = (ptrs, W, bufs[0].numel(), DTYPE_CODE[dtype_name(out)], rank, out.data_ptr(), _stream_handle(stream))
-
-    def call() -> None:
-        st = f(*args)
-        if st != MR_OK:
-            raise MRError(st, "mr_reduce_scatter_sum")
-
-    call.keepalive = (ptrs, list(bufs), out)
-    return call
-
-
-def prepare_allgather_shards(shards: Sequence, out, G: int | None = None, splits: Sequence[int] | None = None,
-                             stream=None):
-    """Pre-marshalled shard-list gather: rank-major (``splits`` None) or param-contiguous."""
-    ptrs = _shard_ptrs(shards)
-    W, T = len(shards), shards[0].numel()
-    dt = DTYPE_CODE[dtype_name(out)]
-    if splits is None:
-        f, args = lib().mr_allgather_into_tensor, (ptrs, W, T, dt, out.data_ptr(), _stream_handle(stream))
-    else:
-        sp = (ctypes.c_uint64 * max(len(splits), 1))(*[int(x) for x in splits])
-        f = lib().mr_allgather_param_contig_shards
-        args = (ptrs, W, G, sp, len(splits), dt, out.data_ptr(), _stream_handle(stream))
-
-    def call() -> None:
-        st = f(*args)
-        if st != MR_OK:
-            raise MRError(st, "shard gather")
-
-    call.keepalive = (args, list(shards), out)
-    return call
-
-
-def prepare_allgather_param_contig(src, W: int, G: int, splits: Sequence[int], out, stream=None):
-    """Pre-marshalled mr_allgather_param_contig call (see prepare_allreduce)."""
-    _dev_tensor(src, "src")
-    _dev_tensor(out, "out")
-    sp = (ctypes.c_uint64 * max(len(splits), 1))(*[int(x) for x in splits])
-    f = lib().mr_allgather_param_contig
-    args = (src.data_ptr(), W, G, sp, len(splits), DTYPE_CODE[dtype_name(src)], out.data_ptr(),
-            _stream_handle(stream))
-
-    def call() -> None:
-        st = f(*args)
-        if st != MR_OK:
-            raise MRError(st, "mr_allgather_param_contig")
-
-    call.keepalive = (sp, src, out)
-    return call

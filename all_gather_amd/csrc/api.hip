@@ -158,7 +158,7 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
     char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (sh.vec ? (po & 15u) : 0);
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws.base + mr::kCtrlBytes);
     if (g_trace)
-      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu tile=%zu t1=%u t2=%u\n",
+      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu tile=%u t1=%u t2=%u\n",
                    W, n, static_cast<int>(dtype), sh.vec, pl.sync, pl.chunk_units, pl.unit1, pl.t1, pl.t2);
     e = mr::launch_twoshot(in, W, dtype, out, stage, reinterpret_cast<mr::Ctrl*>(ws.base), flags, sh, pl, st);
   }
@@ -195,10 +195,13 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
     T += splits[s];
   }
   if (T > (1ull << 56) / (static_cast<uint64_t>(W) * es)) return MR_ERR_INVALID_ARG;
+  // gp may be a reused cache slot: reset every field (vectors keep their capacity)
   gp->T = T;
   gp->es = es;
-  if (T == 0) return MR_OK;
+  gp->rm_mask = 0;
+  gp->groups.clear();
   gp->rank_mask.assign(W <= MR_MAX_TABLE_W ? static_cast<size_t>(W) : 0, 0);
+  if (T == 0) return MR_OK;
   {
     uint64_t O = 0;
     for (int s = 0; s < P; ++s) {
@@ -272,7 +275,6 @@ mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dty
   CachedPlan& c = t_plans[t_plan_next];
   t_plan_next = (t_plan_next + 1) % kPlanSlots;
   c.used = false;
-  c.plan.groups.clear();
   const mr_status s = gather_plan(W, G, splits, P, dtype, span, &c.plan);
   if (s != MR_OK) return s;
   c.span = span;

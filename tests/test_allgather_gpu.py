@@ -158,3 +158,39 @@ def test_equal_splits_with_unaligned_sizes(dtype, E):
     mr.allgather_param_contig(to_dev(src, dtype), W, G, splits, out)
     torch.cuda.synchronize()
     assert np.array_equal(to_bits(out), oracle.allgather_param_contig_ref(src, W, G, splits))
+
+
+_SLOT_REUSE_CHILD = r"""
+import torch
+import all_gather_amd as mr
+W, G = 8, 4
+def run(splits):
+    T = sum(splits)
+    src = torch.arange(W * T, dtype=torch.int32, device="cuda:0").to(torch.int16).view(torch.bfloat16)
+    out = torch.empty_like(src)
+    mr.allgather_param_contig(src, W, G, splits, out)
+    torch.cuda.synchronize()
+run([3, 5])                        # odd sizes: pieces out of 16-byte phase (realign build)
+for k in range(7):
+    run([8 * (k + 2), 16])         # fill the other cached-plan slots with aligned plans
+run([64, 128])                     # aligned, and lands in the first plan's slot
+"""
+
+
+def test_reused_plan_slot_keeps_no_stale_phase_bits():
+    """A plan computed into a reused cache slot must not inherit the previous plan's phase bits, which
+    would send an all-aligned gather to the slower realign build.  The launch trace names the build."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, MR_TRACE="1", PYTHONPATH=root)
+    print("[case] plan slot reuse (child process, MR_TRACE=1)", flush=True)
+    r = subprocess.run([sys.executable, "-c", _SLOT_REUSE_CHILD], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[mr] gather")]
+    assert len(lines) == 9, r.stderr[-2000:]
+    assert "realign=1" in lines[0]
+    assert all("realign=0" in ln for ln in lines[1:]), lines

@@ -108,3 +108,47 @@ def test_empty_inputs_are_no_ops():
     torch.cuda.synchronize()
     assert np.array_equal(to_bits(out), oracle.allreduce_sum_ref(bufs, "bf16"))
     assert mr.workspace_check() == 0
+
+
+def test_binding_rejects_mismatched_extents():
+    """The library takes raw pointers and cannot see extents, so the binding refuses tensors whose sizes,
+    dtypes or layout disagree with the call, before anything is enqueued."""
+    d, bf = device(), torch.bfloat16
+    W = 4
+    sentinel = torch.full((64,), 7, dtype=torch.int32, device=d)
+    bufs = [torch.zeros(100, dtype=bf, device=d) for _ in range(W)]
+    out = torch.zeros(100, dtype=bf, device=d)
+    short = torch.zeros(99, dtype=bf, device=d)
+    strided = torch.zeros(200, dtype=bf, device=d)[::2]
+    bad_calls = {
+        "allreduce short rank buffer": lambda: mr.prepare_allreduce(bufs[:-1] + [short], out),
+        "allreduce short out": lambda: mr.allreduce_sum(bufs, short),
+        "allreduce dtype": lambda: mr.allreduce_sum(bufs, out.float()),
+        "allreduce strided": lambda: mr.allreduce_sum(bufs[:-1] + [strided], out),
+        "reduce-scatter out size": lambda: mr.prepare_reduce_scatter(bufs, 0, short),
+        "reduce-scatter short rank buffer": lambda: mr.reduce_scatter_sum(bufs[:-1] + [short], 0, out[:32]),
+    }
+    src = torch.zeros(W * 10, dtype=bf, device=d)
+    shards = [torch.zeros(10, dtype=bf, device=d) for _ in range(W)]
+    full = torch.empty(W * 10, dtype=bf, device=d)
+    bad_calls.update({
+        "param-contig splits != T": lambda: mr.prepare_allgather_param_contig(src, W, 2, [4, 5], full),
+        "param-contig short out": lambda: mr.allgather_param_contig(src, W, 2, [4, 6], full[:-1]),
+        "param-contig negative split": lambda: mr.allgather_param_contig(src, W, 2, [-1, 11], full),
+        "param-contig no splits": lambda: mr.allgather_param_contig(src, W, 2, [], full),
+        "param-contig W=0": lambda: mr.allgather_param_contig(src, 0, 1, [10], full),
+        "shards splits != T": lambda: mr.allgather_param_contig_shards(shards, 2, [4, 5], full),
+        "shards short out": lambda: mr.prepare_allgather_shards(shards, full[:-1], 2, [4, 6]),
+        "into-tensor short out": lambda: mr.allgather_into_tensor(shards, full[:-1]),
+        "into-tensor short shard": lambda: mr.allgather_into_tensor(shards[:-1] + [shards[0][:9]], full),
+        "into-tensor no shards": lambda: mr.allgather_into_tensor([], full),
+        "list short output": lambda: mr.allgather_list(shards, [torch.empty(9, dtype=bf, device=d)] * W),
+        "list output count": lambda: mr.allgather_list(shards, [full[:10]] * (W - 1)),
+    })
+    for what, call in bad_calls.items():
+        print(f"[case] binding check: {what}", flush=True)
+        with pytest.raises(ValueError):
+            call()
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7).all())
+    assert bool((out == 0).all())
