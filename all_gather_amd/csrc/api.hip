@@ -45,6 +45,9 @@ bool overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
   return na && nb && a < b + nb && b < a + na;
 }
 
+// Every device pointer of a call must be a multiple of the element size.
+bool elem_aligned(const void* p, uint64_t es) { return reinterpret_cast<uintptr_t>(p) % es == 0; }
+
 // ------------------------------------------------------------------------------ workspace registry
 struct Workspace {
   char* base = nullptr;
@@ -121,7 +124,7 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
   const size_t nbytes = n * static_cast<size_t>(es);
   const uintptr_t po = reinterpret_cast<uintptr_t>(out);
   mr::RankPtrs in{};
-  bool same_phase = (po % static_cast<uintptr_t>(es)) == 0;
+  bool same_phase = true;
   for (int r = 0; r < W; ++r) {
     const uintptr_t pr = reinterpret_cast<uintptr_t>(ins[r]);
     if (pr != po && overlap(pr, nbytes, po, nbytes)) return MR_ERR_ALIAS;
@@ -371,9 +374,10 @@ mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dt
   if (!bufs || !out) return MR_ERR_INVALID_ARG;
   const int es = mr::elem_size(dtype);
   if (n > (SIZE_MAX / 2 - mr::kCtrlBytes) / static_cast<size_t>(es)) return MR_ERR_INVALID_ARG;
+  if (!elem_aligned(out, es)) return MR_ERR_INVALID_ARG;
   const char* ins[MR_MAX_W];
   for (int r = 0; r < W; ++r) {
-    if (!bufs[r]) return MR_ERR_INVALID_ARG;
+    if (!bufs[r] || !elem_aligned(bufs[r], es)) return MR_ERR_INVALID_ARG;
     ins[r] = static_cast<const char*>(bufs[r]);
   }
   return reduce_launch(ins, W, n, dtype, static_cast<char*>(out), mode, reinterpret_cast<hipStream_t>(stream));
@@ -401,9 +405,10 @@ mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dty
   if (cnt == 0) return MR_OK;
   if (!bufs || !out) return MR_ERR_INVALID_ARG;
   const size_t es = static_cast<size_t>(mr::elem_size(dtype));
+  if (!elem_aligned(out, es)) return MR_ERR_INVALID_ARG;
   const char* ins[MR_MAX_W];
   for (int r = 0; r < W; ++r) {
-    if (!bufs[r]) return MR_ERR_INVALID_ARG;
+    if (!bufs[r] || !elem_aligned(bufs[r], es)) return MR_ERR_INVALID_ARG;
     ins[r] = static_cast<const char*>(bufs[r]) + off * es;  // this rank's chunk of every rank buffer
   }
   return reduce_launch(ins, W, cnt, dtype, static_cast<char*>(out), MR_ONESHOT, reinterpret_cast<hipStream_t>(stream));
@@ -417,7 +422,7 @@ mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_
   // rank-major copy) measured faster with per-slot tiles
   mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);
   if (s != MR_OK || gp->T == 0) return s;
-  if (!src || !out) return MR_ERR_INVALID_ARG;
+  if (!src || !out || !elem_aligned(src, gp->es) || !elem_aligned(out, gp->es)) return MR_ERR_INVALID_ARG;
   const uint64_t total_bytes = static_cast<uint64_t>(W) * gp->T * gp->es;
   if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
     return MR_ERR_ALIAS;
@@ -435,11 +440,11 @@ mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int
   const GatherPlan* gp = nullptr;
   mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);
   if (s != MR_OK || gp->T == 0) return s;
-  if (!shards || !out) return MR_ERR_INVALID_ARG;
+  if (!shards || !out || !elem_aligned(out, gp->es)) return MR_ERR_INVALID_ARG;
   const uint64_t shard_bytes = gp->T * gp->es, out_bytes = static_cast<uint64_t>(W) * shard_bytes;
   bool realign = false;
   for (int r = 0; r < W; ++r) {
-    if (!shards[r]) return MR_ERR_INVALID_ARG;
+    if (!shards[r] || !elem_aligned(shards[r], gp->es)) return MR_ERR_INVALID_ARG;
     if (overlap(reinterpret_cast<uintptr_t>(shards[r]), shard_bytes, reinterpret_cast<uintptr_t>(out), out_bytes))
       return MR_ERR_ALIAS;
     realign = realign || needs_realign(gp->rank_mask[r], reinterpret_cast<uintptr_t>(shards[r]) -
@@ -470,7 +475,8 @@ mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype
   const uint64_t bytes = gp->T * gp->es;
   bool realign = false;
   for (int i = 0; i < W; ++i) {
-    if (!shards[i] || !outs[i]) return MR_ERR_INVALID_ARG;
+    if (!shards[i] || !outs[i] || !elem_aligned(shards[i], gp->es) || !elem_aligned(outs[i], gp->es))
+      return MR_ERR_INVALID_ARG;
     realign = realign || ((reinterpret_cast<uintptr_t>(shards[i]) - reinterpret_cast<uintptr_t>(outs[i])) & 15u) != 0;
     for (int j = 0; j < W; ++j) {
       const uintptr_t oi = reinterpret_cast<uintptr_t>(outs[i]);

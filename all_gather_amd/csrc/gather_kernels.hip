@@ -110,6 +110,7 @@ __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t l
     const uint32_t m = static_cast<uint32_t>((ps + head) & 15u);  // source offset past its boundary
     const u32x4* sa = reinterpret_cast<const u32x4*>(src + head - m);
     u32x4* d4 = reinterpret_cast<u32x4*>(dst + head);
+    // m is a nonzero multiple of the element size (the host refuses pointers that are not), so even
     switch (m) {  // uniform per tile: one compile-time realignment per source offset
       case 2: copy_realigned<2>(sa, d4, nw); break;
       case 4: copy_realigned<4>(sa, d4, nw); break;

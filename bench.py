@@ -458,7 +458,7 @@ def main():
                      "avg_launch_us": round(t_launch * 1e6, 3), "traffic_source": traffic_src,
                      "traffic_GBps": round(traffic / t_launch / 1e9, 1) if traffic else None,
                      "copy_ceiling_GBps": round(copy_gbs, 1),
-                     "copy_ceiling_kernel": "param_contig<4>: all_gather_into_tensor of one 256 MiB shard",
+                     "copy_ceiling_kernel": "param_contig<4, false>: all_gather_into_tensor of one 256 MiB shard",
                      "frac_of_copy_ceiling": round(gbs / copy_gbs, 4)},
         "cpu_baseline": cpu,
         "paths": paths,

@@ -32,7 +32,7 @@ typedef struct ihipStream_t* mr_stream; /* == hipStream_t */
 
 typedef int mr_status;
 #define MR_OK 0
-#define MR_ERR_INVALID_ARG (-1) /* null pointer, W/G/P out of range, size overflow */
+#define MR_ERR_INVALID_ARG (-1) /* null or misaligned pointer, W/G/P out of range, size overflow */
 #define MR_ERR_DTYPE (-2)       /* dtype not supported by this operation */
 #define MR_ERR_ALIAS (-3)       /* output partially overlaps an input */
 #define MR_ERR_WORKSPACE (-4)   /* two-shot workspace missing, too small, or barrier error seen */
@@ -65,8 +65,10 @@ int mr_last_hip_error(void);
  * in both modes.
  *
  *  bufs   host array of W device pointers, each to n contiguous elements of `dtype` (read only).
- *         Pointers may repeat.  Any alignment is accepted: when every pointer (and out) has the same
- *         address modulo 16 the kernels use 16-byte loads, otherwise a slower element-wise path.
+ *         Pointers may repeat.  Every pointer (and out) must be a multiple of the element size, else
+ *         MR_ERR_INVALID_ARG; beyond that any alignment is accepted: when every pointer and out have
+ *         the same address modulo 16 the kernels use 16-byte loads, otherwise a slower element-wise
+ *         path.
  *  W      1 .. MR_MAX_W.
  *  n      elements per buffer; n == 0 is a successful no-op.
  *  dtype  MR_BF16, MR_FP16 or MR_FP32 (output has the same dtype); MR_INT32 -> MR_ERR_DTYPE.
@@ -103,7 +105,8 @@ mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dt
  *          first is enqueued).
  *  dtype   any mr_dtype (element size 2 or 4 bytes).
  *  out     device pointer, W*T elements.  Any overlap with src -> MR_ERR_ALIAS.
- *  All offsets are 64-bit; buffers beyond 2^31 bytes are supported.
+ *  src and out must be multiples of the element size (else MR_ERR_INVALID_ARG); their 16-byte phases
+ *  are free.  All offsets are 64-bit; buffers beyond 2^31 bytes are supported.
  */
 mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, const uint64_t* splits,
                                     int P, mr_dtype dtype, void* out, mr_stream stream);
@@ -131,6 +134,7 @@ mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dty
 /*
  * All-gathers from W separate rank shards (each a device buffer of T elements), one launch each.
  * Bit copies of any dtype; 1 <= W <= MR_MAX_TABLE_W; shards may not overlap any output (MR_ERR_ALIAS).
+ * Every shard and output pointer must be a multiple of the element size (else MR_ERR_INVALID_ARG).
  *
  * mr_allgather_into_tensor:  rank-major gather (torch.distributed.all_gather_into_tensor's layout):
  *                            out[r*T + j] = shards[r][j]; out holds W*T elements.

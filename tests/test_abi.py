@@ -275,3 +275,23 @@ def test_shard_gather_argument_errors(L):
     assert L.mr_allgather_param_contig_shards(sh, 4, 2, sp, 0, 0, 0x9000000, None) == EINVAL  # no params
     assert L.mr_allgather_param_contig_shards(sh, 4, 2, sp, 2, 0, 0x400000 - 10, None) == EALIAS
     assert outs is not None
+
+
+def test_pointers_must_be_element_aligned(L):
+    """Every device pointer is a multiple of the element size; anything else is refused before launch."""
+    a, b, out = 0x100000, 0x200000, 0x900000
+    assert L.mr_allreduce_sum(_ptrs(a + 1, b), 2, 64, 0, out, 0, None) == EINVAL      # bf16 buffer at odd byte
+    assert L.mr_allreduce_sum(_ptrs(a, b), 2, 64, 0, out + 1, 1, None) == EINVAL      # bf16 out at odd byte
+    assert L.mr_allreduce_sum(_ptrs(a, b + 2), 2, 64, 2, out, 0, None) == EINVAL      # fp32 buffer 2 bytes in
+    assert L.mr_reduce_scatter_sum(_ptrs(a, b + 1), 2, 64, 1, 0, out, None) == EINVAL
+    assert L.mr_reduce_scatter_sum(_ptrs(a, b), 2, 64, 2, 1, out + 2, None) == EINVAL
+    sp = (ctypes.c_uint64 * 2)(8, 16)
+    assert L.mr_allgather_param_contig(a + 1, 4, 2, sp, 2, 0, out, None) == EINVAL
+    assert L.mr_allgather_param_contig(a, 4, 2, sp, 2, 3, out + 2, None) == EINVAL    # int32 out 2 bytes in
+    shards = _ptrs(a, b, a + 0x1000, b + 0x1000 + 1)
+    assert L.mr_allgather_param_contig_shards(shards, 4, 2, sp, 2, 0, out, None) == EINVAL
+    assert L.mr_allgather_into_tensor(shards, 4, 24, 0, out, None) == EINVAL
+    good = _ptrs(a, b, a + 0x1000, b + 0x1000)
+    assert L.mr_allgather_into_tensor(good, 4, 24, 1, out + 1, None) == EINVAL
+    outs = _ptrs(out, out + 0x1000, out + 0x2000, out + 0x3000 + 2)
+    assert L.mr_allgather_list(good, 4, 24, 2, outs, None) == EINVAL                   # fp32 output 2 bytes in
