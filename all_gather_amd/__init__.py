@@ -27,7 +27,7 @@ DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2, "int32": 3}
 MODE_CODE = {"oneshot": 0, "twoshot": 1}
 OPTION_CODE = {"twoshot_sync": 0, "spin_limit": 1, "tile_shape": 2}
 TWOSHOT_SYNC = {"tile": 0, "chunk": 1, "grid": 2, "last": 3, "auto": 4}
-TILE_SHAPE = {"auto": 0, "wide": 1, "medium": 2, "narrow": 3}
+TILE_SHAPE = {"auto": 0, "wide": 1, "medium": 2, "narrow": 3, "wide_pair": 4}
 MAX_W = 16
 MAX_PARAMS_PER_LAUNCH = 128
 MAX_TABLE_W = 64

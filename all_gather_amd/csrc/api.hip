@@ -30,7 +30,7 @@ uint32_t env_u32(const char* name, uint32_t dflt, unsigned long lo, unsigned lon
 // Process-wide options (mr_set_option); defaults may be overridden by the environment at load.
 std::atomic<uint32_t> g_spin_limit{env_u32("MR_SPIN_LIMIT", 1u << 22, 0, 0xffffffffUL)};
 std::atomic<uint32_t> g_twoshot_sync{env_u32("MR_TWOSHOT_SYNC", mr::kSyncAuto, MR_TWOSHOT_SYNC_TILE, MR_TWOSHOT_SYNC_AUTO)};
-std::atomic<uint32_t> g_tile_shape{env_u32("MR_TILE_SHAPE", mr::kShapeAuto, MR_TILE_AUTO, MR_TILE_NARROW)};
+std::atomic<uint32_t> g_tile_shape{env_u32("MR_TILE_SHAPE", mr::kShapeAuto, MR_TILE_AUTO, MR_TILE_WIDE_PAIR)};
 const bool g_trace = env_u32("MR_TRACE", 0, 0, 1) != 0;
 
 mr_status hip_fail(hipError_t e) {
@@ -326,7 +326,7 @@ const char* mr_status_string(mr_status s) {
 
 int mr_last_hip_error(void) { return g_last_hip_error; }
 
-int mr_version(void) { return 101; }
+int mr_version(void) { return 102; }
 
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
   if (W < 1 || W > MR_MAX_W || !is_float(dtype)) return 0;
@@ -346,7 +346,7 @@ mr_status mr_set_option(mr_option opt, int64_t value) {
       g_spin_limit.store(static_cast<uint32_t>(value));
       return MR_OK;
     case MR_OPT_TILE_SHAPE:
-      if (value < MR_TILE_AUTO || value > MR_TILE_NARROW) return MR_ERR_INVALID_ARG;
+      if (value < MR_TILE_AUTO || value > MR_TILE_WIDE_PAIR) return MR_ERR_INVALID_ARG;
       g_tile_shape.store(static_cast<uint32_t>(value));
       return MR_OK;
     default:

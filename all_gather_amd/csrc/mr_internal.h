@@ -47,15 +47,19 @@ enum TwoShotSync : uint32_t {
 
 // Tile shape of the reduce kernels (MR_OPT_TILE_SHAPE).  Wide tiles suit large messages; small ones
 // need narrower tiles so that the grid still holds enough workgroups to keep every CU busy.
-enum TileShape : uint32_t { kShapeAuto = 0, kShapeWide = 1, kShapeMedium = 2, kShapeNarrow = 3 };
+enum TileShape : uint32_t { kShapeAuto = 0, kShapeWide = 1, kShapeMedium = 2, kShapeNarrow = 3, kShapeWidePair = 4 };
 
 // Auto choices, from graph-replayed sweeps at W=8 over 64 KiB .. 64 MiB per rank (bf16 and fp32):
 // the narrow one-shot tile halves the time of messages below 1 MiB against the wide one (3.0 vs
 // 5.4 us at 64 KiB), the medium one leads from 1 to 2-4 MiB, and the wide one from 4 MiB (fp32) or
-// 8 MiB (bf16) up.  For two-shot, 256-pack tiles lead below 2 MiB and 1024-pack tiles above.
+// 8 MiB (bf16) up.  For two-shot, 256-pack tiles lead below 2 MiB and 1024-pack tiles above.  Wide
+// tiles in pairs (one workgroup, results held until both are reduced) lead from 16 to 64 MiB per rank:
+// 512 pairs fill two workgroup slots per CU at 16 MiB, where 1024 single tiles leave a tail on the
+// 768 slots the wide kernel's registers allow.
 inline uint32_t oneshot_shape(size_t npacks, int elem_size, uint32_t forced) {
   if (forced != kShapeAuto) return forced;
   const size_t wide_from = elem_size == 4 ? (size_t(1) << 18) : (size_t(1) << 19);
+  if (npacks >= (size_t(1) << 20) && npacks <= (size_t(1) << 22)) return kShapeWidePair;
   if (npacks >= wide_from) return kShapeWide;          // 256 lanes x 4 packs
   if (npacks >= (size_t(1) << 16)) return kShapeMedium;  // 256 lanes x 1 pack
   return kShapeNarrow;                                   // 64 lanes x 1 pack

@@ -268,6 +268,38 @@ __global__ __launch_bounds__(B) void oneshot_vec(RankPtrs in, char* out, ReduceS
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
 
+// Wide tiles in pairs: workgroup g reduces wide tiles 2g and 2g+1 (consecutive packs), holds the
+// first tile's results in registers while the second one's loads are in flight, then stores both.
+// Same-GPU A/B at W=8 against one wide tile per workgroup, graph-replayed, best of three, on two GPUs:
+// bf16 16 MiB per rank 26.69 -> 25.96 and 26.38 -> 25.87 us, 24 MiB 39.16 -> 38.36, 32 MiB 51.36 ->
+// 50.28, 48 MiB 77.26 -> 75.79, 64 MiB 102.6 -> 100.6; fp32 16 MiB 25.98 -> 25.49, 64 MiB 102.2 ->
+// 100.4.  It loses at 8 MiB (14.08 -> 14.92: 256 pairs leave half the slots empty) and from 128 MiB
+// (203.4 -> 207.1: 170 VGPRs allow two waves per SIMD against the wide kernel's three), so the host
+// picks it from 16 to 64 MiB per rank.
+template <typename D, int W, int B, int U>
+__global__ __launch_bounds__(B) void oneshot_pair(RankPtrs in, char* out, ReduceShape sh, size_t npairs, int xcd) {
+  const size_t hb = sh.head * D::kSize;
+  u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
+  for (size_t b = blockIdx.x; b < npairs; b += gridDim.x) {
+    const size_t g = xcd ? xcd_tile(b, npairs) : b;
+    u32x4 res[2][U];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      reduce_tile<D, W, B, U>(in, hb, (2 * g + h) * (B * U), sh.npacks,
+                              [&](int u, size_t, const u32x4& o) { res[h][u] = o; });
+      __asm__ volatile("" ::: "memory");  // compiler barrier between the two tiles (the measured build)
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t i = wc_pack<B, U>((2 * g + h) * (B * U), u);
+        if (i < sh.npacks) __builtin_nontemporal_store(res[h][u], dst + i);
+      }
+  }
+  if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
+}
+
 template <typename D, int W>
 __global__ __launch_bounds__(kBlock) void oneshot_elem(RankPtrs in, char* out, size_t n) {
   for (size_t e = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; e < n;
@@ -608,8 +640,23 @@ hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& 
 }
 
 template <typename D, int W>
+hipError_t oneshot_pair_launch(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
+  constexpr int B = kOneShotBlock, U = OneShotU<W>::value;
+  const size_t npairs = (sh.npacks + 2 * B * U - 1) / (2 * B * U);
+  size_t grid = npairs < kMaxGrid ? npairs : kMaxGrid;
+  if (grid == 0) grid = 1;  // edges only
+  const int xcd = grid == npairs && npairs <= 512 ? 1 : 0;  // XCD-contiguous order as for small wide grids
+  hipLaunchKernelGGL((oneshot_pair<D, W, B, U>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh,
+                     npairs, xcd);
+  return hipGetLastError();
+}
+
+template <typename D, int W>
 hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, uint32_t shape, hipStream_t st) {
   if (sh.vec) {
+    if constexpr (W <= 8) {
+      if (shape == kShapeWidePair) return oneshot_pair_launch<D, W>(in, out, sh, st);
+    }
     switch (shape) {
       case kShapeNarrow: return oneshot_vec_launch<D, W, 64, 1>(in, out, sh, st);
       case kShapeMedium: return oneshot_vec_launch<D, W, 256, 1>(in, out, sh, st);

@@ -201,12 +201,15 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  *                      that is not already satisfied give up at once (for testing error handling).
  * MR_OPT_TILE_SHAPE    tile shape of the sum-reduce kernels (results are identical for every shape):
  *   MR_TILE_AUTO   (default) chosen from the message size and dtype: narrow below 64 Ki packs
- *                  of 16 B, medium below 256 Ki (fp32) or 512 Ki (16-bit types) packs, wide above;
- *                  two-shot: 64-pack tiles below 8 Ki packs, 256 below 128 Ki, 1024 above;
+ *                  of 16 B, medium below 256 Ki (fp32) or 512 Ki (16-bit types) packs, wide pair
+ *                  from 1 Mi to 4 Mi packs (16 to 64 MiB per rank buffer) when W <= 8, wide
+ *                  otherwise; two-shot: 64-pack tiles below 8 Ki packs, 256 below 128 Ki, 1024 above;
  *   MR_TILE_WIDE   one-shot 256 lanes x 4 packs of 16 B (256 x 1 for W > 8), two-shot phase-1
  *                  tiles of 1024 packs;
  *   MR_TILE_MEDIUM one-shot 256 x 1, two-shot 256-pack tiles;
- *   MR_TILE_NARROW one-shot 64 x 1, two-shot 64-pack tiles.
+ *   MR_TILE_NARROW one-shot 64 x 1, two-shot 64-pack tiles;
+ *   MR_TILE_WIDE_PAIR  one-shot: each workgroup reduces two wide tiles and stores both after the
+ *                  second (W <= 8; wide for W > 8); two-shot as MR_TILE_WIDE.
  * Unknown options or out-of-range values -> MR_ERR_INVALID_ARG.  Environment variables
  * MR_TWOSHOT_SYNC, MR_SPIN_LIMIT and MR_TILE_SHAPE set the initial values when the library loads; a
  * value that is not a whole number in the option's range is ignored.  MR_TRACE=1 makes every launch
@@ -222,11 +225,12 @@ typedef enum mr_option { MR_OPT_TWOSHOT_SYNC = 0, MR_OPT_SPIN_LIMIT = 1, MR_OPT_
 #define MR_TILE_WIDE 1
 #define MR_TILE_MEDIUM 2
 #define MR_TILE_NARROW 3
+#define MR_TILE_WIDE_PAIR 4
 mr_status mr_set_option(mr_option opt, int64_t value);
 mr_status mr_get_option(mr_option opt, int64_t* value);
 
 /* Library ABI version (major*100 + minor).  1.01 added MR_OPT_TILE_SHAPE, MR_TWOSHOT_SYNC_LAST and
- * MR_TWOSHOT_SYNC_AUTO (the new default hand-off). */
+ * MR_TWOSHOT_SYNC_AUTO (the new default hand-off); 1.02 added MR_TILE_WIDE_PAIR. */
 int mr_version(void);
 
 #ifdef __cplusplus

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mr_version() == 101
+    assert L.mr_version() == 102
     for code, name in mr.STATUS.items():
         assert L.mr_status_string(code).decode().startswith(name)
     assert b"unknown" in L.mr_status_string(-99)
@@ -146,8 +146,8 @@ def test_options_validate_and_round_trip(L):
     assert mr.get_option("spin_limit") == 1000
     mr.set_option("spin_limit", 1 << 22)
     assert L.mr_get_option(2, ctypes.byref(v)) == OK and v.value == 0          # tile shape: auto
-    assert L.mr_set_option(2, 4) == EINVAL and L.mr_set_option(2, -1) == EINVAL
-    for shape in ("wide", "medium", "narrow", "auto"):
+    assert L.mr_set_option(2, 5) == EINVAL and L.mr_set_option(2, -1) == EINVAL
+    for shape in ("wide", "medium", "narrow", "wide_pair", "auto"):
         mr.set_option("tile_shape", shape)
         assert mr.get_option("tile_shape") == shape
 
@@ -165,7 +165,7 @@ def test_environment_sets_initial_options(tmp_path):
     assert out.returncode == 0, out.stderr
     assert out.stdout.split() == ["grid", "77", "narrow"]
     for bad in (dict(MR_TWOSHOT_SYNC="x", MR_SPIN_LIMIT="", MR_TILE_SHAPE="3z"),
-                dict(MR_TWOSHOT_SYNC="9", MR_SPIN_LIMIT="-1", MR_TILE_SHAPE="4"),
+                dict(MR_TWOSHOT_SYNC="9", MR_SPIN_LIMIT="-1", MR_TILE_SHAPE="5"),
                 dict(MR_TWOSHOT_SYNC="-2", MR_SPIN_LIMIT="4294967296", MR_TILE_SHAPE="0x10")):
         out = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, **bad), capture_output=True,
                              text=True, timeout=120)

@@ -407,7 +407,7 @@ def test_every_16bit_pattern_against_structured_partners(dtype):
         _check_modes(bufs, dtype, f"16-bit sweep {dtype} W={len(bufs)}")
 
 
-@pytest.mark.parametrize("shape", ["wide", "medium", "narrow"])
+@pytest.mark.parametrize("shape", ["wide", "medium", "narrow", "wide_pair"])
 def test_every_tile_shape_in_every_mode(shape):
     """Each forced tile shape (one-shot lanes x packs, two-shot phase-1 tile) gives the oracle's bits,
     on sizes that leave partial tiles, partial chunks and unaligned edges."""

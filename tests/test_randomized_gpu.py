@@ -30,7 +30,7 @@ def test_random_reduce_cases(block):
         dtype = str(rng.choice(["bf16", "fp16", "fp32"]))
         mode = str(rng.choice(["oneshot", "twoshot"]))
         sync = str(rng.choice(["auto", "tile", "chunk", "grid", "last"]))
-        shape = str(rng.choice(["auto", "wide", "medium", "narrow"]))
+        shape = str(rng.choice(["auto", "wide", "medium", "narrow", "wide_pair"]))
         aligned = rng.random() < 0.6
         offs = [0] * (W + 1) if aligned else [int(x) for x in rng.integers(0, 9, size=W + 1)]
         what = f"block {block} case {case}: W={W} n={n} {dtype} {mode} sync={sync} shape={shape} offs={offs}"
