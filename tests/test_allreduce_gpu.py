@@ -419,3 +419,32 @@ def test_every_tile_shape_in_every_mode(shape):
                 _check_modes(bufs, dtype, f"{shape} {dtype} W={W} n={n}")
     finally:
         mr.set_option("tile_shape", "auto")
+
+
+def test_rank_buffers_beyond_2GiB():
+    """W=3 bf16 rank buffers of 2^30 + 12,347 elements (just over 2 GiB each), so byte offsets pass 2^31 in
+    every kernel: one-shot wide tiles, wide pairs, two-shot.  Finite random bit patterns (exponent's top
+    bit cleared); sampled outputs, the first and last 4096 included, against the oracle."""
+    W, n = 3, (1 << 30) + 12_347
+    bufs = [workloads.random_bits(91, r, n, "bf16") & np.uint16(0xBFFF) for r in range(W)]
+    idx = np.unique(np.concatenate([np.arange(4096), np.arange(n - 4096, n),
+                                    np.linspace(0, n - 1, 1 << 20).astype(np.int64)]))
+    want = oracle.allreduce_sum_ref([b[idx] for b in bufs], "bf16")
+    dbufs = [to_dev(b, "bf16") for b in bufs]
+    del bufs
+    out = torch.empty(n, dtype=torch.bfloat16, device=device())
+    try:
+        for mode, shape in (("oneshot", "auto"), ("oneshot", "wide_pair"), ("twoshot", "auto")):
+            print(f"[case] beyond 2 GiB {mode} shape={shape}", flush=True)
+            out.view(torch.int16).fill_(-1)
+            mr.set_option("tile_shape", shape)
+            try:
+                _run(dbufs, "bf16", n, mode, out)
+            finally:
+                mr.set_option("tile_shape", "auto")
+            got = out.view(torch.int16)[torch.from_numpy(idx).to(device())].cpu().numpy().view(np.uint16)
+            assert_reduce_equal(got, want, "bf16", f"beyond 2 GiB {mode} {shape}")
+        assert mr.workspace_check() == 0
+    finally:
+        del dbufs, out
+        torch.cuda.empty_cache()
