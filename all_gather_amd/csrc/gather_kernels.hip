@@ -70,7 +70,7 @@ __device__ __forceinline__ void copy_realigned(const u32x4* sa, u32x4* d4, uint3
 
 // RA: the launch may hold spans whose source and destination 16-byte phases differ.  The kernel is
 // built twice because the realigning path, compiled in, slows the aligned one it never runs (same-GPU
-// A/B, config 4 bf16: 143 -> 146-149 us); the host picks the lean build whenever every span is in phase.
+// A/B, W=8 G=4 P=64 log-uniform splits, bf16: 143 -> 146-149 us); the host picks the lean build whenever every span is in phase.
 template <int S, bool RA>
 __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t len) {
   const uintptr_t ps = reinterpret_cast<uintptr_t>(src), pd = reinterpret_cast<uintptr_t>(dst);
@@ -129,8 +129,8 @@ __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t l
 // Param-major destination: the W slots of parameter s are contiguous in out (W*E_s elements from
 // O_s*W), so tiles are cut per parameter over that whole block and a tile crossing a rank boundary
 // switches source row mid-tile (W*P partial tiles become P).  Same-GPU A/B of lean builds against
-// tiles cut per (node-block, parameter, slot) segment, three interleaved repeats: config 4 (W=8, G=4,
-// P=64 log-uniform) bf16 143.1-144.2 -> 142.1-142.7 us, fp32 282.7-283.6 -> 279.5-281.0 us, from
+// tiles cut per (node-block, parameter, slot) segment, three interleaved repeats, FSDP-style splits
+// (W=8, G=4, P=64 log-uniform): bf16 143.1-144.2 -> 142.1-142.7 us, fp32 282.7-283.6 -> 279.5-281.0 us, from
 // separate shards bf16 141.9-142.2 -> 140.1-140.4 us; but one parameter (a rank-major copy) fp32
 // 271-272.5 -> 277.6-278.8 us, so the host uses these tiles only when P > 1.
 template <int S, bool RA>

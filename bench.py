@@ -132,7 +132,7 @@ def copy_ceiling(mr, torch, dev, stream, reps=40):
 
 def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes):
     """Ops alone and beside bf16 8192^3 GEMMs on a second stream (default priority): W=8 fp32 one-shot
-    and two-shot at 512 MiB per rank, and the config-4 param-contiguous scatter.  GB/s of the op and
+    and two-shot at 512 MiB per rank, and the param-contiguous scatter at the FSDP-style splits.  GB/s of the op and
     TFLOP/s of the GEMM, alone and together."""
     W, n = 8, 134_217_728
     algo = (W + 1) * n * 4
@@ -149,7 +149,7 @@ def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes):
     res = {"note": "op window overlaps the GEMM stream; GEMM figure averaged over its own window"}
     legs = [("reduce_oneshot_fp32_512MiB", mr.prepare_allreduce(bufs, out, "oneshot"), algo, 20, 24),
             ("reduce_twoshot_fp32_512MiB", mr.prepare_allreduce(bufs, out, "twoshot"), algo, 20, 24),
-            ("scatter_config4_bf16", gather_sets[0], gather_bytes, 100, 24)]
+            ("scatter_fsdp_splits_bf16", gather_sets[0], gather_bytes, 100, 24)]
     for name, call, nbytes, R, G in legs:
         t_op, t_gemm, t_op_c, t_gemm_c = _overlap(torch, stream, side, call, R, gemm, G)
         r = {"op_GBps_alone": nbytes / t_op / 1e9, "op_GBps_with_gemm": nbytes / t_op_c / 1e9,
@@ -278,12 +278,12 @@ def main():
     stream = torch.cuda.current_stream()
     mr.lib()
 
-    c = workloads.CONFIG2
+    c = workloads.W8_BF16_16MIB
     W, n, dtype = c["W"], c["n"], c["dtype"]
     s = 2
     algo = (W + 1) * n * s  # 150,994,944
-    log(f"[bench] inputs: config2 W={W} n={n} {dtype} N(0,1), {args.sets} buffer sets")
-    host = workloads.rank_buffers(c["cfg"], W, n, dtype, c["dist"])
+    log(f"[bench] inputs: W={W} n={n} {dtype} N(0,1), {args.sets} buffer sets")
+    host = workloads.rank_buffers(c["seed"], W, n, dtype, c["dist"])
     base = [torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in host]
     sets = []
     for k in range(args.sets):
@@ -356,8 +356,8 @@ def main():
                 f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")
         mr.set_option("twoshot_sync", "auto")
         # param-contiguous scatter: W=8, G=4, P=64 log-uniform splits, bf16 random bits
-        c4 = workloads.CONFIG4
-        splits = [int(x) for x in workloads.log_uniform_splits(c4["cfg"], c4["P"])]
+        c4 = workloads.FSDP_SPLITS_W8_G4_P64
+        splits = [int(x) for x in workloads.log_uniform_splits(c4["seed"], c4["P"])]
         T = sum(splits)
         gsets = []
         for k in range(2):

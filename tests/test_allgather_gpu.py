@@ -29,12 +29,12 @@ def _check(src_bits, W, G, splits, dtype, what):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32", "int32"])
-def test_config4_random_bits(dtype):
-    c = workloads.CONFIG4
-    splits = workloads.log_uniform_splits(c["cfg"], c["P"])
+def test_fsdp_splits_random_bits(dtype):
+    c = workloads.FSDP_SPLITS_W8_G4_P64
+    splits = workloads.log_uniform_splits(c["seed"], c["P"])
     T = int(splits.sum())
-    src = workloads.gather_source(c["cfg"], c["W"], T, dtype)
-    _check(src, c["W"], c["G"], splits, dtype, f"config4 {dtype} T={T}")
+    src = workloads.gather_source(c["seed"], c["W"], T, dtype)
+    _check(src, c["W"], c["G"], splits, dtype, f"FSDP splits W=8 G=4 P=64 {dtype} T={T}")
 
 
 def test_G_does_not_change_the_output():

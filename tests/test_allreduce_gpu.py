@@ -47,14 +47,14 @@ def _check_modes(bufs, dtype, what):
     assert mr.workspace_check() == 0
 
 
-def test_config1_w4_bf16_uniform():
-    c = workloads.CONFIG1
-    _check_modes(workloads.rank_buffers(c["cfg"], c["W"], c["n"], c["dtype"], c["dist"]), "bf16", "config1")
+def test_w4_bf16_64ki_uniform():
+    c = workloads.W4_BF16_64KI
+    _check_modes(workloads.rank_buffers(c["seed"], c["W"], c["n"], c["dtype"], c["dist"]), "bf16", "W=4 bf16 n=65,536")
 
 
-def test_config2_w8_bf16_16MiB_normal():
-    c = workloads.CONFIG2
-    _check_modes(workloads.rank_buffers(c["cfg"], c["W"], c["n"], c["dtype"], c["dist"]), "bf16", "config2")
+def test_w8_bf16_16MiB_normal():
+    c = workloads.W8_BF16_16MIB
+    _check_modes(workloads.rank_buffers(c["seed"], c["W"], c["n"], c["dtype"], c["dist"]), "bf16", "W=8 bf16 16 MiB")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
@@ -299,9 +299,9 @@ def test_cross_stream_consumer_waits_on_event():
         assert_reduce_equal(to_bits(copy), want, "bf16", f"rep {rep}")
 
 
-@pytest.mark.parametrize("per_rank", workloads.CONFIG3_BYTES, ids=lambda b: f"{b >> 10}KiB")
+@pytest.mark.parametrize("per_rank", workloads.SWEEP_BYTES_PER_RANK, ids=lambda b: f"{b >> 10}KiB")
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_config3_size_sweep(dtype, per_rank):
+def test_w8_size_sweep(dtype, per_rank):
     es = 2 if dtype == "bf16" else 4
     n = per_rank // es
     bufs = workloads.rank_buffers(3, 8, n, dtype, "uniform")
@@ -314,7 +314,7 @@ def test_config3_size_sweep(dtype, per_rank):
         want = oracle.allreduce_sum_ref([b[idx] for b in bufs], dtype)
     del bufs
     for mode in MODES:
-        print(f"[case] config3 {dtype} per-rank {per_rank >> 10} KiB {mode}", flush=True)
+        print(f"[case] size sweep {dtype} per-rank {per_rank >> 10} KiB {mode}", flush=True)
         got = to_bits(_run(dbufs, dtype, n, mode))
         assert_reduce_equal(got if idx is None else got[idx], want, dtype, f"{dtype} {per_rank} {mode}")
     del dbufs
@@ -338,15 +338,15 @@ def test_twoshot_elementwise_path_large():
     assert mr.workspace_check() == 0
 
 
-def test_config5_fp32_512MiB_alone_and_beside_a_gemm():
+def test_w8_fp32_512MiB_alone_and_beside_a_gemm():
     """W=8 fp32 rank buffers of 134,217,728 elements (512 MiB each), uniform[-1,1): sampled outputs
     against the oracle, alone and while bf16 8192^3 GEMMs run on a second stream."""
-    c = workloads.CONFIG5
+    c = workloads.W8_FP32_512MIB
     W, n = c["W"], c["n"]
     idx = np.linspace(0, n - 1, 1 << 20).astype(np.int64)
     dbufs, cols = [], []
     for r in range(W):  # one rank at a time keeps host memory near 1 GiB
-        b = workloads.rank_buffer(c["cfg"], r, n, "fp32", c["dist"])
+        b = workloads.rank_buffer(c["seed"], r, n, "fp32", c["dist"])
         cols.append(b[idx].copy())
         dbufs.append(to_dev(b, "fp32"))
         del b
@@ -355,7 +355,7 @@ def test_config5_fp32_512MiB_alone_and_beside_a_gemm():
     for mode in ("oneshot", "twoshot:tile"):
         out.zero_()
         got = to_bits(_run(dbufs, "fp32", n, mode))
-        assert_reduce_equal(got[idx], want, "fp32", f"config5 {mode}")
+        assert_reduce_equal(got[idx], want, "fp32", f"W=8 fp32 512 MiB {mode}")
     # beside a GEMM on another stream (default priority)
     g = torch.Generator(device=device())
     g.manual_seed(5)
@@ -371,7 +371,7 @@ def test_config5_fp32_512MiB_alone_and_beside_a_gemm():
         out.zero_()
         _call(dbufs, out, mode)
         got = to_bits(out.index_select(0, idx_dev))  # waits for this stream only; the GEMMs go on
-        assert_reduce_equal(got, want, "fp32", f"config5 {mode} under GEMM")
+        assert_reduce_equal(got, want, "fp32", f"W=8 fp32 512 MiB {mode} under GEMM")
         with torch.cuda.stream(side):
             for _ in range(2):
                 cgemm = torch.matmul(a, bm)

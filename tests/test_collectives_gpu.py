@@ -55,12 +55,12 @@ def test_allgather_into_tensor_and_list(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_param_contig_from_shards_config4(dtype):
-    c = workloads.CONFIG4
+def test_param_contig_from_shards_fsdp_splits(dtype):
+    c = workloads.FSDP_SPLITS_W8_G4_P64
     W, G = c["W"], c["G"]
-    splits = [int(x) for x in workloads.log_uniform_splits(c["cfg"], c["P"])]
+    splits = [int(x) for x in workloads.log_uniform_splits(c["seed"], c["P"])]
     T = sum(splits)
-    shards = [workloads.random_bits(c["cfg"], r, T, dtype) for r in range(W)]
+    shards = [workloads.random_bits(c["seed"], r, T, dtype) for r in range(W)]
     dshards = [to_dev(x, dtype) for x in shards]
     out = torch.empty(W * T, dtype=TORCH_DT[dtype], device=device())
     mr.allgather_param_contig_shards(dshards, G, splits, out)
