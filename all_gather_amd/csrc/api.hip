@@ -103,7 +103,7 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
   if (e != hipSuccess) return hip_fail(e);
   e = ws_clear(static_cast<char*>(p), bytes, st);
   if (e != hipSuccess) {
-    hipFree(p);
+    (void)hipFree(p);  // the launch error is the one reported
     return hip_fail(e);
   }
   if (w.base) g_retired[{dev, st}].push_back(w.base);  // grown: keep the old buffer alive (see g_retired)
@@ -507,9 +507,18 @@ mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {
   if ((w.base && w.owned) || !old.empty()) {  // free every library-owned buffer of this stream
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e);
-    if (w.base && w.owned) hipFree(w.base);
-    for (char* b : old) hipFree(b);
+    // every buffer is released even if one free fails; the first failure is reported and the stream is
+    // left unbound (the buffers are dropped either way, never freed twice)
+    hipError_t fe = (w.base && w.owned) ? hipFree(w.base) : hipSuccess;
+    for (char* b : old) {
+      const hipError_t f = hipFree(b);
+      if (fe == hipSuccess) fe = f;
+    }
     old.clear();
+    if (fe != hipSuccess) {
+      w = Workspace{};
+      return hip_fail(fe);
+    }
   }
   w = Workspace{};
   if (!dev_ptr) return MR_OK;

@@ -173,8 +173,9 @@ mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int
  *                     that call return MR_ERR_WORKSPACE.  dev_ptr == NULL unbinds (the library
  *                     allocates again on next use).  Either way it synchronises `stream` and frees
  *                     every library-owned workspace buffer of the stream, so a graph that captured a
- *                     two-shot call on it must not be replayed afterwards.  Not thread-safe against
- *                     concurrent calls on that stream.
+ *                     two-shot call on it must not be replayed afterwards.  If a free fails, the
+ *                     call returns MR_ERR_HIP and leaves the stream with no workspace bound.  Not
+ *                     thread-safe against concurrent calls on that stream.
  * mr_workspace_check: synchronises `stream`, then reads and clears the barrier error word of its
  *                     workspace.  *flags receives it (0 = no error; bit 0 = a phase-2 block gave up
  *                     waiting for phase 1, so that call's output is not valid).  Returns
