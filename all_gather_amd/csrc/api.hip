@@ -151,9 +151,10 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
   } else {
     const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, mr::twoshot_sync_for(n * static_cast<size_t>(es), g_twoshot_sync.load()),
                                                  g_spin_limit.load(), g_tile_shape.load());
-    const uint64_t grid = static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
+    const uint64_t grid = pl.xcd ? uint64_t{mr::kXcds} * (pl.run_padded + pl.run_padded / mr::kXcdGroup)
+                                 : static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
     if (grid >= (1ull << 24)) return MR_ERR_INVALID_ARG;
-    const size_t flags_needed = static_cast<size_t>(pl.chunks) * pl.t1;
+    const size_t flags_needed = pl.xcd ? pl.units : static_cast<size_t>(pl.chunks) * pl.t1;
     Workspace ws;
     mr_status s = get_workspace(st, n, es, flags_needed, &ws);
     if (s != MR_OK) return s;
@@ -161,8 +162,9 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
     char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (sh.vec ? (po & 15u) : 0);
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws.base + mr::kCtrlBytes);
     if (g_trace)
-      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu tile=%u t1=%u t2=%u\n",
-                   W, n, static_cast<int>(dtype), sh.vec, pl.sync, pl.chunk_units, pl.unit1, pl.t1, pl.t2);
+      std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu tile=%u t1=%u t2=%u "
+                   "xcd=%u units=%zu run=%u\n", W, n, static_cast<int>(dtype), sh.vec, pl.sync, pl.chunk_units, pl.unit1,
+                   pl.t1, pl.t2, pl.xcd, pl.units, pl.run);
     e = mr::launch_twoshot(in, W, dtype, out, stage, reinterpret_cast<mr::Ctrl*>(ws.base), flags, sh, pl, st);
   }
   return e == hipSuccess ? MR_OK : hip_fail(e);

@@ -27,7 +27,9 @@ struct Ctrl {
   uint32_t done1[MR_MAX_W][64];  // per-chunk phase-1 completions (chunk and grid barriers)
   uint32_t done2[MR_MAX_W][64];  // per-chunk phase-2 completions (grid barrier: phase-2 group pools)
   uint32_t gdone[64];            // workgroups finished (grid barrier)
-  uint32_t err[64];              // bit 0: a wait gave up after the spin limit
+  uint32_t err[64];              // bit 0: a wait gave up after the spin limit (that call's output is not
+                                 // valid); bits 1 and 2: the XCD-local two-shot recomputed units after a
+                                 // wait gave up / whose producer ran on another XCD (output valid)
 };
 static_assert(sizeof(Ctrl) <= kCtrlBytes, "ctrl layout");
 
@@ -64,6 +66,13 @@ inline uint32_t oneshot_shape(size_t npacks, int elem_size, uint32_t forced) {
   if (npacks >= (size_t(1) << 16)) return kShapeMedium;  // 256 lanes x 1 pack
   return kShapeNarrow;                                   // 64 lanes x 1 pack
 }
+// Lanes (= packs) of the two-shot's wide phase-1 tile; the kernel's workgroup size and the planner's
+// tile size both come from it.
+#ifndef MR_TS_BLOCK
+#define MR_TS_BLOCK 1024
+#endif
+constexpr uint32_t kTwoShotWideTile = MR_TS_BLOCK;
+static_assert(kTwoShotWideTile == 256 || kTwoShotWideTile == 512 || kTwoShotWideTile == 1024, "workgroup size");
 // Two-shot phase-1 tile (lanes = packs per tile) for a message of `npacks` packs.  The grid barrier
 // orders every workgroup through one ticket counter (about 11.6 ns per same-address atomic), so it
 // keeps the tile count low: 256-pack tiles only below 64 Ki packs, never 64-pack ones.
@@ -73,7 +82,16 @@ inline uint32_t twoshot_tile_packs(size_t npacks, uint32_t sync, uint32_t forced
                          : npacks >= (size_t(1) << (grid ? 16 : 17))      ? kShapeWide
                          : grid || npacks >= (size_t(1) << 13)            ? kShapeMedium
                                                                           : kShapeNarrow;
-  return shape == kShapeNarrow ? 64u : shape == kShapeMedium ? 256u : 1024u;
+  return shape == kShapeNarrow ? 64u : shape == kShapeMedium ? 256u : kTwoShotWideTile;
+}
+// The per-tile hand-off runs on XCD-local units (twoshot_xcd) on the 16-byte path for W <= 8, from
+// 1 Mi packs (16 MiB per rank buffer) up, or at any size under MR_TILE_WIDE_PAIR.  Below 16 MiB the
+// ticketed chunk tiles lead (8 MiB bf16: 20.1 against 21.6 us).
+constexpr uint32_t kXcds = 8;      // XCDs of an MI355X: one run of units each
+constexpr uint32_t kXcdGroup = 4;  // units per phase-2 copy
+inline bool twoshot_xcd_units(int vec, int W, size_t npacks, uint32_t sync, uint32_t forced) {
+  if (!vec || W > 8 || sync != kSyncTile) return false;
+  return forced == kShapeWidePair || (forced == kShapeAuto && npacks >= (size_t(1) << 20));
 }
 // Two-shot hand-off under MR_TWOSHOT_SYNC_AUTO: the last-arriver hand-off leads below 16 MiB per rank
 // (12.3 vs 16.4 us for per-tile flags at 4 MiB, W=8 bf16), per-tile flags above (125 vs 149 us at
@@ -109,6 +127,11 @@ struct TwoShotPlan {
   uint32_t unit2;        // units per phase-2 tile
   uint32_t sync;         // TwoShotSync
   uint32_t spin_limit;   // bounded wait (polls)
+  // XCD-local units (xcd == 1; the chunk fields above are then unused by the kernel)
+  uint32_t xcd;
+  uint32_t run;          // units per XCD run
+  uint32_t run_padded;   // run rounded up to whole copy groups
+  size_t units;          // units of the message (16 KiB of output each)
 };
 
 hipError_t launch_oneshot(const RankPtrs& in, int W, mr_dtype dt, char* out, const ReduceShape& sh,

@@ -31,9 +31,6 @@ __device__ void raw_buffer_store_v4(i32x4 data, i32x4 rsrc, int voffset, int sof
 #ifndef MR_TS_LOAD_AUX
 #define MR_TS_LOAD_AUX (1 << 4)
 #endif
-#ifndef MR_TS_BLOCK
-#define MR_TS_BLOCK 1024
-#endif
 #ifndef MR_TS_RATIO
 #define MR_TS_RATIO 4
 #endif
@@ -461,7 +458,7 @@ static_assert(kRatio >= 1 && kRatio <= 64, "one lane of the first wave waits for
 // (same-GPU A/B at W=8 bf16, 16 MiB per rank, per-tile flags: 1024 lanes x 1 pack 35.4 us, 512 x 2
 // 39.2 us, 256 x 4 39.8 us; each publish waits for its stores); smaller ones TB=256 or 64, so that
 // each chunk still splits into enough tiles to fill the CUs.
-constexpr int kTBlock = MR_TS_BLOCK;
+constexpr int kTBlock = static_cast<int>(kTwoShotWideTile);  // the planner sizes wide tiles by it too
 constexpr int kP2 = kRatio;  // packs per lane, phase 2
 // Element-wise path (pointers in different 16-byte phases): elements per lane per phase-1 tile.  Same-GPU
 // A/B, W=8 bf16, 16 MiB per rank, inputs at alternating 2-byte phases: one element per lane with the
@@ -470,22 +467,22 @@ constexpr int kP2 = kRatio;  // packs per lane, phase 2
 // outstanding loads a wave can count).  The 16-byte path takes 35.6 us.
 constexpr int kElemPer = 4;
 
-// Phase 2 of one group: copy phase-2 tile q of chunk c (ratio phase-1 tiles) from the stage to out with
-// device-scope stage loads.
-template <typename D, int TB>
+// Phase 2 of one group: copy the TB*P2 packs from `first` (clipped to cend) from the stage to out with
+// device-scope stage loads, P2 packs per lane, wave-contiguous.
+template <typename D, int TB, int P2, int LAUX = kStageLoadAux>
 __device__ __forceinline__ void copy_group(char* out, char* stage, const ReduceShape& sh, size_t first, size_t cend,
                                            bool with_edges) {
   const size_t hb = sh.head * D::kSize;
-  const i32x4 rs = make_rsrc(stage + hb + first * 16, TB * kP2 * 16);
-  u32x4 v[kP2];
+  const i32x4 rs = make_rsrc(stage + hb + first * 16, TB * P2 * 16);
+  u32x4 v[P2];
 #pragma unroll
-  for (int u = 0; u < kP2; ++u) {
-    const size_t i = wc_pack<TB, kP2>(first, u);
-    if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, static_cast<int>((i - first) * 16), 0, kStageLoadAux));
+  for (int u = 0; u < P2; ++u) {
+    const size_t i = wc_pack<TB, P2>(first, u);
+    if (i < cend) v[u] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, static_cast<int>((i - first) * 16), 0, LAUX));
   }
 #pragma unroll
-  for (int u = 0; u < kP2; ++u) {
-    const size_t i = wc_pack<TB, kP2>(first, u);
+  for (int u = 0; u < P2; ++u) {
+    const size_t i = wc_pack<TB, P2>(first, u);
     if (i < cend) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + hb) + i);
   }
   if (with_edges) copy_edges_from_stage<D>(stage, out, sh);
@@ -538,14 +535,149 @@ __global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* 
     publish_phase1(ctrl, flags, pl, c, k);
     if (pl.sync == kSyncLast && arrive_last(flags, pl, c, k)) {
       const uint32_t q = k / pl.ratio;
-      copy_group<D, TB>(out, stage, sh, c0 + static_cast<size_t>(q) * (TB * kRatio), cend, c == 0 && q == 0);
+      copy_group<D, TB, kP2>(out, stage, sh, c0 + static_cast<size_t>(q) * (TB * kRatio), cend, c == 0 && q == 0);
     }
   } else if (k < pl.t1 + pl.t2) {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
-    copy_group<D, TB>(out, stage, sh, c0 + static_cast<size_t>(q) * (TB * kRatio), cend, c == 0 && q == 0);
+    copy_group<D, TB, kP2>(out, stage, sh, c0 + static_cast<size_t>(q) * (TB * kRatio), cend, c == 0 && q == 0);
   }
   finish_twoshot(ctrl, pl, c, k);
+}
+
+// XCD-local two-shot with per-unit producer flags (16-byte path, W <= 8; the per-tile hand-off from
+// 16 MiB per rank buffer).
+//
+// Units.  The message is cut into units of one wide tile (256 lanes x 4 packs, 16 KiB of output) and
+// the units into kXcds runs of `run` consecutive units, one run per XCD.  Workgroup b belongs to run
+// x = b % kXcds, because workgroups are dealt to the XCDs in turn; its index s = b / kXcds inside the
+// run gives its role: s < run_padded reduces unit s of the run into the stage (phase 1), larger s copy
+// a group of kXcdGroup consecutive units of the run from the stage to out (phase 2, always units that
+// other workgroups reduced).  Roles come from the index, so no ticket atomic delays a workgroup's loads.
+//
+// Hand-off inside one XCD.  A producer writes its unit to the stage with ordinary write-back stores,
+// waits until the XCD's L2 has acknowledged every one of them (vmcnt 0) and then publishes the unit by
+// exchanging its flag word for 1 + the XCC id it runs on (a relaxed agent-scope atomic).  A copier
+// polls the flags of its group; a flag holding 1 + its own XCC id means the unit sits in the L2 it
+// reads through, so it reads the stage with L1-bypassing (sc0) loads.  One L2 serves every CU of an XCD,
+// so that is all the ordering the copy needs; no whole-L2 write-back and no write-through stores.
+//
+// Nothing rests on where the dispatcher places workgroups or in which order it starts them.  A unit
+// whose flag names another XCD, or whose producer has not published within the spin limit, is
+// recomputed by the copier from the rank buffers straight into out (same arithmetic, same bits).  On a
+// timeout the copier first claims the flag (compare-and-swap 0 -> kTaken); a producer that publishes
+// later finds kTaken and clears it, and a copier that finds a published value clears it, so every flag
+// is zero again when the launch ends and a late release can never satisfy a later launch.  The error
+// word records these rare paths (bit 1: recomputed after a timeout, bit 2: producer on another XCD);
+// the output stays valid in both.
+//
+// Same-GPU A/B against the ticketed 1024-lane tile kernel (W=8, rotating buffer sets, three repeats):
+// bf16 16 MiB per rank 35.1 -> 34.1-34.3 us and 35.4 -> 33.0 us on two GPUs, 32 MiB 66.3 -> 63.5-64.4,
+// 64 MiB 119-129 -> 118-119; fp32 16 MiB 35.1 -> 34.1-34.3, 64 MiB 124.6 -> 119.3.  Units of two wide
+// tiles (one round of 512 workgroups at 16 MiB), a copy group of 1 or 3 units, a non-temporal stage
+// load, and copies interleaved into the dispatch order after a lag of 24-192 units per run all
+// measured the same or slower; the interleaved copies wait and hold slots.
+constexpr uint32_t kTaken = 0xffffffffu;  // flag claimed by a copier that stopped waiting
+constexpr int kXcdStageLoadAux = 1;       // sc0: the stage is read through this XCD's L2, past the CU's L1
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t x;
+  __asm__ volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 0xfu;
+}
+
+// Lanes 0..kXcdGroup-1 of the first wave settle one unit each: 0 nothing (past the end), 1 copy it from
+// the stage, 2 recompute it.
+__device__ __forceinline__ uint32_t settle_unit(Ctrl* ctrl, uint32_t* flags, size_t u, uint32_t spin_limit) {
+  uint32_t* f = &flags[u];
+  uint32_t v, spins = 0;
+  while ((v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > spin_limit) {
+      uint32_t expect = 0u;
+      v = __hip_atomic_compare_exchange_strong(f, &expect, kTaken, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+              ? kTaken
+              : expect;  // published meanwhile
+      break;
+    }
+  }
+  if (v == kTaken) {  // our claim: the producer clears it when it publishes
+    __hip_atomic_fetch_or(&ctrl->err[0], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return 2u;
+  }
+  __hip_atomic_store(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // consumed: re-arm
+  if (v == 1u + xcc_id()) return 1u;
+  __hip_atomic_fetch_or(&ctrl->err[0], 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 2u;
+}
+
+template <typename D, int W>
+__global__ __launch_bounds__(kOneShotBlock) void twoshot_xcd(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
+                                                             uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
+  constexpr int B = kOneShotBlock, U = OneShotU<W>::value, R = static_cast<int>(kXcdGroup);
+  constexpr size_t UP = static_cast<size_t>(B) * U;  // packs per unit
+  static_assert(U == 4, "wide units");
+  const size_t hb = sh.head * D::kSize;
+  const uint32_t x = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
+  const size_t run0 = static_cast<size_t>(x) * pl.run;  // first unit of this run
+  u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
+  if (s < pl.run_padded) {
+    const size_t u = run0 + s;
+    if (s >= pl.run || u >= pl.units) return;  // padding
+    const size_t first = u * UP;
+    const i32x4 rs = make_rsrc(stage + hb + first * 16, static_cast<uint32_t>(UP * 16));
+    reduce_tile<D, W, B, U>(in, hb, first, sh.npacks, [&](int, size_t i, const u32x4& o) {
+      raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), rs, static_cast<int>((i - first) * 16), 0, 0);
+    });
+    if (u == 0) reduce_edges<D, W, false>(in, out, sh);  // the few elements outside the packs: straight to out
+    __builtin_amdgcn_s_waitcnt(0x0f70);                 // vmcnt(0): the L2 holds this lane's stage stores
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t old = __hip_atomic_exchange(&flags[u], 1u + xcc_id(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == kTaken) __hip_atomic_store(&flags[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  const uint32_t g = s - pl.run_padded;  // copy group of this run
+  __shared__ uint32_t s_mode[R];
+  if (threadIdx.x < R) {
+    const size_t i = static_cast<size_t>(g) * R + threadIdx.x;
+    s_mode[threadIdx.x] = (i < pl.run && run0 + i < pl.units) ? settle_unit(ctrl, flags, run0 + i, pl.spin_limit) : 0u;
+  }
+  __syncthreads();
+  const size_t first = (run0 + static_cast<size_t>(g) * R) * UP;
+  bool from_stage = true;
+#pragma unroll
+  for (int r = 0; r < R; ++r) from_stage = from_stage && s_mode[r] != 2u;
+  if (from_stage) {  // the common case: every unit from the stage, all loads in flight before the stores
+    const i32x4 rs = make_rsrc(stage + hb + first * 16, static_cast<uint32_t>(UP * R * 16));
+    u32x4 v[R * U];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const size_t i = wc_pack<B, U>(first + r * UP, uu);
+        if (s_mode[r] == 1u && i < sh.npacks)
+          v[r * U + uu] = __builtin_bit_cast(u32x4, raw_buffer_load_v4(rs, static_cast<int>((i - first) * 16), 0, kXcdStageLoadAux));
+      }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const size_t i = wc_pack<B, U>(first + r * UP, uu);
+        if (s_mode[r] == 1u && i < sh.npacks) __builtin_nontemporal_store(v[r * U + uu], dst + i);
+      }
+    return;
+  }
+#pragma unroll 1
+  for (int r = 0; r < R; ++r) {  // some unit recomputed: one unit at a time
+    const size_t f = first + r * UP;
+    if (s_mode[r] == 1u)
+      copy_group<D, B, U, kXcdStageLoadAux>(out, stage, sh, f, sh.npacks, false);
+    else if (s_mode[r] == 2u)
+      reduce_tile<D, W, B, U>(in, hb, f, sh.npacks, [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); });
+  }
 }
 
 // Element-wise two-shot for pointers that do not share one 16-byte alignment (units are elements;
@@ -692,6 +824,13 @@ hipError_t twoshot_vec_launch(const RankPtrs& in, char* out, char* stage, Ctrl* 
 template <typename D, int W>
 hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uint32_t* flags, const ReduceShape& sh,
                      const TwoShotPlan& pl, hipStream_t st) {
+  if constexpr (W <= 8) {
+    if (sh.vec && pl.xcd) {
+      const unsigned g = kXcds * (pl.run_padded + pl.run_padded / kXcdGroup);
+      hipLaunchKernelGGL((twoshot_xcd<D, W>), dim3(g), dim3(kOneShotBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
+      return hipGetLastError();
+    }
+  }
   const unsigned grid = pl.chunks * (pl.sync == kSyncLast ? pl.t1 : pl.t1 + pl.t2);
   if (sh.vec && pl.unit1 == 64)
     return twoshot_vec_launch<D, W, 64>(in, out, stage, ctrl, flags, sh, pl, grid, st);
@@ -777,6 +916,13 @@ TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t s
   pl.t2 = static_cast<uint32_t>(t2);
   pl.sync = sync;
   pl.spin_limit = spin_limit;
+  if (twoshot_xcd_units(sh.vec, W, sh.npacks, sync, shape)) {  // XCD-local units replace the chunk tiles
+    constexpr size_t UP = static_cast<size_t>(kOneShotBlock) * 4;
+    pl.xcd = 1;
+    pl.units = sh.npacks ? (sh.npacks + UP - 1) / UP : 1;  // an edges-only call still has one unit
+    pl.run = static_cast<uint32_t>((pl.units + kXcds - 1) / kXcds);
+    pl.run_padded = (pl.run + kXcdGroup - 1) / kXcdGroup * kXcdGroup;
+  }
   return pl;
 }
 

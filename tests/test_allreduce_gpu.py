@@ -148,7 +148,7 @@ def test_oneshot_equals_twoshot_and_is_deterministic():
     assert mr.workspace_check() == 0
 
 
-@pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last"])
+@pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last", "tile:wide_pair"])
 def test_twoshot_stale_stage_is_never_read(sync):
     """Two input sets alternate on one caller-owned workspace, so when a call starts its stage still
     holds the previous call's (different) sums: a phase-2 copy that ran ahead of its phase-1 producer
@@ -159,7 +159,9 @@ def test_twoshot_stale_stage_is_never_read(sync):
     dsets = [[to_dev(b, "bf16") for b in s] for s in sets]
     ws = torch.empty(mr.workspace_bytes(W, n, "bf16"), dtype=torch.uint8, device=device())
     mr.set_workspace(ws)
+    sync, _, shape = sync.partition(":")
     mr.set_option("twoshot_sync", sync)
+    mr.set_option("tile_shape", shape or "auto")
     try:
         outs = [torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(2)]
         for i in range(200):
@@ -171,6 +173,7 @@ def test_twoshot_stale_stage_is_never_read(sync):
                 assert_reduce_equal(to_bits(outs[k]), wants[k], "bf16", f"{sync} launch {i}")
         assert mr.workspace_check() == 0
     finally:
+        mr.set_option("tile_shape", "auto")
         mr.set_option("twoshot_sync", "auto")
         mr.set_workspace(None)
 
@@ -182,7 +185,8 @@ def test_twoshot_poisoned_stage_stress(sync):
     match the oracle bit for bit.  A phase-2 copy that ran ahead of its producer, or a phase-1 tile
     that was never written, would publish the poison."""
     W = 8
-    cases = [("narrow", 30_011), ("medium", 1_000_003), ("wide", 4_194_304 + 8), ("auto", 2_500_001)]
+    cases = [("narrow", 30_011), ("medium", 1_000_003), ("wide", 4_194_304 + 8), ("auto", 2_500_001),
+             ("wide_pair", 8_388_608 + 24)]
     n_max = max(n for _, n in cases)
     ws = torch.empty(mr.workspace_bytes(W, n_max, "bf16"), dtype=torch.uint8, device=device())
     flags_cap = ws.numel() >> 8
@@ -257,6 +261,45 @@ def test_bounded_wait_reports_and_recovers():
         torch.cuda.synchronize()
         assert_reduce_equal(to_bits(out), want, "bf16", f"after recovery {mode}")
     assert mr.workspace_check() == 0
+
+
+def test_xcd_twoshot_timeouts_recompute_and_leave_no_flag_set():
+    """XCD-local two-shot with a spin limit of 0: a copier whose unit is not yet published gives up at
+    once, claims the flag and recomputes the unit from the rank buffers.  The output must still match
+    the oracle, the error word may only carry the 'recomputed' bits (never bit 0), and after the launch
+    every flag word of the caller-owned workspace is zero again, so a late producer's release cannot
+    satisfy the next launch; the next launch (normal spin limit) is correct too."""
+    W, n = 8, 8_388_608 + 40
+    sets = [workloads.rank_buffers(90 + k, W, n, "bf16", "normal") for k in range(2)]
+    wants = [oracle.allreduce_sum_ref(b, "bf16") for b in sets]
+    dsets = [[to_dev(b, "bf16") for b in s] for s in sets]
+    nbytes = mr.workspace_bytes(W, n, "bf16")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device())
+    flags_cap = nbytes >> 8
+    mr.set_workspace(ws)
+    mr.set_option("twoshot_sync", "tile")
+    mr.set_option("tile_shape", "wide_pair")
+    try:
+        outs = [torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(2)]
+        for rep in range(6):
+            k = rep % 2
+            mr.set_option("spin_limit", 0 if k == 0 else 1 << 22)
+            outs[k].view(torch.int16).fill_(-1)
+            mr.allreduce_sum(dsets[k], outs[k], mode="twoshot")
+            torch.cuda.synchronize()
+            assert_reduce_equal(to_bits(outs[k]), wants[k], "bf16", f"rep {rep} spin {'0' if k == 0 else 'default'}")
+            leftover = int((ws[16384:16384 + 4 * flags_cap].view(torch.int32) != 0).sum())
+            assert leftover == 0, f"rep {rep}: {leftover} flag words left set"
+            err = int(ws[:16384].view(torch.int32)[(3 * 16 * 64 + 64):(3 * 16 * 64 + 65)].item())
+            assert err & 1 == 0, f"rep {rep}: error word {err:#x}"
+        flags = mr.workspace_check()
+        assert flags & 1 == 0
+        print(f"[case] error word after the spin-0 launches: {flags:#x}", flush=True)
+    finally:
+        mr.set_option("spin_limit", 1 << 22)
+        mr.set_option("tile_shape", "auto")
+        mr.set_option("twoshot_sync", "auto")
+        mr.set_workspace(None)
 
 
 def test_twoshot_on_two_streams_concurrently():
