@@ -22,6 +22,7 @@ STATUS = {
     -3: "MR_ERR_ALIAS",
     -4: "MR_ERR_WORKSPACE",
     -5: "MR_ERR_HIP",
+    -6: "MR_ERR_ENGINE",
 }
 DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2, "int32": 3}
 MODE_CODE = {"oneshot": 0, "twoshot": 1}
@@ -56,6 +57,10 @@ _SIGS = {
     "mr_allgather_param_contig_shards": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int,
                                                         ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int,
                                                         ctypes.c_void_p, ctypes.c_void_p]),
+    "mr_allgather_param_contig_sdma": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                      ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int,
+                                                      ctypes.c_void_p, ctypes.c_void_p]),
+    "mr_sdma_engines": (ctypes.c_int, []),
     "mr_set_option": (ctypes.c_int, [ctypes.c_int, ctypes.c_int64]),
     "mr_get_option": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -200,6 +205,29 @@ def allgather_param_contig(src, W: int, G: int, splits: Sequence[int], out, stre
     """Scatter the rank-major ``src`` ([W][T], T = sum(splits)) into [param][rank] order in ``out``."""
     prepare_allgather_param_contig(src, W, G, splits, out, stream)()
     return out
+
+
+def prepare_allgather_param_contig_sdma(src, W: int, G: int, splits: Sequence[int], out, stream=None):
+    """Pre-marshalled mr_allgather_param_contig_sdma: the same placement on the SDMA copy engines (a
+    synchronous call: it waits for ``stream``, copies, and returns when the copies are complete)."""
+    _dev_tensor(src, "src")
+    sp, T = _splits_array(splits)
+    if W < 1 or src.numel() != W * T:
+        raise ValueError(f"src must hold W*sum(splits) = {max(W, 0) * T} elements")
+    _same([out], src, "out", src.numel())
+    args = (src.data_ptr(), W, G, sp, len(sp), DTYPE_CODE[dtype_name(src)], out.data_ptr(), _stream_handle(stream))
+    return _prepared("mr_allgather_param_contig_sdma", lib().mr_allgather_param_contig_sdma, args, (sp, src, out))
+
+
+def allgather_param_contig_sdma(src, W: int, G: int, splits: Sequence[int], out, stream=None):
+    """mr_allgather_param_contig's placement copied by the SDMA engines (synchronous)."""
+    prepare_allgather_param_contig_sdma(src, W, G, splits, out, stream)()
+    return out
+
+
+def sdma_engines() -> int:
+    """SDMA engines the current device offers for copies within its own memory."""
+    return int(lib().mr_sdma_engines())
 
 
 def _shard_ptrs(shards):

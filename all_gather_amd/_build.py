@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmr.so")
-SOURCES = ["api.hip", "reduce_kernels.hip", "gather_kernels.hip", "probe_kernels.hip"]
+SOURCES = ["api.hip", "reduce_kernels.hip", "gather_kernels.hip", "probe_kernels.hip", "sdma.hip"]
 ARCH = "gfx950"
 
 # Device flags: no fast-math and no contraction (the sums must be plain fp32 RNE adds in order),
@@ -52,7 +52,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-lhsa-runtime64", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

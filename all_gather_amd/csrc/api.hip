@@ -322,13 +322,14 @@ const char* mr_status_string(mr_status s) {
     case MR_ERR_ALIAS: return "MR_ERR_ALIAS: output partially overlaps an input";
     case MR_ERR_WORKSPACE: return "MR_ERR_WORKSPACE: two-shot workspace missing, too small or in error";
     case MR_ERR_HIP: return "MR_ERR_HIP: HIP runtime call failed";
+    case MR_ERR_ENGINE: return "MR_ERR_ENGINE: copy engines unavailable or a copy failed";
     default: return "unknown mr_status";
   }
 }
 
 int mr_last_hip_error(void) { return g_last_hip_error; }
 
-int mr_version(void) { return 102; }
+int mr_version(void) { return 103; }
 
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
   if (W < 1 || W > MR_MAX_W || !is_float(dtype)) return 0;
@@ -434,6 +435,53 @@ mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_
     a.src = static_cast<const char*>(src);
     a.out = static_cast<char*>(out);
   }, realign, reinterpret_cast<hipStream_t>(stream));
+}
+
+mr_status mr_allgather_param_contig_sdma(const void* src, int W, int G, const uint64_t* splits, int P, mr_dtype dtype,
+                                         void* out, mr_stream stream) {
+  if (W < 1 || W > 65535) return MR_ERR_INVALID_ARG;
+  const GatherPlan* gp = nullptr;
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);
+  if (s != MR_OK || gp->T == 0) return s;
+  if (!src || !out || !elem_aligned(src, gp->es) || !elem_aligned(out, gp->es)) return MR_ERR_INVALID_ARG;
+  const uint64_t total_bytes = static_cast<uint64_t>(W) * gp->T * gp->es;
+  if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
+    return MR_ERR_ALIAS;
+  // one piece per (parameter, rank), in the order of the page's node-block -> split -> slot loop;
+  // pieces that continue the previous one on both sides are merged (one parameter: a single copy)
+  std::vector<mr::CopyPiece> pieces;
+  const char* sb = static_cast<const char*>(src);
+  char* ob = static_cast<char*>(out);
+  const uint64_t es = gp->es, T = gp->T;
+  for (int m = 0; m < W / G; ++m)
+    for (const mr::GatherArgs& g : gp->groups)
+      for (uint32_t i = 0; i < g.P; ++i) {
+        const uint64_t O = g.O[i], E = g.O[i + 1] - O;
+        for (int gg = 0; E && gg < G; ++gg) {
+          const uint64_t r = static_cast<uint64_t>(m) * G + gg;
+          const mr::CopyPiece c{sb + (r * T + O) * es, ob + (O * W + r * E) * es, E * es};
+          if (!pieces.empty() && pieces.back().src + pieces.back().bytes == c.src &&
+              pieces.back().dst + pieces.back().bytes == c.dst)
+            pieces.back().bytes += c.bytes;
+          else
+            pieces.push_back(c);
+        }
+      }
+  const hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));  // src is ready
+  if (e != hipSuccess) return hip_fail(e);
+  const int rc = mr::sdma_copy(pieces.data(), pieces.size());
+  if (rc != 0) {
+    g_last_hip_error = rc;
+    return MR_ERR_ENGINE;
+  }
+  return MR_OK;
+}
+
+int mr_sdma_engines(void) {
+  int status = 0;
+  const int count = mr::sdma_engine_count(&status);
+  if (count == 0) g_last_hip_error = status;
+  return count;
 }
 
 mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int G, const uint64_t* splits, int P,

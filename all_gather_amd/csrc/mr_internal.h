@@ -177,6 +177,17 @@ struct GatherArgs {
   uint32_t total_tiles;                  // span: tile_prefix[P]; else W/G node-blocks * tiles_per_block
 };
 
+// SDMA copy engines (sdma.hip).  sdma_copy copies every piece on the current device's engines and
+// waits for all of them: 0 on success, an hsa_status_t (> 0) if the engines are unavailable or a copy
+// could not be issued, -1 if an engine reported a failed copy.
+struct CopyPiece {
+  const char* src;
+  char* dst;
+  uint64_t bytes;
+};
+int sdma_copy(const CopyPiece* pieces, size_t count);
+int sdma_engine_count(int* status);  // status: the hsa_status_t of finding the engines
+
 // realign: some span's source and destination differ in 16-byte phase (selects the kernel build)
 hipError_t launch_param_contig(const GatherArgs& a, bool realign, hipStream_t st);
 uint64_t gather_tiles_per_segment(uint64_t E, uint32_t elem);

@@ -76,7 +76,9 @@ def time_steps(calls, K, W_, stream):
 
 def _overlap(torch, stream, side, call, R, gemm, G):
     """Time R calls alone on `stream`, G GEMMs alone on `side`, then both at once (the GEMM window is
-    opened first).  Returns seconds per call and per GEMM, alone and together."""
+    opened first).  Returns seconds per call and per GEMM, alone and together.  A synchronous call (the
+    copy-engine gather returns only when its copies are complete) is timed by the same events: the
+    second is recorded after the last call has returned."""
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def op_run():
@@ -130,7 +132,48 @@ def copy_ceiling(mr, torch, dev, stream, reps=40):
     return 2 * (1 << 28) / t / 1e9
 
 
-def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes):
+def stream_mix_ceiling(mr, torch, sets, n, s, stream, K, warmup):
+    """Same-run ceilings of the one-shot's access pattern on its own buffer sets: the library's probe
+    kernel (mrx_stream_mix, not part of the mr.h ABI) streams the 8 rank buffers and writes the XOR of
+    them to out with the one-shot's lane layout, and once more without the write.  Returns GB/s
+    counting every byte moved (9 and 8 times the per-rank bytes)."""
+    import ctypes
+
+    L = mr.lib()
+    f = L.mrx_stream_mix
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                  ctypes.c_void_p]
+    res = {}
+    for name, write in (("reads8_write1", 1), ("reads8_only", 0)):
+        calls = []
+        for bufs, out in sets:
+            ptrs = (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+            args = (ptrs, len(bufs), out.data_ptr(), n * s, write, stream.cuda_stream or None)
+            calls.append(lambda a=args, keep=ptrs: _probe_ok(f(*a)))
+        ms = time_steps(calls, K, warmup, stream)
+        t = ms / K * 1e-3
+        nbytes = (len(sets[0][0]) + write) * n * s
+        res[name] = {"us": t * 1e6, "GBps": nbytes / t / 1e9, "bytes": nbytes}
+    return res
+
+
+def _same_bytes_copy(mr, prepared, K, warmup, stream, nbytes, gbs):
+    """A plain copy of exactly the bytes a prepared gather moves, on its own source and output buffers,
+    made by the same kernel (all_gather_into_tensor of one shard) and timed the same way."""
+    calls = [mr.prepare_allgather_shards([c.keepalive[1]], c.keepalive[2]) for c in prepared]
+    ms = time_steps(calls, K, max(2, warmup // 10), stream)
+    t = ms / K * 1e-3
+    copy = nbytes / t / 1e9
+    return {"copy_same_bytes_us": t * 1e6, "copy_same_bytes_GBps": copy, "frac_of_copy_same_bytes": gbs / copy}
+
+
+def _probe_ok(rc):
+    if rc != 0:
+        raise RuntimeError(f"mrx_stream_mix failed: {rc}")
+
+
+def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes, sdma_sets=None):
     """Ops alone and beside bf16 8192^3 GEMMs on a second stream (default priority): W=8 fp32 one-shot
     and two-shot at 512 MiB per rank, and the param-contiguous scatter at the FSDP-style splits.  GB/s of the op and
     TFLOP/s of the GEMM, alone and together."""
@@ -150,6 +193,8 @@ def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes):
     legs = [("reduce_oneshot_fp32_512MiB", mr.prepare_allreduce(bufs, out, "oneshot"), algo, 20, 24),
             ("reduce_twoshot_fp32_512MiB", mr.prepare_allreduce(bufs, out, "twoshot"), algo, 20, 24),
             ("scatter_fsdp_splits_bf16", gather_sets[0], gather_bytes, 100, 24)]
+    if sdma_sets:
+        legs.append(("scatter_fsdp_splits_bf16_sdma", sdma_sets[0], gather_bytes, 12, 24))
     for name, call, nbytes, R, G in legs:
         t_op, t_gemm, t_op_c, t_gemm_c = _overlap(torch, stream, side, call, R, gemm, G)
         r = {"op_GBps_alone": nbytes / t_op / 1e9, "op_GBps_with_gemm": nbytes / t_op_c / 1e9,
@@ -322,6 +367,11 @@ def main():
     traffic, traffic_src = traffic_from_profile(algo)
     copy_gbs = copy_ceiling(mr, torch, dev, stream)
     log(f"[bench] plain 256 MiB copy (gather kernel, one shard) on the same GPU: {copy_gbs:.1f} GB/s")
+    smix = stream_mix_ceiling(mr, torch, sets, n, s, stream, K, args.warmup)
+    mix_gbs = smix["reads8_write1"]["GBps"]
+    log(f"[bench] stream-mix probe on the same buffers: 8 reads + 1 write {smix['reads8_write1']['us']:.2f} us "
+        f"({mix_gbs:.1f} GB/s), 8 reads only {smix['reads8_only']['us']:.2f} us "
+        f"({smix['reads8_only']['GBps']:.1f} GB/s)")
 
     paths = {}
     if not args.only_headline:
@@ -351,6 +401,8 @@ def main():
             t2 = ms2 / K * 1e-3
             paths[f"twoshot_{sync}"] = {"us": t2 * 1e6, "GBps_metric_bytes": algo / t2 / 1e9,
                                         "GBps_actual_bytes": actual2 / t2 / 1e9, "actual_bytes": actual2,
+                                        "frac_actual_bytes": actual2 / t2 / 1e9 / PEAK_GBS,
+                                        "kernel": "twoshot_xcd (XCD-local units)" if sync == "tile" else "twoshot_vec",
                                         "barrier_error_word": mr.workspace_check()}
             log(f"[bench] twoshot ({sync}): {t2 * 1e6:.2f} us/launch, {algo / t2 / 1e9:.1f} GB/s (metric bytes), "
                 f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")
@@ -368,8 +420,22 @@ def main():
         msg = time_steps(gsets, Kg, max(2, args.warmup // 10), stream)
         tg = msg / Kg * 1e-3
         paths["param_contig"] = {"us": tg * 1e6, "GBps": gbytes / tg / 1e9, "bytes": gbytes, "W": c4["W"],
-                                 "G": c4["G"], "P": c4["P"], "T": T, "dtype": "bf16"}
-        log(f"[bench] param_contig: {tg * 1e6:.1f} us/launch, {gbytes / tg / 1e9:.1f} GB/s ({gbytes} B)")
+                                 "G": c4["G"], "P": c4["P"], "T": T, "dtype": "bf16",
+                                 "frac": gbytes / tg / 1e9 / PEAK_GBS}
+        paths["param_contig"].update(_same_bytes_copy(mr, gsets, Kg, args.warmup, stream, gbytes, gbytes / tg / 1e9))
+        log(f"[bench] param_contig: {tg * 1e6:.1f} us/launch, {gbytes / tg / 1e9:.1f} GB/s ({gbytes} B); plain copy of "
+            f"the same bytes {paths['param_contig']['copy_same_bytes_GBps']:.1f} GB/s")
+        # the same gather on the SDMA copy engines (synchronous calls; no compute units)
+        sdma_sets = [mr.prepare_allgather_param_contig_sdma(c.keepalive[1], c4["W"], c4["G"], splits, c.keepalive[2])
+                     for c in gsets]
+        Ks = 10
+        mss = time_steps(sdma_sets, Ks, 2, stream)
+        ts = mss / Ks * 1e-3
+        paths["param_contig_sdma"] = {"us": ts * 1e6, "GBps": gbytes / ts / 1e9, "bytes": gbytes, "dtype": "bf16",
+                                      "engines": mr.sdma_engines(),
+                                      "note": "SDMA copy engines through the HSA runtime; synchronous calls, "
+                                              "host-observed time per call"}
+        log(f"[bench] param_contig on {mr.sdma_engines()} SDMA engines: {ts * 1e6:.1f} us/call, {gbytes / ts / 1e9:.1f} GB/s")
         # the same splits in fp32 (4-byte elements: twice the bytes of the bf16 case)
         fsets = []
         for k in range(2):
@@ -381,6 +447,7 @@ def main():
         paths["param_contig_fp32"] = {"us": tf * 1e6, "GBps": fbytes / tf / 1e9, "bytes": fbytes, "W": c4["W"],
                                       "G": c4["G"], "P": c4["P"], "T": T, "dtype": "fp32",
                                       "frac": fbytes / tf / 1e9 / PEAK_GBS}
+        paths["param_contig_fp32"].update(_same_bytes_copy(mr, fsets, Kg, args.warmup, stream, fbytes, fbytes / tf / 1e9))
         log(f"[bench] param_contig fp32: {tf * 1e6:.1f} us/launch, {fbytes / tf / 1e9:.1f} GB/s "
             f"({fbytes / tf / 1e9 / PEAK_GBS:.1%} of peak)")
         del fsets
@@ -399,25 +466,24 @@ def main():
             log(f"[bench] {name}: {tx * 1e6:.1f} us/launch, {gbytes / tx / 1e9:.1f} GB/s")
         del shard_sets
         torch.cuda.empty_cache()
-        paths["contention"] = contention_leg(mr, torch, dev, stream, gsets, gbytes)
-        del gsets
+        paths["contention"] = contention_leg(mr, torch, dev, stream, gsets, gbytes, sdma_sets)
+        del gsets, sdma_sets
         torch.cuda.empty_cache()
         if not args.no_sweep:
             paths["sweep_w8"] = sweep_leg(mr, torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
-        reps, times = 0, []
-        t_end = time.perf_counter() + 10.0
-        while reps < 3 or time.perf_counter() < t_end:
+        # the oracle on the full headline workload (one call is the whole sample: about 0.07 s), median of
+        # 3 runs single-threaded, then the same oracle over disjoint index ranges on every core this
+        # process may run on (per-element rank order unchanged, so the bits are the same), median of 3
+        times = []
+        for _ in range(3):
             t0 = time.perf_counter()
             oracle.allreduce_sum_ref(host, dtype)
             times.append(time.perf_counter() - t0)
-            reps += 1
         med = float(np.median(times))
-        # the same oracle over disjoint index ranges on several threads (bits unchanged); the pool is
-        # held to this process's share of the host, at most 16 threads
-        nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+        nthr = max(1, len(os.sched_getaffinity(0)))
         ttimes = []
         for _ in range(3):
             t0 = time.perf_counter()
@@ -425,11 +491,12 @@ def main():
             ttimes.append(time.perf_counter() - t0)
         tmed = float(np.median(ttimes))
         cpu = {"value": algo / med / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"the full workload (W=8 x 8,388,608 bf16), {reps} runs, median {med:.3f} s, "
-                         f"numpy single-threaded on {os.cpu_count()} host CPUs",
+               "sample": f"the full workload (W=8 x 8,388,608 bf16, one call), median of 3 runs ({med:.3f} s), "
+                         f"numpy single-threaded",
                "cpu_model": cpu_model(),
                "threaded": {"value": algo / tmed / 1e9, "unit": "GB/s", "cores": nthr, "seconds": tmed,
-                            "sample": "the same workload split over disjoint index ranges, median of 3"}}
+                            "sample": "the same workload split over disjoint index ranges on every affinity "
+                                      "core, median of 3"}}
         log(f"[bench] cpu oracle: {med:.3f} s per call, {algo / med / 1e9:.2f} GB/s; "
             f"{nthr} threads: {tmed:.3f} s, {algo / tmed / 1e9:.2f} GB/s ({cpu['cpu_model']})")
 
@@ -457,6 +524,11 @@ def main():
                      "kernel": "oneshot_pair<Bf16, 8>", "bytes_per_launch": algo,
                      "avg_launch_us": round(t_launch * 1e6, 3), "traffic_source": traffic_src,
                      "traffic_GBps": round(traffic / t_launch / 1e9, 1) if traffic else None,
+                     "stream_mix_ceiling_GBps": round(mix_gbs, 1),
+                     "stream_mix_ceiling_kernel": "mrx_stream_mix: the one-shot's 8 rank buffers read and their XOR "
+                                                  "written to out, same lane layout, same rotating sets",
+                     "frac_of_stream_mix_ceiling": round(gbs / mix_gbs, 4),
+                     "reads_only_GBps": round(smix["reads8_only"]["GBps"], 1),
                      "copy_ceiling_GBps": round(copy_gbs, 1),
                      "copy_ceiling_kernel": "param_contig<4, false>: all_gather_into_tensor of one 256 MiB shard",
                      "frac_of_copy_ceiling": round(gbs / copy_gbs, 4)},

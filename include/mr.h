@@ -37,6 +37,7 @@ typedef int mr_status;
 #define MR_ERR_ALIAS (-3)       /* output partially overlaps an input */
 #define MR_ERR_WORKSPACE (-4)   /* two-shot workspace missing, too small, or barrier error seen */
 #define MR_ERR_HIP (-5)         /* a HIP runtime call failed; see mr_last_hip_error() */
+#define MR_ERR_ENGINE (-6)      /* SDMA copy engines unavailable or a copy failed; see mr_last_hip_error() */
 
 typedef enum mr_dtype { MR_BF16 = 0, MR_FP16 = 1, MR_FP32 = 2, MR_INT32 = 3 } mr_dtype;
 typedef enum mr_mode { MR_ONESHOT = 0, MR_TWOSHOT = 1 } mr_mode;
@@ -48,7 +49,8 @@ typedef enum mr_mode { MR_ONESHOT = 0, MR_TWOSHOT = 1 } mr_mode;
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mr_status_string(mr_status status);
 
-/* hipError_t value behind the calling thread's most recent MR_ERR_HIP (0 if none). */
+/* hipError_t value behind the calling thread's most recent MR_ERR_HIP, or for MR_ERR_ENGINE the HSA
+ * runtime's hsa_status_t (or -1: an engine reported a failed copy); 0 if none. */
 int mr_last_hip_error(void);
 
 /*
@@ -110,6 +112,29 @@ mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dt
  */
 mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, const uint64_t* splits,
                                     int P, mr_dtype dtype, void* out, mr_stream stream);
+
+/*
+ * mr_allgather_param_contig_sdma -- mr_allgather_param_contig's placement, copied by the GPU's SDMA
+ * engines instead of its compute units.
+ *
+ * The mori page's hierarchical all-gather moves intra-node data on copy engines so that a concurrent
+ * GEMM keeps the compute units (page "ccl: hierarchical cross-node AllGather (intra-node SDMA +
+ * inter-node RDMA) #441", PR summary: copy engines against CU contention).  Here every (parameter,
+ * rank) piece -- src[r*T + O_s .. + splits[s]) to out[O_s*W + r*splits[s] ..) -- is one 1-D engine copy
+ * (pieces above 4 MiB are cut), spread over every SDMA engine the device reports.  Output bits are
+ * those of mr_allgather_param_contig.
+ *
+ * Arguments, limits and errors as mr_allgather_param_contig, plus MR_ERR_ENGINE.  Unlike every other
+ * entry point this call is synchronous: it waits until `stream` has finished its earlier work (the
+ * engines are not ordered by the stream), then copies, and returns once every copy is complete; work
+ * enqueued on any stream afterwards sees the result.  Not capturable in a HIP graph.
+ *
+ * mr_sdma_engines: number of SDMA engines the current device offers for its own memory; 0 if none or
+ * the HSA runtime is unavailable, and then mr_last_hip_error() gives the HSA runtime's hsa_status_t.
+ */
+mr_status mr_allgather_param_contig_sdma(const void* src_rank_major, int W, int G, const uint64_t* splits, int P,
+                                         mr_dtype dtype, void* out, mr_stream stream);
+int mr_sdma_engines(void);
 
 /*
  * mr_reduce_scatter_chunk / mr_reduce_scatter_sum -- one rank's share of a sum reduce-scatter.
@@ -231,7 +256,8 @@ mr_status mr_set_option(mr_option opt, int64_t value);
 mr_status mr_get_option(mr_option opt, int64_t* value);
 
 /* Library ABI version (major*100 + minor).  1.01 added MR_OPT_TILE_SHAPE, MR_TWOSHOT_SYNC_LAST and
- * MR_TWOSHOT_SYNC_AUTO (the new default hand-off); 1.02 added MR_TILE_WIDE_PAIR. */
+ * MR_TWOSHOT_SYNC_AUTO (the new default hand-off); 1.02 added MR_TILE_WIDE_PAIR; 1.03 added
+ * mr_allgather_param_contig_sdma, mr_sdma_engines and MR_ERR_ENGINE. */
 int mr_version(void);
 
 #ifdef __cplusplus

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mr_version() == 102
+    assert L.mr_version() == 103
     for code, name in mr.STATUS.items():
         assert L.mr_status_string(code).decode().startswith(name)
     assert b"unknown" in L.mr_status_string(-99)
@@ -101,6 +101,24 @@ def test_gather_argument_errors(L):
     # overlap of src and out (W*T*s = 8*48*2 = 768 bytes)
     assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 0, src + 766, None) == EALIAS
     assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 0, src - 766, None) == EALIAS
+
+
+def test_sdma_gather_argument_errors(L):
+    """The copy-engine gather validates exactly like the kernel gather, before touching the stream."""
+    sp = (ctypes.c_uint64 * 3)(8, 16, 24)
+    src, out = 0x100000, 0x800000
+    f = L.mr_allgather_param_contig_sdma
+    assert f(src, 8, 3, sp, 3, 0, out, None) == EINVAL    # G does not divide W
+    assert f(src, 0, 1, sp, 3, 0, out, None) == EINVAL
+    assert f(src, 8, 4, sp, 0, 0, out, None) == EINVAL    # no params
+    assert f(src, 8, 4, None, 3, 0, out, None) == EINVAL
+    assert f(src, 8, 4, sp, 3, 9, out, None) == EINVAL    # unknown dtype
+    assert f(None, 8, 4, sp, 3, 0, out, None) == EINVAL
+    assert f(src + 1, 8, 4, sp, 3, 0, out, None) == EINVAL  # not a multiple of the element size
+    zero = (ctypes.c_uint64 * 2)(0, 0)
+    assert f(None, 8, 4, zero, 2, 0, None, None) == OK     # empty: no-op
+    assert f(src, 8, 4, sp, 3, 0, src + 766, None) == EALIAS
+    assert L.mr_status_string(-6).decode().startswith("MR_ERR_ENGINE")
 
 
 def test_workspace_sizes_and_errors(L):
