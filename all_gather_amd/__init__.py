@@ -40,6 +40,8 @@ _SIGS = {
     "mr_version": (ctypes.c_int, []),
     "mr_allreduce_sum": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t,
                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
+    "mr_allreduce_sum_noalloc": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t,
+                                                ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
     "mr_allgather_param_contig": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                                  ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_void_p, ctypes.c_void_p]),
@@ -160,6 +162,25 @@ def prepare_allreduce(bufs: Sequence, out, mode: str = "oneshot", stream=None):
 def allreduce_sum(bufs: Sequence, out, mode: str = "oneshot", stream=None):
     """out = elementwise fp32 sum (rank order 0..W-1) of the W same-shape, same-dtype tensors ``bufs``."""
     prepare_allreduce(bufs, out, mode, stream)()
+    return out
+
+
+NOALLOC_MAX_BYTES = 32 << 20
+
+
+def prepare_allreduce_noalloc(bufs: Sequence, out, mode: str = "oneshot", stream=None):
+    """Pre-marshalled mr_allreduce_sum_noalloc (two-shot workspace inside the library; never allocates)."""
+    _dev_tensor(out, "out")
+    _same(bufs, out, "rank buffer", out.numel())
+    ptrs = (ctypes.c_void_p * max(len(bufs), 1))(*[b.data_ptr() for b in bufs])
+    args = (ptrs, len(bufs), out.numel(), DTYPE_CODE[dtype_name(out)], out.data_ptr(), MODE_CODE[mode],
+            _stream_handle(stream))
+    return _prepared("mr_allreduce_sum_noalloc", lib().mr_allreduce_sum_noalloc, args, (ptrs, list(bufs), out))
+
+
+def allreduce_sum_noalloc(bufs: Sequence, out, mode: str = "oneshot", stream=None):
+    """allreduce_sum without any device allocation (rank buffers up to NOALLOC_MAX_BYTES)."""
+    prepare_allreduce_noalloc(bufs, out, mode, stream)()
     return out
 
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmr.so")
-SOURCES = ["api.hip", "reduce_kernels.hip", "gather_kernels.hip", "probe_kernels.hip", "sdma.hip"]
+SOURCES = ["api.hip", "reduce_kernels.hip", "gather_kernels.hip", "probe_kernels.hip", "sdma.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # Device flags: no fast-math and no contraction (the sums must be plain fp32 RNE adds in order),

@@ -118,8 +118,12 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
 // ------------------------------------------------------------------------------------ reduce launch
 // Alias check, 16-byte layout of the call, and the one-shot or two-shot launch.  `ins` are already
 // validated non-null.
+// `fixed`: a workspace the call must use instead of the stream's (the no-allocation entry point);
+// `wait_free`: take only the two-shot hand-offs that leave every barrier word and flag at zero when a
+// launch ends and never produce an invalid output (the last arriver, which never waits, and the
+// XCD-local units, which recompute instead of failing).
 mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype, char* out, mr_mode mode,
-                        hipStream_t st) {
+                        hipStream_t st, const Workspace* fixed = nullptr, bool wait_free = false) {
   const int es = mr::elem_size(dtype);
   const size_t nbytes = n * static_cast<size_t>(es);
   const uintptr_t po = reinterpret_cast<uintptr_t>(out);
@@ -149,15 +153,25 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
                    static_cast<int>(dtype), sh.vec, sh.head, sh.npacks, shape);
     e = mr::launch_oneshot(in, W, dtype, out, sh, shape, st);
   } else {
-    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, mr::twoshot_sync_for(n * static_cast<size_t>(es), g_twoshot_sync.load()),
-                                                 g_spin_limit.load(), g_tile_shape.load());
+    uint32_t sync = mr::twoshot_sync_for(n * static_cast<size_t>(es), g_twoshot_sync.load());
+    uint32_t shape = g_tile_shape.load();
+    if (wait_free) {
+      shape = mr::kShapeAuto;
+      sync = mr::twoshot_xcd_units(sh.vec, W, sh.npacks, mr::kSyncTile, shape) ? mr::kSyncTile : mr::kSyncLast;
+    }
+    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, sync, g_spin_limit.load(), shape);
     const uint64_t grid = pl.xcd ? uint64_t{mr::kXcds} * (pl.run_padded + pl.run_padded / mr::kXcdGroup)
                                  : static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
     if (grid >= (1ull << 24)) return MR_ERR_INVALID_ARG;
     const size_t flags_needed = pl.xcd ? pl.units : static_cast<size_t>(pl.chunks) * pl.t1;
     Workspace ws;
-    mr_status s = get_workspace(st, n, es, flags_needed, &ws);
-    if (s != MR_OK) return s;
+    if (fixed) {
+      if (!ws_fits(fixed->bytes, n, es, flags_needed)) return MR_ERR_WORKSPACE;
+      ws = *fixed;
+    } else {
+      mr_status s = get_workspace(st, n, es, flags_needed, &ws);
+      if (s != MR_OK) return s;
+    }
     // the stage shares out's 16-byte phase so that its body is 16-byte aligned too
     char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (sh.vec ? (po & 15u) : 0);
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws.base + mr::kCtrlBytes);
@@ -312,6 +326,43 @@ mr_status gather_launch(const GatherPlan& gp, Bind bind, bool realign, hipStream
 
 }  // namespace
 
+namespace mr {
+
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+
+size_t workspace_bytes_for(size_t n, int esize) { return ws_bytes_for(n, esize); }
+
+hipError_t clear_workspace_words(char* base, size_t bytes, hipStream_t st) { return ws_clear(base, bytes, st); }
+
+mr_status check_allreduce_args(const void* const* bufs, int W, size_t n, mr_dtype dtype, const void* out, mr_mode mode) {
+  if (W < 1 || W > MR_MAX_W) return MR_ERR_INVALID_ARG;
+  if (mode != MR_ONESHOT && mode != MR_TWOSHOT) return MR_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
+  if (!is_float(dtype)) return MR_ERR_DTYPE;
+  if (n == 0) return MR_OK;
+  if (!bufs || !out) return MR_ERR_INVALID_ARG;
+  const int es = elem_size(dtype);
+  if (n > (SIZE_MAX / 2 - kCtrlBytes) / static_cast<size_t>(es)) return MR_ERR_INVALID_ARG;
+  if (!elem_aligned(out, es)) return MR_ERR_INVALID_ARG;
+  for (int r = 0; r < W; ++r)
+    if (!bufs[r] || !elem_aligned(bufs[r], es)) return MR_ERR_INVALID_ARG;
+  return MR_OK;
+}
+
+mr_status allreduce_in_workspace(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out, mr_mode mode,
+                                 hipStream_t st, char* ws_base, size_t ws_bytes) {
+  const mr_status s = check_allreduce_args(bufs, W, n, dtype, out, mode);
+  if (s != MR_OK || n == 0) return s;
+  const char* ins[MR_MAX_W];
+  for (int r = 0; r < W; ++r) ins[r] = static_cast<const char*>(bufs[r]);
+  Workspace ws;
+  ws.base = ws_base;
+  ws.bytes = ws_bytes;
+  return reduce_launch(ins, W, n, dtype, static_cast<char*>(out), mode, st, &ws, true);
+}
+
+}  // namespace mr
+
 extern "C" {
 
 const char* mr_status_string(mr_status s) {
@@ -369,20 +420,10 @@ mr_status mr_get_option(mr_option opt, int64_t* value) {
 
 mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out, mr_mode mode,
                            mr_stream stream) {
-  if (W < 1 || W > MR_MAX_W) return MR_ERR_INVALID_ARG;
-  if (mode != MR_ONESHOT && mode != MR_TWOSHOT) return MR_ERR_INVALID_ARG;
-  if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
-  if (!is_float(dtype)) return MR_ERR_DTYPE;
-  if (n == 0) return MR_OK;
-  if (!bufs || !out) return MR_ERR_INVALID_ARG;
-  const int es = mr::elem_size(dtype);
-  if (n > (SIZE_MAX / 2 - mr::kCtrlBytes) / static_cast<size_t>(es)) return MR_ERR_INVALID_ARG;
-  if (!elem_aligned(out, es)) return MR_ERR_INVALID_ARG;
+  const mr_status s = mr::check_allreduce_args(bufs, W, n, dtype, out, mode);
+  if (s != MR_OK || n == 0) return s;
   const char* ins[MR_MAX_W];
-  for (int r = 0; r < W; ++r) {
-    if (!bufs[r] || !elem_aligned(bufs[r], es)) return MR_ERR_INVALID_ARG;
-    ins[r] = static_cast<const char*>(bufs[r]);
-  }
+  for (int r = 0; r < W; ++r) ins[r] = static_cast<const char*>(bufs[r]);
   return reduce_launch(ins, W, n, dtype, static_cast<char*>(out), mode, reinterpret_cast<hipStream_t>(stream));
 }
 

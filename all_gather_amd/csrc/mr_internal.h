@@ -141,6 +141,16 @@ hipError_t launch_twoshot(const RankPtrs& in, int W, mr_dtype dt, char* out, cha
 TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit, uint32_t shape);
 hipError_t launch_zero_words(void* p, size_t words, hipStream_t st);
 
+// Host-side helpers of api.hip shared with the no-allocation entry point (noalloc.hip).
+void set_last_hip_error(int e);
+size_t workspace_bytes_for(size_t n, int esize);  // a workspace that holds a two-shot call of n elements
+hipError_t clear_workspace_words(char* base, size_t bytes, hipStream_t st);  // barrier words and flags
+mr_status check_allreduce_args(const void* const* bufs, int W, size_t n, mr_dtype dtype, const void* out, mr_mode mode);
+// mr_allreduce_sum with the two-shot workspace given (never allocated) and only the hand-offs that leave
+// it clean after every launch
+mr_status allreduce_in_workspace(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out, mr_mode mode,
+                                 hipStream_t st, char* ws_base, size_t ws_bytes);
+
 // ---------------------------------------------------------------------------------- param-contiguous
 constexpr int kMaxParams = MR_MAX_PARAMS_PER_LAUNCH;
 #ifndef MR_GATHER_TILE

@@ -157,6 +157,29 @@ mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dty
                                 mr_stream stream);
 
 /*
+ * mr_allreduce_sum_noalloc -- mr_allreduce_sum that never allocates device memory, for callers that
+ * cannot allocate: code under HIP graph capture, serving loops that must not allocate, harnesses that
+ * forbid it.
+ *
+ * Same arguments, result bits and errors as mr_allreduce_sum, with these differences:
+ *  - the two-shot workspace is a device array inside the library (MR_NOALLOC_MAX_BYTES of stage plus
+ *    the barrier words, about 34 MiB per GPU), held by each GPU the library runs on until the process
+ *    ends; the first call on a device looks its address up and clears it on `stream`;
+ *  - a rank buffer larger than MR_NOALLOC_MAX_BYTES (n * element size) -> MR_ERR_WORKSPACE, nothing
+ *    enqueued;
+ *  - the two-shot hand-off is always chosen from the message size (the last arriver below 16 MiB per
+ *    rank buffer, the XCD-local units from 16 MiB on the 16-byte path with W <= 8), ignoring
+ *    MR_OPT_TWOSHOT_SYNC and MR_OPT_TILE_SHAPE, because those hand-offs never leave a barrier word set
+ *    after a launch and never produce an invalid output; there is no error word to check;
+ *  - every call on one GPU shares that GPU's array: two-shot calls that overlap in time on one GPU (on
+ *    two streams, or from two host threads) race and give undefined output.  One-shot calls use no
+ *    workspace and never race.
+ */
+#define MR_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+mr_status mr_allreduce_sum_noalloc(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out,
+                                   mr_mode mode, mr_stream stream);
+
+/*
  * All-gathers from W separate rank shards (each a device buffer of T elements), one launch each.
  * Bit copies of any dtype; 1 <= W <= MR_MAX_TABLE_W; shards may not overlap any output (MR_ERR_ALIAS).
  * Every shard and output pointer must be a multiple of the element size (else MR_ERR_INVALID_ARG).

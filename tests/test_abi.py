@@ -103,6 +103,20 @@ def test_gather_argument_errors(L):
     assert L.mr_allgather_param_contig(src, 8, 4, sp, 3, 0, src - 766, None) == EALIAS
 
 
+def test_noalloc_reduce_argument_errors(L):
+    """The no-allocation reduce validates like mr_allreduce_sum and refuses rank buffers over its limit
+    before any HIP call."""
+    f = L.mr_allreduce_sum_noalloc
+    a, b = 0x1000000, 0x9000000
+    assert f(_ptrs(a, b), 0, 16, 0, 0x20000000, 1, None) == EINVAL
+    assert f(_ptrs(a, b), 2, 16, 3, 0x20000000, 1, None) == EDTYPE
+    assert f(_ptrs(a, b), 2, 16, 0, 0x20000000, 7, None) == EINVAL
+    assert f(None, 2, 0, 0, None, 1, None) == OK
+    limit = mr.NOALLOC_MAX_BYTES
+    assert f(_ptrs(a, b), 2, limit // 2 + 1, 0, 0x40000000, 1, None) == EWS     # bf16, one element over
+    assert f(_ptrs(a, b), 2, limit // 4 + 1, 2, 0x40000000, 0, None) == EWS     # fp32, one-shot too
+
+
 def test_sdma_gather_argument_errors(L):
     """The copy-engine gather validates exactly like the kernel gather, before touching the stream."""
     sp = (ctypes.c_uint64 * 3)(8, 16, 24)
