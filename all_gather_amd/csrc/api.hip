@@ -8,6 +8,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -55,11 +56,18 @@ struct Workspace {
   bool owned = false;
 };
 
+// Workspaces by (device, stream, capture id).  Capture id 0 is the stream's own workspace (eager calls,
+// and caller-owned memory bound with mr_set_workspace); a call made while the stream is being captured
+// into a HIP graph gets a library-owned workspace of that capture, so graphs captured one after
+// another on one stream (torch.cuda.graph captures every graph on one shared stream) never share
+// barrier words and may be replayed at the same time on different streams.
+using WsKey = std::tuple<int, hipStream_t, unsigned long long>;
 std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-// Library-owned buffers that a larger workspace replaced.  Launches still in flight, and HIP graphs
-// that captured a two-shot call, may point at them, so they are freed only when the caller unbinds the
-// stream's workspace (mr_set_workspace).  Growth at least doubles, so they total less than the live one.
+std::map<WsKey, Workspace> g_ws;
+// Library-owned buffers that a larger workspace replaced, by (device, stream).  Launches still in
+// flight, and HIP graphs that captured a two-shot call, may point at them, so they are freed only when
+// the caller unbinds the stream's workspace (mr_set_workspace).  Growth at least doubles, so they total
+// less than the live one.
 std::map<std::pair<int, hipStream_t>, std::vector<char*>> g_retired;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -87,8 +95,21 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  unsigned long long capture = 0;
+  e = hipStreamGetCaptureInfo(st, &cs, &capture);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cs != hipStreamCaptureStatusActive) capture = 0;
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  Workspace& w = g_ws[{dev, st}];
+  if (capture) {  // caller-owned memory bound to the stream is used for captured calls too
+    auto own = g_ws.find(WsKey{dev, st, 0});
+    if (own != g_ws.end() && own->second.base && !own->second.owned) {
+      if (!ws_fits(own->second.bytes, n, esize, flags)) return MR_ERR_WORKSPACE;
+      *out = own->second;
+      return MR_OK;
+    }
+  }
+  Workspace& w = g_ws[WsKey{dev, st, capture}];
   if (w.base && ws_fits(w.bytes, n, esize, flags)) {
     *out = w;
     return MR_OK;
@@ -99,7 +120,17 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
   if (w.base && bytes < 2 * w.bytes) bytes = 2 * w.bytes;
   if (!ws_fits(bytes, n, esize, flags)) return MR_ERR_WORKSPACE;  // the sizing rule covers every plan
   void* p = nullptr;
-  e = hipMalloc(&p, bytes);
+  if (capture) {
+    // an allocation is not a stream operation: allowed inside a capture once this thread's capture mode
+    // is relaxed for the call (the clear below is a kernel, recorded into the graph before the reduce)
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    e = hipThreadExchangeStreamCaptureMode(&mode);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMalloc(&p, bytes);
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
+  } else {
+    e = hipMalloc(&p, bytes);
+  }
   if (e != hipSuccess) return hip_fail(e);
   e = ws_clear(static_cast<char*>(p), bytes, st);
   if (e != hipSuccess) {
@@ -593,25 +624,34 @@ mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  Workspace& w = g_ws[{dev, st}];
-  std::vector<char*>& old = g_retired[{dev, st}];
-  if ((w.base && w.owned) || !old.empty()) {  // free every library-owned buffer of this stream
+  // every library-owned buffer of this stream: its own workspace, those of captures made on it, and
+  // the ones growth replaced
+  std::vector<char*> owned = std::move(g_retired[{dev, st}]);
+  g_retired.erase({dev, st});
+  for (auto it = g_ws.begin(); it != g_ws.end();) {
+    if (std::get<0>(it->first) == dev && std::get<1>(it->first) == st) {
+      if (it->second.base && it->second.owned) owned.push_back(it->second.base);
+      it = g_ws.erase(it);
+    } else {
+      ++it;
+    }
+  }
+  if (!owned.empty()) {
     e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e);
+    if (e != hipSuccess) {
+      g_retired[{dev, st}] = std::move(owned);  // nothing freed; the stream is left unbound
+      return hip_fail(e);
+    }
     // every buffer is released even if one free fails; the first failure is reported and the stream is
     // left unbound (the buffers are dropped either way, never freed twice)
-    hipError_t fe = (w.base && w.owned) ? hipFree(w.base) : hipSuccess;
-    for (char* b : old) {
+    hipError_t fe = hipSuccess;
+    for (char* b : owned) {
       const hipError_t f = hipFree(b);
       if (fe == hipSuccess) fe = f;
     }
-    old.clear();
-    if (fe != hipSuccess) {
-      w = Workspace{};
-      return hip_fail(fe);
-    }
+    if (fe != hipSuccess) return hip_fail(fe);
   }
-  w = Workspace{};
+  Workspace& w = g_ws[WsKey{dev, st, 0}];
   if (!dev_ptr) return MR_OK;
   e = ws_clear(static_cast<char*>(dev_ptr), bytes, st);
   if (e != hipSuccess) return hip_fail(e);
@@ -627,23 +667,29 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
-  Workspace w;
+  std::vector<Workspace> ws;  // the stream's own workspace and those of captures made on it
   {
     std::lock_guard<std::mutex> lk(g_ws_mu);
-    auto it = g_ws.find({dev, st});
-    if (it == g_ws.end() || !it->second.base) return MR_ERR_WORKSPACE;
-    w = it->second;
+    for (const auto& kv : g_ws)
+      if (std::get<0>(kv.first) == dev && std::get<1>(kv.first) == st && kv.second.base) ws.push_back(kv.second);
+  }
+  if (ws.empty()) return MR_ERR_WORKSPACE;
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  uint32_t all = 0;
+  for (const Workspace& w : ws) {
+    uint32_t err = 0;
+    e = hipMemcpy(&err, w.base + offsetof(mr::Ctrl, err), sizeof(err), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+    all |= err;
+    // clear the error word and every barrier word and flag (each launch re-arms them itself; this
+    // also resets a workspace that a caller's own kernels may have written)
+    e = ws_clear(w.base, w.bytes, st);
+    if (e != hipSuccess) return hip_fail(e);
   }
   e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e);
-  uint32_t err = 0;
-  e = hipMemcpy(&err, w.base + offsetof(mr::Ctrl, err), sizeof(err), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(e);
-  *flags = err;
-  // clear the error bit and re-arm every barrier word and flag (a timed-out call may leave counts)
-  e = ws_clear(w.base, w.bytes, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return hip_fail(e);
+  *flags = all;
   return MR_OK;
 }
 

@@ -391,16 +391,18 @@ __device__ __forceinline__ void publish_phase1(Ctrl* ctrl, uint32_t* flags, cons
   __syncthreads();
   if (threadIdx.x == 0 && pl.sync != kSyncLast) {
     if (pl.sync == kSyncTile)
-      __hip_atomic_store(&flags[static_cast<size_t>(c) * pl.t1 + k], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&flags[static_cast<size_t>(c) * pl.t1 + k], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else  // chunk and grid barriers count per chunk (W words instead of one contended word)
       __hip_atomic_fetch_add(&ctrl->done1[c][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Thread 0 polls `word` until it reaches `target`; false if it gave up.
+// Thread 0 polls `word` until it reaches `target` (compared as signed: a word a consumer has already
+// given back reads negative until its late producer arrives); false if it gave up.
 __device__ __forceinline__ bool wait_at_least(uint32_t* word, uint32_t target, uint32_t spin_limit) {
   uint32_t spins = 0;
-  while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+  while (static_cast<int32_t>(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
+         static_cast<int32_t>(target)) {
     __builtin_amdgcn_s_sleep(1);
     if (++spins > spin_limit) return false;
   }
@@ -415,7 +417,9 @@ __device__ __forceinline__ void wait_phase1(Ctrl* ctrl, uint32_t* flags, const T
       uint32_t* f = &flags[static_cast<size_t>(c) * pl.t1 + j];
       if (!wait_at_least(f, 1u, pl.spin_limit))
         __hip_atomic_fetch_or(&ctrl->err[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // consumed: re-arm
+      // consumed: give the release back.  After a timeout this leaves -1, and the late producer's +1
+      // (still inside this launch) brings the flag back to zero, so it cannot satisfy a later launch.
+      __hip_atomic_fetch_sub(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else if (pl.sync == kSyncChunk) {
     if (threadIdx.x == 0 && !wait_at_least(&ctrl->done1[c][0], pl.t1, pl.spin_limit))
@@ -429,14 +433,18 @@ __device__ __forceinline__ void wait_phase1(Ctrl* ctrl, uint32_t* flags, const T
 }
 
 // End of a workgroup's two-shot work (k = its ticket).  Chunk barrier: the last phase-2 tile of chunk c
-// clears that chunk's words.  Grid barrier: every workgroup counts itself out, and the last one clears
-// the pools and counters of every chunk (no workgroup can still be claiming work then).
+// re-arms that chunk's words.  Grid barrier: every workgroup counts itself out, and the last one re-arms
+// the pools and counters of every chunk (no workgroup can still be claiming work then).  The words that
+// only count with returning atomics (pools, done2, gdone) have seen every increment of the launch and
+// are stored to zero; the release counts done1 get non-returning increments, which may still be in
+// flight (or, after a timeout, still to come), so t1 is subtracted instead: the count reaches zero once
+// every phase-1 tile of the launch has released, in whatever order the atomics land.
 __device__ __forceinline__ void finish_twoshot(Ctrl* ctrl, const TwoShotPlan& pl, uint32_t c, uint32_t k) {
   if (threadIdx.x != 0) return;
   if (pl.sync == kSyncChunk && k >= pl.t1) {
     const uint32_t d = __hip_atomic_fetch_add(&ctrl->done2[c][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == pl.t2 - 1) {
-      __hip_atomic_store(&ctrl->done1[c][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_sub(&ctrl->done1[c][0], pl.t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&ctrl->done2[c][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else if (pl.sync == kSyncGrid) {
@@ -444,7 +452,7 @@ __device__ __forceinline__ void finish_twoshot(Ctrl* ctrl, const TwoShotPlan& pl
     if (d == pl.chunks * (pl.t1 + pl.t2) - 1) {
       for (uint32_t x = 0; x < pl.chunks; ++x) {
         __hip_atomic_store(&ctrl->claim[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ctrl->done1[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_sub(&ctrl->done1[x][0], pl.t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&ctrl->done2[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __hip_atomic_store(&ctrl->gdone[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -35,7 +35,7 @@ typedef int mr_status;
 #define MR_ERR_INVALID_ARG (-1) /* null or misaligned pointer, W/G/P out of range, size overflow */
 #define MR_ERR_DTYPE (-2)       /* dtype not supported by this operation */
 #define MR_ERR_ALIAS (-3)       /* output partially overlaps an input */
-#define MR_ERR_WORKSPACE (-4)   /* two-shot workspace missing, too small, or barrier error seen */
+#define MR_ERR_WORKSPACE (-4)   /* two-shot workspace missing or too small (barrier errors: mr_workspace_check) */
 #define MR_ERR_HIP (-5)         /* a HIP runtime call failed; see mr_last_hip_error() */
 #define MR_ERR_ENGINE (-6)      /* SDMA copy engines unavailable or a copy failed; see mr_last_hip_error() */
 
@@ -206,12 +206,23 @@ mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int
  * Two-shot workspace.
  *
  * By default the library allocates, on first two-shot use of a (device, stream) pair, a grow-only
- * workspace of at least mr_workspace_bytes() bytes holding the stage buffer and the barrier words;
- * that first call (and a call that grows it) allocates and is therefore not safe under graph capture.
+ * workspace of at least mr_workspace_bytes() bytes holding the stage buffer and the barrier words.
  * Growth at least doubles the size and keeps the replaced buffer alive, so launches in flight and HIP
  * graphs that captured a two-shot call on the stream stay valid; replaced buffers are freed only by
- * mr_set_workspace on that stream.  One workspace per (device, stream): two-shot calls on different
- * streams never share barrier words.
+ * mr_set_workspace on that stream.  One workspace per (device, stream): eager two-shot calls on
+ * different streams never share barrier words.
+ *
+ * A two-shot call made while its stream is being captured into a HIP graph uses a library-owned
+ * workspace of that capture (device, stream, capture id), allocated during the capture with this
+ * thread's capture mode relaxed for the allocation and cleared by a kernel recorded into the graph.  So
+ * graphs captured one after another on one stream -- torch.cuda.graph captures every graph on one
+ * shared stream -- never share barrier words, and may be replayed at the same time on different
+ * streams.  Two replays of the same graph that overlap in time do share its workspace and race.  These
+ * workspaces live until mr_set_workspace is called on the capture stream (destroy the graphs first).
+ * Caller-owned memory bound with mr_set_workspace is used for captured calls too.
+ *
+ * Every launch returns its barrier words and flags to zero before it ends, also when a bounded wait
+ * gave up (the call that timed out has invalid output; later calls are unaffected).
  *
  * mr_workspace_bytes: bytes a caller-owned workspace needs for a two-shot call of this shape.
  * mr_set_workspace:   bind caller-owned device memory (256-byte aligned) as the workspace of `stream`
@@ -220,14 +231,17 @@ mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int
  *                     stage -> MR_ERR_INVALID_ARG; a bound workspace too small for a later call makes
  *                     that call return MR_ERR_WORKSPACE.  dev_ptr == NULL unbinds (the library
  *                     allocates again on next use).  Either way it synchronises `stream` and frees
- *                     every library-owned workspace buffer of the stream, so a graph that captured a
- *                     two-shot call on it must not be replayed afterwards.  If a free fails, the
- *                     call returns MR_ERR_HIP and leaves the stream with no workspace bound.  Not
- *                     thread-safe against concurrent calls on that stream.
- * mr_workspace_check: synchronises `stream`, then reads and clears the barrier error word of its
- *                     workspace.  *flags receives it (0 = no error; bit 0 = a phase-2 block gave up
- *                     waiting for phase 1, so that call's output is not valid).  Returns
- *                     MR_ERR_WORKSPACE if there is no workspace for the stream.
+ *                     every library-owned workspace buffer of the stream (its captures' included), so
+ *                     a graph that captured a two-shot call on it must not be replayed afterwards.
+ *                     If a free fails, the call returns MR_ERR_HIP and leaves the stream with no
+ *                     workspace bound.  Not thread-safe against concurrent calls on that stream.
+ * mr_workspace_check: synchronises `stream`, then reads and clears the barrier error words of its
+ *                     workspaces (its own and those of graphs captured on it).  *flags receives their
+ *                     OR: 0 = no error; bit 0 = a phase-2 workgroup gave up waiting for phase 1, so
+ *                     that call's output is not valid; bits 1 and 2 = the XCD-local two-shot
+ *                     recomputed units from the rank buffers (after a wait gave up / because a
+ *                     unit's producer ran on another XCD), output valid.  Returns MR_ERR_WORKSPACE if
+ *                     there is no workspace for the stream.
  */
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype);
 mr_status mr_set_workspace(mr_stream stream, void* dev_ptr, size_t bytes);

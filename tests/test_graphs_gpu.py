@@ -127,3 +127,43 @@ def test_twoshot_graph_replays_after_the_workspace_grew():
     assert mr.workspace_check(s) == 0
     del g
     mr.set_workspace(None, stream=s)  # frees the live and the replaced buffers of this stream
+
+
+@pytest.mark.parametrize("mode", ["twoshot", "twoshot:tile", "twoshot:last", "twoshot:chunk"])
+def test_graphs_captured_on_one_stream_replay_together(mode):
+    """Two two-shot calls captured into two graphs on the same capture stream (torch.cuda.graph's default
+    shares one), replayed at the same time on two different streams with different inputs.  Each
+    capture has its own workspace, so the replays cannot hand each other's workgroups tickets, flags or
+    stage bytes; every replay must match the oracle, and the capture workspaces' error words (read by
+    mr_workspace_check on the capture stream) must stay clear."""
+    W, n = 8, 8_388_608 + 16
+    kind, _, sync = mode.partition(":")
+    cap = torch.cuda.Stream()
+    sets = [[torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(W)] for _ in range(2)]
+    outs = [torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(2)]
+    if sync:
+        mr.set_option("twoshot_sync", sync)
+    try:
+        graphs = [_capture(lambda k=k: mr.allreduce_sum(sets[k], outs[k], mode=kind), cap) for k in range(2)]
+        run = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for rep in range(4):
+            wants = []
+            for k in range(2):
+                bufs = workloads.rank_buffers(120 + 2 * rep + k, W, n, "bf16", "normal")
+                for d, b in zip(sets[k], bufs):
+                    d.copy_(to_dev(b, "bf16"))
+                outs[k].fill_(0)
+                wants.append(oracle.allreduce_sum_ref(bufs, "bf16"))
+            torch.cuda.synchronize()
+            for k in range(2):
+                with torch.cuda.stream(run[k]):
+                    graphs[k].replay()
+            torch.cuda.synchronize()
+            for k in range(2):
+                assert_reduce_equal(to_bits(outs[k]), wants[k], "bf16", f"{mode} rep {rep} graph {k}")
+        assert mr.workspace_check(cap) == 0
+        del graphs
+        torch.cuda.synchronize()
+        mr.set_workspace(None, cap)  # frees the capture workspaces of the stream
+    finally:
+        mr.set_option("twoshot_sync", "auto")
