@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "mr_internal.h"
+#include "mr_probe.h"
 
 namespace {
 
@@ -147,6 +148,34 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
 
 
 // ------------------------------------------------------------------------------------ reduce launch
+// 16-byte layout of a reduce call: element-wise head up to out's 16-byte boundary, packs, element-wise
+// tail; everything element-wise when the pointers do not share one 16-byte phase.
+mr::ReduceShape reduce_shape(size_t n, int es, uintptr_t po, bool same_phase) {
+  mr::ReduceShape sh{};
+  sh.n = n;
+  sh.vec = same_phase ? 1 : 0;
+  if (sh.vec) {
+    const size_t V = 16 / static_cast<size_t>(es);
+    size_t head = ((16u - (po & 15u)) & 15u) / static_cast<size_t>(es);
+    if (head > n) head = n;
+    sh.head = head;
+    sh.npacks = (n - head) / V;
+  }
+  return sh;
+}
+
+// The two-shot plan of a call under the given options (wait_free: see reduce_launch).
+mr::TwoShotPlan twoshot_plan_for(int W, const mr::ReduceShape& sh, int es, uint32_t sync_opt, uint32_t shape_opt,
+                                 bool wait_free) {
+  uint32_t sync = mr::twoshot_sync_for(sh.n * static_cast<size_t>(es), sync_opt);
+  uint32_t shape = shape_opt;
+  if (wait_free) {
+    shape = mr::kShapeAuto;
+    sync = mr::twoshot_xcd_units(sh.vec, W, sh.npacks, mr::kSyncTile, shape) ? mr::kSyncTile : mr::kSyncLast;
+  }
+  return mr::plan_twoshot(W, sh, sync, g_spin_limit.load(), shape);
+}
+
 // Alias check, 16-byte layout of the call, and the one-shot or two-shot launch.  `ins` are already
 // validated non-null.
 // `fixed`: a workspace the call must use instead of the stream's (the no-allocation entry point);
@@ -166,16 +195,7 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
     if ((pr & 15u) != (po & 15u)) same_phase = false;
     in.p[r] = ins[r];
   }
-  mr::ReduceShape sh{};
-  sh.n = n;
-  sh.vec = same_phase ? 1 : 0;
-  if (sh.vec) {
-    const size_t V = 16 / static_cast<size_t>(es);
-    size_t head = ((16u - (po & 15u)) & 15u) / static_cast<size_t>(es);
-    if (head > n) head = n;
-    sh.head = head;
-    sh.npacks = (n - head) / V;
-  }
+  const mr::ReduceShape sh = reduce_shape(n, es, po, same_phase);
   hipError_t e;
   if (mode == MR_ONESHOT) {
     const uint32_t shape = mr::oneshot_shape(sh.npacks, es, g_tile_shape.load());
@@ -184,13 +204,7 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
                    static_cast<int>(dtype), sh.vec, sh.head, sh.npacks, shape);
     e = mr::launch_oneshot(in, W, dtype, out, sh, shape, st);
   } else {
-    uint32_t sync = mr::twoshot_sync_for(n * static_cast<size_t>(es), g_twoshot_sync.load());
-    uint32_t shape = g_tile_shape.load();
-    if (wait_free) {
-      shape = mr::kShapeAuto;
-      sync = mr::twoshot_xcd_units(sh.vec, W, sh.npacks, mr::kSyncTile, shape) ? mr::kSyncTile : mr::kSyncLast;
-    }
-    const mr::TwoShotPlan pl = mr::plan_twoshot(W, sh, sync, g_spin_limit.load(), shape);
+    const mr::TwoShotPlan pl = twoshot_plan_for(W, sh, es, g_twoshot_sync.load(), g_tile_shape.load(), wait_free);
     const uint64_t grid = pl.xcd ? uint64_t{mr::kXcds} * (pl.run_padded + pl.run_padded / mr::kXcdGroup)
                                  : static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
     if (grid >= (1ull << 24)) return MR_ERR_INVALID_ARG;
@@ -547,6 +561,39 @@ mr_status mr_allgather_param_contig_sdma(const void* src, int W, int G, const ui
     return MR_ERR_ENGINE;
   }
   return MR_OK;
+}
+
+// ------------------------------------------------------------------------ planning hooks (mr_probe.h)
+
+int mrx_twoshot_plan(int W, size_t n, int dtype, uintptr_t out_addr, int same_phase, int sync_opt, int shape_opt,
+                     int wait_free, uint64_t* f, int nf) {
+  if (W < 1 || W > MR_MAX_W || !is_float(static_cast<mr_dtype>(dtype)) || !f || nf < 16) return -1;
+  const int es = mr::elem_size(static_cast<mr_dtype>(dtype));
+  const mr::ReduceShape sh = reduce_shape(n, es, out_addr, same_phase != 0);
+  const mr::TwoShotPlan pl = twoshot_plan_for(W, sh, es, static_cast<uint32_t>(sync_opt), static_cast<uint32_t>(shape_opt),
+                                              wait_free != 0);
+  const uint64_t grid = pl.xcd ? uint64_t{mr::kXcds} * (pl.run_padded + pl.run_padded / mr::kXcdGroup)
+                               : static_cast<uint64_t>(pl.chunks) * (pl.sync == mr::kSyncLast ? pl.t1 : pl.t1 + pl.t2);
+  const uint64_t v[16] = {pl.xcd, pl.units, pl.run, pl.run_padded, pl.chunks, pl.chunk_units, pl.t1, pl.t2, pl.ratio,
+                          pl.unit1, pl.sync, static_cast<uint64_t>(sh.vec), sh.head, sh.npacks, grid,
+                          pl.xcd ? pl.units : static_cast<uint64_t>(pl.chunks) * pl.t1};
+  for (int i = 0; i < 16; ++i) f[i] = v[i];
+  return 0;
+}
+
+int mrx_gather_phase_masks(int W, int G, const uint64_t* splits, int P, int dtype, uint16_t* rm_mask,
+                           uint16_t* rank_masks, int n_rank_masks) {
+  if (W < 1 || W > 65535 || !rm_mask || (n_rank_masks && !rank_masks)) return -1;
+  GatherPlan gp;
+  const mr_status s = gather_plan(W, G, splits, P, static_cast<mr_dtype>(dtype), P > 1, &gp);
+  if (s != MR_OK) return s;
+  *rm_mask = gp.rm_mask;
+  for (int r = 0; r < n_rank_masks; ++r) rank_masks[r] = r < static_cast<int>(gp.rank_mask.size()) ? gp.rank_mask[r] : 0;
+  return 0;
+}
+
+int mrx_needs_realign(uint16_t mask, uint64_t base_difference) {
+  return needs_realign(mask, static_cast<uintptr_t>(base_difference)) ? 1 : 0;
 }
 
 int mr_sdma_engines(void) {

@@ -1,14 +1,17 @@
 /*
- * mr_probe.h -- measurement kernels of libmr that are not part of its C ABI (include/mr.h).
+ * mr_probe.h -- entry points of libmr that are not part of its C ABI (include/mr.h).
  *
- * They bound what the reduce can reach on the machine it runs on, so that a benchmark can report
- * the reduce's rate beside the rate of the plain access pattern it is made of, measured in the same
- * process on the same buffers.
+ * A measurement kernel, which bounds what the reduce can reach on the machine it runs on (so that a
+ * benchmark can report the reduce's rate beside the rate of the plain access pattern it is made of,
+ * measured in the same process on the same buffers), and planning hooks through which host-side tests
+ * check the library's own launch plans against brute force.  None of them launches work except
+ * mrx_stream_mix.
  */
 #ifndef MR_PROBE_H_
 #define MR_PROBE_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -30,6 +33,27 @@ extern "C" {
  * for invalid arguments (nothing is enqueued then).
  */
 int mrx_stream_mix(const void* const* reads, int K, void* out, size_t bytes, int write, void* stream);
+
+/*
+ * mrx_twoshot_plan -- the plan mr_allreduce_sum would launch for a two-shot call: W rank buffers of n
+ * elements of `dtype`, out at address out_addr, all pointers at out's 16-byte phase if same_phase,
+ * options sync_opt / shape_opt (MR_TWOSHOT_SYNC_*, MR_TILE_*), wait_free as mr_allreduce_sum_noalloc.
+ * f[0..15] receive: xcd, units, run, run_padded, chunks, chunk_units, t1, t2, ratio, unit1, sync, vec,
+ * head, npacks, grid (workgroups), flag words used.  Returns 0, or -1 for invalid arguments.
+ */
+int mrx_twoshot_plan(int W, size_t n, int dtype, uintptr_t out_addr, int same_phase, int sync_opt, int shape_opt,
+                     int wait_free, uint64_t* f, int nf);
+
+/*
+ * mrx_gather_phase_masks -- the 16-bit phase masks the gather planner keeps for a split table: bit
+ * (dst_off - src_off) mod 16 of every (parameter, rank) piece, for a rank-major source (*rm_mask) and
+ * for per-rank shard sources (rank_masks[r], r < n_rank_masks, W <= 64).  Returns 0 or an mr_status.
+ * mrx_needs_realign -- whether a mask requires the realigning kernel build for a given source - out
+ * base-address difference.
+ */
+int mrx_gather_phase_masks(int W, int G, const uint64_t* splits, int P, int dtype, uint16_t* rm_mask,
+                           uint16_t* rank_masks, int n_rank_masks);
+int mrx_needs_realign(uint16_t mask, uint64_t base_difference);
 
 #ifdef __cplusplus
 }
