@@ -6,6 +6,7 @@
 #include <cstdlib>
 #include <cstddef>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -150,10 +151,12 @@ mr_status get_workspace(hipStream_t st, size_t n, int esize, size_t flags, Works
 // ------------------------------------------------------------------------------------ reduce launch
 // 16-byte layout of a reduce call: element-wise head up to out's 16-byte boundary, packs, element-wise
 // tail; everything element-wise when the pointers do not share one 16-byte phase.
-mr::ReduceShape reduce_shape(size_t n, int es, uintptr_t po, bool same_phase) {
+mr::ReduceShape reduce_shape(size_t n, int es, uintptr_t po, bool same_phase, bool on_grid = true) {
   mr::ReduceShape sh{};
   sh.n = n;
-  sh.vec = same_phase ? 1 : 0;
+  sh.vec = on_grid ? 1 : 0;
+  sh.realign = on_grid && !same_phase ? 1 : 0;
+  sh.bytes = on_grid ? 0 : 1;
   if (sh.vec) {
     const size_t V = 16 / static_cast<size_t>(es);
     size_t head = ((16u - (po & 15u)) & 15u) / static_cast<size_t>(es);
@@ -189,13 +192,16 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
   const uintptr_t po = reinterpret_cast<uintptr_t>(out);
   mr::RankPtrs in{};
   bool same_phase = true;
+  bool aligned = po % static_cast<uintptr_t>(es) == 0;
   for (int r = 0; r < W; ++r) {
     const uintptr_t pr = reinterpret_cast<uintptr_t>(ins[r]);
     if (pr != po && overlap(pr, nbytes, po, nbytes)) return MR_ERR_ALIAS;
     if ((pr & 15u) != (po & 15u)) same_phase = false;
+    if (pr % static_cast<uintptr_t>(es) != 0) aligned = false;
     in.p[r] = ins[r];
+    in.shift[r] = static_cast<uint8_t>((pr - po) & 15u);
   }
-  const mr::ReduceShape sh = reduce_shape(n, es, po, same_phase);
+  const mr::ReduceShape sh = reduce_shape(n, es, po, same_phase, aligned);
   hipError_t e;
   if (mode == MR_ONESHOT) {
     const uint32_t shape = mr::oneshot_shape(sh.npacks, es, g_tile_shape.load());
@@ -248,15 +254,19 @@ bool needs_realign(uint16_t mask, uintptr_t d) { return (mask & ~(1u << (d & 15u
 
 // span: tiles cut per parameter over its W*E_s contiguous destination elements (every param-major
 // output); otherwise per (node-block, parameter, slot) segment (the list output's separate buffers).
-mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, bool span, GatherPlan* gp) {
+// bytes: plan the same placement on bytes (element size 1, every count times the dtype's size), for
+// pointers that are not multiples of the element size.
+mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, bool span, GatherPlan* gp,
+                      bool bytes = false) {
   if (G < 1 || W % G != 0) return MR_ERR_INVALID_ARG;
   if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
-  const uint64_t es = static_cast<uint64_t>(mr::elem_size(dtype));
+  const uint64_t scale = bytes ? static_cast<uint64_t>(mr::elem_size(dtype)) : 1;
+  const uint64_t es = bytes ? 1 : static_cast<uint64_t>(mr::elem_size(dtype));
   uint64_t T = 0;
   for (int s = 0; s < P; ++s) {
     if (splits[s] > (1ull << 56) || T > (1ull << 56)) return MR_ERR_INVALID_ARG;
-    T += splits[s];
+    T += splits[s] * scale;
   }
   if (T > (1ull << 56) / (static_cast<uint64_t>(W) * es)) return MR_ERR_INVALID_ARG;
   // gp may be a reused cache slot: reset every field (vectors keep their capacity)
@@ -269,7 +279,7 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
   {
     uint64_t O = 0;
     for (int s = 0; s < P; ++s) {
-      const uint64_t E = splits[s];
+      const uint64_t E = splits[s] * scale;
       for (int r = 0; E && r < W; ++r) {
         const uint64_t dst_off = (O * W + static_cast<uint64_t>(r) * E) * es;
         if (r < 16) gp->rm_mask |= static_cast<uint16_t>(1u << ((dst_off - (static_cast<uint64_t>(r) * T + O) * es) & 15u));
@@ -294,7 +304,7 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
     for (int i = 0; i < np; ++i) {
       a.O[i] = base;
       a.tile_prefix[i] = static_cast<uint32_t>(tiles);
-      const uint64_t E = splits[s0 + i];
+      const uint64_t E = splits[s0 + i] * scale;
       tiles += span ? mr::gather_tiles_per_segment(E * static_cast<uint64_t>(W), static_cast<uint32_t>(es))
                     : static_cast<uint64_t>(G) * mr::gather_tiles_per_segment(E, static_cast<uint32_t>(es));
       base += E;
@@ -317,6 +327,7 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
 struct CachedPlan {
   bool used = false;
   bool span = false;
+  bool bytes = false;
   int W = 0, G = 0, P = 0;
   mr_dtype dtype = MR_BF16;
   std::vector<uint64_t> splits;
@@ -327,11 +338,11 @@ thread_local CachedPlan t_plans[kPlanSlots];
 thread_local int t_plan_next = 0;
 
 mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, bool span,
-                             const GatherPlan** out) {
+                             const GatherPlan** out, bool bytes = false) {
   if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
   const size_t key_bytes = static_cast<size_t>(P) * sizeof(uint64_t);
   for (const CachedPlan& c : t_plans)
-    if (c.used && c.span == span && c.W == W && c.G == G && c.P == P && c.dtype == dtype &&
+    if (c.used && c.span == span && c.bytes == bytes && c.W == W && c.G == G && c.P == P && c.dtype == dtype &&
         std::memcmp(c.splits.data(), splits, key_bytes) == 0) {
       *out = &c.plan;
       return MR_OK;
@@ -339,9 +350,10 @@ mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dty
   CachedPlan& c = t_plans[t_plan_next];
   t_plan_next = (t_plan_next + 1) % kPlanSlots;
   c.used = false;
-  const mr_status s = gather_plan(W, G, splits, P, dtype, span, &c.plan);
+  const mr_status s = gather_plan(W, G, splits, P, dtype, span, &c.plan, bytes);
   if (s != MR_OK) return s;
   c.span = span;
+  c.bytes = bytes;
   c.W = W;
   c.G = G;
   c.P = P;
@@ -388,10 +400,9 @@ mr_status check_allreduce_args(const void* const* bufs, int W, size_t n, mr_dtyp
   if (!bufs || !out) return MR_ERR_INVALID_ARG;
   const int es = elem_size(dtype);
   if (n > (SIZE_MAX / 2 - kCtrlBytes) / static_cast<size_t>(es)) return MR_ERR_INVALID_ARG;
-  if (!elem_aligned(out, es)) return MR_ERR_INVALID_ARG;
   for (int r = 0; r < W; ++r)
-    if (!bufs[r] || !elem_aligned(bufs[r], es)) return MR_ERR_INVALID_ARG;
-  return MR_OK;
+    if (!bufs[r]) return MR_ERR_INVALID_ARG;
+  return MR_OK;  // any alignment: pointers off the element grid take the byte-access path
 }
 
 mr_status allreduce_in_workspace(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out, mr_mode mode,
@@ -494,13 +505,22 @@ mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dty
   if (cnt == 0) return MR_OK;
   if (!bufs || !out) return MR_ERR_INVALID_ARG;
   const size_t es = static_cast<size_t>(mr::elem_size(dtype));
-  if (!elem_aligned(out, es)) return MR_ERR_INVALID_ARG;
   const char* ins[MR_MAX_W];
   for (int r = 0; r < W; ++r) {
-    if (!bufs[r] || !elem_aligned(bufs[r], es)) return MR_ERR_INVALID_ARG;
+    if (!bufs[r]) return MR_ERR_INVALID_ARG;
     ins[r] = static_cast<const char*>(bufs[r]) + off * es;  // this rank's chunk of every rank buffer
   }
   return reduce_launch(ins, W, cnt, dtype, static_cast<char*>(out), MR_ONESHOT, reinterpret_cast<hipStream_t>(stream));
+}
+
+// Element size of a gather's pointers: the dtype's, or 1 when some pointer is off the element grid (then
+// the plan and the copy work on bytes).
+bool gather_on_grid(mr_dtype dtype, std::initializer_list<const void*> ptrs) {
+  if (!valid_dtype(dtype)) return true;
+  const uint64_t es = static_cast<uint64_t>(mr::elem_size(dtype));
+  for (const void* p : ptrs)
+    if (!elem_aligned(p, es)) return false;
+  return true;
 }
 
 mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_t* splits, int P, mr_dtype dtype,
@@ -509,9 +529,9 @@ mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_
   const GatherPlan* gp = nullptr;
   // tiles span a parameter's W slots when there are several parameters; one parameter (a plain
   // rank-major copy) measured faster with per-slot tiles
-  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp, !gather_on_grid(dtype, {src, out}));
   if (s != MR_OK || gp->T == 0) return s;
-  if (!src || !out || !elem_aligned(src, gp->es) || !elem_aligned(out, gp->es)) return MR_ERR_INVALID_ARG;
+  if (!src || !out) return MR_ERR_INVALID_ARG;
   const uint64_t total_bytes = static_cast<uint64_t>(W) * gp->T * gp->es;
   if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
     return MR_ERR_ALIAS;
@@ -527,9 +547,9 @@ mr_status mr_allgather_param_contig_sdma(const void* src, int W, int G, const ui
                                          void* out, mr_stream stream) {
   if (W < 1 || W > 65535) return MR_ERR_INVALID_ARG;
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);  // engines copy bytes: any alignment
   if (s != MR_OK || gp->T == 0) return s;
-  if (!src || !out || !elem_aligned(src, gp->es) || !elem_aligned(out, gp->es)) return MR_ERR_INVALID_ARG;
+  if (!src || !out) return MR_ERR_INVALID_ARG;
   const uint64_t total_bytes = static_cast<uint64_t>(W) * gp->T * gp->es;
   if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
     return MR_ERR_ALIAS;
@@ -581,6 +601,27 @@ int mrx_twoshot_plan(int W, size_t n, int dtype, uintptr_t out_addr, int same_ph
   return 0;
 }
 
+int mrx_reduce_shape(const void* const* bufs, int W, size_t n, int dtype, const void* out, uint64_t* f, int nf) {
+  if (W < 1 || W > MR_MAX_W || !bufs || !out || !is_float(static_cast<mr_dtype>(dtype)) || !f || nf < 5 + MR_MAX_W)
+    return -1;
+  const int es = mr::elem_size(static_cast<mr_dtype>(dtype));
+  const uintptr_t po = reinterpret_cast<uintptr_t>(out);
+  bool same_phase = true, aligned = po % static_cast<uintptr_t>(es) == 0;
+  for (int r = 0; r < W; ++r) {
+    const uintptr_t pr = reinterpret_cast<uintptr_t>(bufs[r]);
+    if ((pr & 15u) != (po & 15u)) same_phase = false;
+    if (pr % static_cast<uintptr_t>(es) != 0) aligned = false;
+    f[5 + r] = (pr - po) & 15u;
+  }
+  const mr::ReduceShape sh = reduce_shape(n, es, po, same_phase, aligned);
+  f[0] = static_cast<uint64_t>(sh.vec);
+  f[1] = static_cast<uint64_t>(sh.realign);
+  f[2] = static_cast<uint64_t>(sh.bytes);
+  f[3] = sh.head;
+  f[4] = sh.npacks;
+  return 0;
+}
+
 int mrx_gather_phase_masks(int W, int G, const uint64_t* splits, int P, int dtype, uint16_t* rm_mask,
                            uint16_t* rank_masks, int n_rank_masks) {
   if (W < 1 || W > 65535 || !rm_mask || (n_rank_masks && !rank_masks)) return -1;
@@ -606,14 +647,16 @@ int mr_sdma_engines(void) {
 mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int G, const uint64_t* splits, int P,
                                            mr_dtype dtype, void* out, mr_stream stream) {
   if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
+  bool on_grid = gather_on_grid(dtype, {out});
+  for (int r = 0; shards && r < W; ++r) on_grid = on_grid && gather_on_grid(dtype, {shards[r]});
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp, !on_grid);
   if (s != MR_OK || gp->T == 0) return s;
-  if (!shards || !out || !elem_aligned(out, gp->es)) return MR_ERR_INVALID_ARG;
+  if (!shards || !out) return MR_ERR_INVALID_ARG;
   const uint64_t shard_bytes = gp->T * gp->es, out_bytes = static_cast<uint64_t>(W) * shard_bytes;
   bool realign = false;
   for (int r = 0; r < W; ++r) {
-    if (!shards[r] || !elem_aligned(shards[r], gp->es)) return MR_ERR_INVALID_ARG;
+    if (!shards[r]) return MR_ERR_INVALID_ARG;
     if (overlap(reinterpret_cast<uintptr_t>(shards[r]), shard_bytes, reinterpret_cast<uintptr_t>(out), out_bytes))
       return MR_ERR_ALIAS;
     realign = realign || needs_realign(gp->rank_mask[r], reinterpret_cast<uintptr_t>(shards[r]) -
@@ -637,15 +680,16 @@ mr_status mr_allgather_list(const void* const* shards, int W, size_t T, mr_dtype
                             mr_stream stream) {
   if (W < 1 || W > MR_MAX_TABLE_W) return MR_ERR_INVALID_ARG;
   const uint64_t split = T;
+  bool on_grid = true;
+  for (int i = 0; shards && outs && i < W; ++i) on_grid = on_grid && gather_on_grid(dtype, {shards[i], outs[i]});
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, W, &split, 1, dtype, false, &gp);
+  mr_status s = cached_gather_plan(W, W, &split, 1, dtype, false, &gp, !on_grid);
   if (s != MR_OK || gp->T == 0) return s;
   if (!shards || !outs) return MR_ERR_INVALID_ARG;
   const uint64_t bytes = gp->T * gp->es;
   bool realign = false;
   for (int i = 0; i < W; ++i) {
-    if (!shards[i] || !outs[i] || !elem_aligned(shards[i], gp->es) || !elem_aligned(outs[i], gp->es))
-      return MR_ERR_INVALID_ARG;
+    if (!shards[i] || !outs[i]) return MR_ERR_INVALID_ARG;
     realign = realign || ((reinterpret_cast<uintptr_t>(shards[i]) - reinterpret_cast<uintptr_t>(outs[i])) & 15u) != 0;
     for (int j = 0; j < W; ++j) {
       const uintptr_t oi = reinterpret_cast<uintptr_t>(outs[i]);

@@ -26,9 +26,12 @@ constexpr int kGB = kGatherBlock;
 constexpr int kCopyU = kGatherTileBytes / (16 * kGB);  // 16-byte words per lane per full tile
 static_assert(kCopyU * 16 * kGB == kGatherTileBytes, "a tile is a whole number of workgroup sweeps");
 
+// One element (S = 1: one byte, for pointers off their dtype's element grid; the host then plans the
+// whole gather in bytes, so no access wider than a byte touches an address off its own alignment).
 template <int S>
 __device__ __forceinline__ void copy_elem(const char* src, char* dst, uint32_t o) {
-  if (S == 2) *reinterpret_cast<uint16_t*>(dst + o) = *reinterpret_cast<const uint16_t*>(src + o);
+  if (S == 1) dst[o] = src[o];
+  else if (S == 2) *reinterpret_cast<uint16_t*>(dst + o) = *reinterpret_cast<const uint16_t*>(src + o);
   else *reinterpret_cast<uint32_t*>(dst + o) = *reinterpret_cast<const uint32_t*>(src + o);
 }
 
@@ -44,7 +47,8 @@ __device__ __forceinline__ u32x4 realign(const u32x4& A, const u32x4& B) {
   return o;
 }
 
-// 16-byte stores to a 16-byte-aligned destination from a source M (1..15, even) bytes past a 16-byte
+// 16-byte stores to a 16-byte-aligned destination from a source M (1..15; a multiple of the element
+// size, so even unless the gather is planned in bytes) bytes past a 16-byte
 // boundary: each lane loads the two aligned source packs its output straddles and realigns them in
 // registers.  Every loaded pack holds at least one byte of the span, so no access leaves the pages the
 // source occupies.
@@ -110,15 +114,35 @@ __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t l
     const uint32_t m = static_cast<uint32_t>((ps + head) & 15u);  // source offset past its boundary
     const u32x4* sa = reinterpret_cast<const u32x4*>(src + head - m);
     u32x4* d4 = reinterpret_cast<u32x4*>(dst + head);
-    // m is a nonzero multiple of the element size (the host refuses pointers that are not), so even
+    // m is a nonzero multiple of the element size S (S = 1 when the host planned in bytes)
     switch (m) {  // uniform per tile: one compile-time realignment per source offset
-      case 2: copy_realigned<2>(sa, d4, nw); break;
       case 4: copy_realigned<4>(sa, d4, nw); break;
-      case 6: copy_realigned<6>(sa, d4, nw); break;
       case 8: copy_realigned<8>(sa, d4, nw); break;
-      case 10: copy_realigned<10>(sa, d4, nw); break;
       case 12: copy_realigned<12>(sa, d4, nw); break;
-      default: copy_realigned<14>(sa, d4, nw); break;
+      default:
+        if constexpr (S <= 2) {
+          switch (m) {
+            case 2: copy_realigned<2>(sa, d4, nw); break;
+            case 6: copy_realigned<6>(sa, d4, nw); break;
+            case 10: copy_realigned<10>(sa, d4, nw); break;
+            case 14: copy_realigned<14>(sa, d4, nw); break;
+            default:
+              if constexpr (S == 1) {
+                switch (m) {
+                  case 1: copy_realigned<1>(sa, d4, nw); break;
+                  case 3: copy_realigned<3>(sa, d4, nw); break;
+                  case 5: copy_realigned<5>(sa, d4, nw); break;
+                  case 7: copy_realigned<7>(sa, d4, nw); break;
+                  case 9: copy_realigned<9>(sa, d4, nw); break;
+                  case 11: copy_realigned<11>(sa, d4, nw); break;
+                  case 13: copy_realigned<13>(sa, d4, nw); break;
+                  default: copy_realigned<15>(sa, d4, nw); break;
+                }
+              }
+              break;
+          }
+        }
+        break;
     }
     const uint32_t tail0 = head + (nw << 4);
     const uint32_t edge = head + (len - tail0);
@@ -209,7 +233,9 @@ hipError_t launch_param_contig(const GatherArgs& a, bool realign, hipStream_t st
   if (a.total_tiles == 0) return hipSuccess;
   const uint32_t kMaxGrid = 1u << 20;
   const uint32_t grid = a.total_tiles < kMaxGrid ? a.total_tiles : kMaxGrid;
-  if (a.elem == 2 && realign)
+  if (a.elem == 1)  // planned in bytes: pointers off the element grid
+    hipLaunchKernelGGL((param_contig<1, true>), dim3(grid), dim3(kGB), 0, st, a);
+  else if (a.elem == 2 && realign)
     hipLaunchKernelGGL((param_contig<2, true>), dim3(grid), dim3(kGB), 0, st, a);
   else if (a.elem == 2)
     hipLaunchKernelGGL((param_contig<2, false>), dim3(grid), dim3(kGB), 0, st, a);

@@ -103,18 +103,25 @@ inline uint32_t twoshot_sync_for(size_t bytes, uint32_t sync) {
 
 struct RankPtrs {
   const char* p[MR_MAX_W];
+  // realigned 16-byte path: byte offset of rank r's 16-byte phase past out's, (p[r] - out) mod 16
+  uint8_t shift[MR_MAX_W];
 };
 
 // Element layout of one reduce call after the host has split off the unaligned head and tail.
 //   [0, head)                        element-wise
-//   [head, head + npacks*V)          16-byte packs (V = 16 / elem_size)
+//   [head, head + npacks*V)          16-byte packs (V = 16 / elem_size), aligned on out
 //   [head + npacks*V, n)             element-wise tail
-// When the pointers do not share one alignment, vec == 0 and everything is element-wise (V = 1).
+// Pointers that are all multiples of the element size take the 16-byte path; when some input's 16-byte
+// phase differs from out's, `realign` is set and that input's packs are loaded as the two aligned packs
+// they straddle and realigned in registers (RankPtrs::shift).  A pointer that is not a multiple of the
+// element size makes the whole call element-wise with byte accesses only (vec == 0, bytes == 1).
 struct ReduceShape {
   size_t n;
   size_t head;
   size_t npacks;   // packs of the vector body
   int vec;
+  int realign;     // vec path with some input out of out's 16-byte phase
+  int bytes;       // element-wise path with byte loads and stores (some pointer not element-aligned)
 };
 
 struct TwoShotPlan {

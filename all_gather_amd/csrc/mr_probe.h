@@ -45,6 +45,14 @@ int mrx_twoshot_plan(int W, size_t n, int dtype, uintptr_t out_addr, int same_ph
                      int wait_free, uint64_t* f, int nf);
 
 /*
+ * mrx_reduce_shape -- how mr_allreduce_sum would lay out a call on these pointers: f[0] vec (16-byte
+ * path), f[1] realign (some input in another 16-byte phase than out), f[2] bytes (a pointer off the
+ * element grid: byte accesses only), f[3] head elements before out's 16-byte boundary, f[4] packs,
+ * f[5 + r] rank r's phase past out's, (bufs[r] - out) mod 16.  Needs nf >= 5 + MR_MAX_W (21).
+ */
+int mrx_reduce_shape(const void* const* bufs, int W, size_t n, int dtype, const void* out, uint64_t* f, int nf);
+
+/*
  * mrx_gather_phase_masks -- the 16-bit phase masks the gather planner keeps for a split table: bit
  * (dst_off - src_off) mod 16 of every (parameter, rank) piece, for a rank-major source (*rm_mask) and
  * for per-rank shard sources (rank_masks[r], r < n_rank_masks, W <= 64).  Returns 0 or an mr_status.

@@ -150,16 +150,62 @@ __device__ __forceinline__ void store_bits(char* p, uint32_t b) {
   else *q = b;
 }
 
+// Element bits through single-byte accesses only (pointers that are not multiples of the element size:
+// no unaligned multi-byte access is ever issued).  Little-endian, as the element's bytes sit in memory.
+template <int S>
+__device__ __forceinline__ uint32_t load_bytes(const char* p) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < S; ++i) v |= static_cast<uint32_t>(static_cast<uint8_t>(p[i])) << (8 * i);
+  return v;
+}
+template <int S>
+__device__ __forceinline__ void store_bytes(char* p, uint32_t v) {
+#pragma unroll
+  for (int i = 0; i < S; ++i) p[i] = static_cast<char>(static_cast<uint8_t>(v >> (8 * i)));
+}
+
 // ---------------------------------------------------------------------------------- shared bodies
 
-// One element, any alignment: fp32 accumulation in rank order.
-template <typename D, int W, bool Dev>
+// One element: fp32 accumulation in rank order.  BYTES: inputs read (and out written, unless Dev) one
+// byte at a time; Dev: written to the stage with a device-coherent store (the stage is always aligned).
+template <typename D, int W, bool Dev, bool BYTES = false>
 __device__ __forceinline__ void reduce_elem(const RankPtrs& in, char* dst, size_t e) {
   const size_t off = e * D::kSize;
-  float acc = D::widen1(load_bits<D::kSize, false>(in.p[0] + off));
+  auto ld = [&](const char* q) { return BYTES ? load_bytes<D::kSize>(q) : load_bits<D::kSize, false>(q); };
+  float acc = D::widen1(ld(in.p[0] + off));
 #pragma unroll
-  for (int r = 1; r < W; ++r) acc = acc + D::widen1(load_bits<D::kSize, false>(in.p[r] + off));
-  store_bits<D::kSize, Dev>(dst + off, D::narrow1(acc));
+  for (int r = 1; r < W; ++r) acc = acc + D::widen1(ld(in.p[r] + off));
+  if (BYTES && !Dev) store_bytes<D::kSize>(dst + off, D::narrow1(acc));
+  else store_bits<D::kSize, Dev>(dst + off, D::narrow1(acc));
+}
+
+// Bytes d .. d+15 of the 32 bytes A:B (d the same in every lane), with selects only: no branch, so the
+// loads of every rank can be in flight before any realignment.  Used for an input whose 16-byte phase is
+// d bytes past out's: A and B are the two aligned packs an output pack's bytes straddle.
+__device__ __forceinline__ u32x4 realign_rt(const u32x4& A, const u32x4& B, uint32_t d) {
+  const bool h8 = (d & 8u) != 0, h4 = (d & 4u) != 0;
+  const uint32_t w0 = h8 ? A[2] : A[0], w1 = h8 ? A[3] : A[1], w2 = h8 ? B[0] : A[2];
+  const uint32_t w3 = h8 ? B[1] : A[3], w4 = h8 ? B[2] : B[0], w5 = h8 ? B[3] : B[1];
+  const uint32_t x0 = h4 ? w1 : w0, x1 = h4 ? w2 : w1, x2 = h4 ? w3 : w2, x3 = h4 ? w4 : w3, x4 = h4 ? w5 : w4;
+  const uint32_t sh = d & 3u;
+  u32x4 o;
+  o[0] = __builtin_amdgcn_alignbyte(x1, x0, sh);
+  o[1] = __builtin_amdgcn_alignbyte(x2, x1, sh);
+  o[2] = __builtin_amdgcn_alignbyte(x3, x2, sh);
+  o[3] = __builtin_amdgcn_alignbyte(x4, x3, sh);
+  return o;
+}
+
+// The two aligned packs that output pack i (on out's 16-byte grid) of rank r straddles, for an input
+// in.shift[r] = d bytes past out's phase.  The second is pack i + 1 when d != 0 -- it then holds bytes of
+// the output pack itself, so no load leaves the input's pages -- and pack i again when d == 0, so the
+// address needs no branch.
+__device__ __forceinline__ void load_pack_pair(const RankPtrs& in, int r, size_t hb, size_t i, u32x4& a, u32x4& b) {
+  const uint32_t d = in.shift[r];
+  const u32x4* base = reinterpret_cast<const u32x4*>(in.p[r] + hb - d);
+  a = __builtin_nontemporal_load(base + i);
+  b = base[i + (d != 0 ? 1 : 0)];
 }
 
 // Wave-contiguous tile layout: a workgroup of B lanes owns B*P consecutive 16-byte packs starting at
@@ -172,30 +218,38 @@ __device__ __forceinline__ size_t wc_pack(size_t first, int u) {
 
 // Reduce a wave-contiguous tile of B*P packs (i < end), PC packs at a time: all W*PC loads in flight,
 // rank by rank, before the adds; each result goes to st(u, i, pack).
-template <typename D, int W, int B, int P, typename Store>
+template <typename D, int W, int B, int P, typename Store, bool RA = false>
 __device__ __forceinline__ void reduce_tile(const RankPtrs& in, size_t hb, size_t first, size_t end, Store st) {
   constexpr int PC = (W <= 8 || P == 1) ? P : 2;  // wide W: fewer packs in flight per lane
   static_assert(P % PC == 0, "pack groups");
 #pragma unroll
   for (int u0 = 0; u0 < P; u0 += PC) {
     u32x4 v[PC][W];
+    u32x4 vb[RA ? PC : 1][RA ? W : 1];  // RA: the second aligned pack of each
 #pragma unroll
     for (int r = 0; r < W; ++r)
 #pragma unroll
       for (int u = 0; u < PC; ++u) {
         const size_t i = wc_pack<B, P>(first, u0 + u);
-        if (i < end) v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
+        if (i < end) {
+          if constexpr (RA) load_pack_pair(in, r, hb, i, v[u][r], vb[u][r]);
+          else v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
+        }
       }
 #pragma unroll
     for (int u = 0; u < PC; ++u) {
       const size_t i = wc_pack<B, P>(first, u0 + u);
       if (i < end) {
+        auto pack = [&](int r) {
+          if constexpr (RA) return realign_rt(v[u][r], vb[u][r], in.shift[r]);
+          else return v[u][r];
+        };
         float acc[D::V];
-        D::widen(v[u][0], acc);
+        D::widen(pack(0), acc);
 #pragma unroll
         for (int r = 1; r < W; ++r) {
           float t[D::V];
-          D::widen(v[u][r], t);
+          D::widen(pack(r), t);
 #pragma unroll
           for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
         }
@@ -253,14 +307,14 @@ __device__ __forceinline__ size_t xcd_tile(size_t b, size_t ntiles) {
   return x * q + (x < rem ? x : rem) + b / kXcds;
 }
 
-template <typename D, int W, int B, int U>
+template <typename D, int W, int B, int U, bool RA = false>
 __global__ __launch_bounds__(B) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles, int xcd) {
   const size_t hb = sh.head * D::kSize;
   u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
+  auto store = [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); };
   for (size_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
     const size_t t = xcd ? xcd_tile(b, ntiles) : b;
-    reduce_tile<D, W, B, U>(in, hb, t * (B * U), sh.npacks,
-                            [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); });
+    reduce_tile<D, W, B, U, decltype(store), RA>(in, hb, t * (B * U), sh.npacks, store);
   }
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
@@ -297,11 +351,11 @@ __global__ __launch_bounds__(B) void oneshot_pair(RankPtrs in, char* out, Reduce
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
 
-template <typename D, int W>
+template <typename D, int W, bool BYTES>
 __global__ __launch_bounds__(kBlock) void oneshot_elem(RankPtrs in, char* out, size_t n) {
   for (size_t e = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; e < n;
        e += static_cast<size_t>(gridDim.x) * kBlock)
-    reduce_elem<D, W, false>(in, out, e);
+    reduce_elem<D, W, false, BYTES>(in, out, e);
 }
 
 // ---------------------------------------------------------------------------------------- two-shot
@@ -518,7 +572,7 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counts, const TwoShotPlan&
 // out.  Same-GPU A/B against one build for all modes, W=8 bf16: 4 MiB per rank tile 16.0 -> 15.65 us,
 // chunk 16.3 -> 15.85, last arriver 11.8 -> 11.55, grid 17.2 -> 17.6; 16 MiB last 38.1 -> 37.7, grid
 // 38.2 -> 37.7.
-template <typename D, int W, int TB, int SYNC>
+template <typename D, int W, int TB, int SYNC, bool RA = false>
 __global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* stage, Ctrl* ctrl, uint32_t* flags,
                                                   ReduceShape sh, TwoShotPlan pl_arg) {
   TwoShotPlan pl = pl_arg;
@@ -536,9 +590,10 @@ __global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* 
   if (k < pl.t1) {
     const size_t first = c0 + static_cast<size_t>(k) * TB;
     const i32x4 rs = make_rsrc(stage + hb + first * 16, TB * 16);
-    reduce_tile<D, W, TB, 1>(in, hb, first, cend, [&](int, size_t i, const u32x4& o) {
+    auto store = [&](int, size_t i, const u32x4& o) {
       raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), rs, static_cast<int>((i - first) * 16), 0, kStageStoreAux);
-    });
+    };
+    reduce_tile<D, W, TB, 1, decltype(store), RA>(in, hb, first, cend, store);
     if (c == 0 && k == 0) reduce_edges<D, W, true>(in, stage, sh);
     publish_phase1(ctrl, flags, pl, c, k);
     if (pl.sync == kSyncLast && arrive_last(flags, pl, c, k)) {
@@ -690,7 +745,7 @@ __global__ __launch_bounds__(kOneShotBlock) void twoshot_xcd(RankPtrs in, char* 
 
 // Element-wise two-shot for pointers that do not share one 16-byte alignment (units are elements;
 // a phase-2 group copies ratio phase-1 tiles, kElemPer elements per lane each).
-template <typename D>
+template <typename D, bool BYTES>
 __device__ __forceinline__ void copy_group_elem(char* out, const char* stage, size_t first, size_t cend) {
   constexpr int N = kRatio * kElemPer;  // elements per lane
   uint32_t v[N];
@@ -702,13 +757,16 @@ __device__ __forceinline__ void copy_group_elem(char* out, const char* stage, si
 #pragma unroll
   for (int u = 0; u < N; ++u) {
     const size_t e = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
-    if (e < cend) store_bits<D::kSize, false>(out + e * D::kSize, v[u]);
+    if (e < cend) {
+      if (BYTES) store_bytes<D::kSize>(out + e * D::kSize, v[u]);
+      else store_bits<D::kSize, false>(out + e * D::kSize, v[u]);
+    }
   }
 }
 
 // Phase-1 tile of the element-wise path: kElemPer elements per lane at stride kBlock (each step
 // coalesced), every rank's loads in flight before the adds.
-template <typename D, int W>
+template <typename D, int W, bool BYTES>
 __device__ __forceinline__ void reduce_tile_elem(const RankPtrs& in, char* stage, size_t first, size_t cend) {
   uint32_t v[kElemPer][W];
 #pragma unroll
@@ -716,7 +774,7 @@ __device__ __forceinline__ void reduce_tile_elem(const RankPtrs& in, char* stage
 #pragma unroll
     for (int u = 0; u < kElemPer; ++u) {
       const size_t e = first + static_cast<size_t>(u) * kBlock + threadIdx.x;
-      if (e < cend) v[u][r] = load_bits<D::kSize, false>(in.p[r] + e * D::kSize);
+      if (e < cend) v[u][r] = BYTES ? load_bytes<D::kSize>(in.p[r] + e * D::kSize) : load_bits<D::kSize, false>(in.p[r] + e * D::kSize);
     }
 #pragma unroll
   for (int u = 0; u < kElemPer; ++u) {
@@ -730,7 +788,7 @@ __device__ __forceinline__ void reduce_tile_elem(const RankPtrs& in, char* stage
   }
 }
 
-template <typename D, int W>
+template <typename D, int W, bool BYTES>
 __global__ __launch_bounds__(kBlock) void twoshot_elem(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
                                                        uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
   uint32_t c, k;
@@ -744,14 +802,14 @@ __global__ __launch_bounds__(kBlock) void twoshot_elem(RankPtrs in, char* out, c
   const size_t c0 = static_cast<size_t>(c) * pl.chunk_units;
   const size_t cend = c0 + pl.chunk_units < sh.n ? c0 + pl.chunk_units : sh.n;
   if (k < pl.t1) {
-    reduce_tile_elem<D, W>(in, stage, c0 + static_cast<size_t>(k) * kTileE, cend);
+    reduce_tile_elem<D, W, BYTES>(in, stage, c0 + static_cast<size_t>(k) * kTileE, cend);
     publish_phase1(ctrl, flags, pl, c, k);
     if (pl.sync == kSyncLast && arrive_last(flags, pl, c, k))
-      copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(k / pl.ratio) * (kTileE * kRatio), cend);
+      copy_group_elem<D, BYTES>(out, stage, c0 + static_cast<size_t>(k / pl.ratio) * (kTileE * kRatio), cend);
   } else if (k < pl.t1 + pl.t2) {
     const uint32_t q = k - pl.t1;
     wait_phase1(ctrl, flags, pl, c, q);
-    copy_group_elem<D>(out, stage, c0 + static_cast<size_t>(q) * (kTileE * kRatio), cend);
+    copy_group_elem<D, BYTES>(out, stage, c0 + static_cast<size_t>(q) * (kTileE * kRatio), cend);
   }
   finish_twoshot(ctrl, pl, c, k);
 }
@@ -766,7 +824,7 @@ __global__ void zero_words(uint32_t* p, size_t words) {
 
 constexpr size_t kMaxGrid = size_t(1) << 20;  // workgroups; beyond this the one-shot kernels grid-stride
 
-template <typename D, int W, int B, int U>
+template <typename D, int W, int B, int U, bool RA = false>
 hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
   constexpr size_t tile = static_cast<size_t>(B) * U;
   const size_t ntiles = (sh.npacks + tile - 1) / tile;
@@ -774,8 +832,8 @@ hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& 
   if (grid == 0) grid = 1;  // edges only
   // XCD-contiguous tile order on small grids and on the wide tiles up to 1024 of them (see xcd_tile)
   const int xcd = grid == ntiles && (ntiles <= 512 || (tile == 1024 && ntiles <= 1024)) ? 1 : 0;
-  hipLaunchKernelGGL((oneshot_vec<D, W, B, U>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh, ntiles,
-                     xcd);
+  hipLaunchKernelGGL((oneshot_vec<D, W, B, U, RA>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh,
+                     ntiles, xcd);
   return hipGetLastError();
 }
 
@@ -791,8 +849,13 @@ hipError_t oneshot_pair_launch(const RankPtrs& in, char* out, const ReduceShape&
   return hipGetLastError();
 }
 
+// Realigned 16-byte path (inputs in other 16-byte phases than out): two aligned loads per pack per
+// realigned rank, so two packs per lane (one for W > 8) keep the registers of the wide tile's four.
+template <int W> struct RealignU { static constexpr int value = W <= 8 ? 2 : 1; };
+
 template <typename D, int W>
 hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, uint32_t shape, hipStream_t st) {
+  if (sh.vec && sh.realign) return oneshot_vec_launch<D, W, kOneShotBlock, RealignU<W>::value, true>(in, out, sh, st);
   if (sh.vec) {
     if constexpr (W <= 8) {
       if (shape == kShapeWidePair) return oneshot_pair_launch<D, W>(in, out, sh, st);
@@ -805,7 +868,10 @@ hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, uint3
   }
   const size_t need = (sh.n + kBlock - 1) / kBlock;
   const size_t grid = need < kMaxGrid ? need : kMaxGrid;
-  hipLaunchKernelGGL((oneshot_elem<D, W>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, st, in, out, sh.n);
+  if (sh.bytes)
+    hipLaunchKernelGGL((oneshot_elem<D, W, true>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, st, in, out, sh.n);
+  else
+    hipLaunchKernelGGL((oneshot_elem<D, W, false>), dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, st, in, out, sh.n);
   return hipGetLastError();
 }
 
@@ -840,13 +906,21 @@ hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uin
     }
   }
   const unsigned grid = pl.chunks * (pl.sync == kSyncLast ? pl.t1 : pl.t1 + pl.t2);
+  if (sh.vec && sh.realign) {  // the planner fixes the last-arriver hand-off and wide tiles here
+    hipLaunchKernelGGL((twoshot_vec<D, W, kTBlock, kSyncLast, true>), dim3(grid), dim3(kTBlock), 0, st, in, out, stage,
+                       ctrl, flags, sh, pl);
+    return hipGetLastError();
+  }
   if (sh.vec && pl.unit1 == 64)
     return twoshot_vec_launch<D, W, 64>(in, out, stage, ctrl, flags, sh, pl, grid, st);
   if (sh.vec && pl.unit1 == 256)
     return twoshot_vec_launch<D, W, 256>(in, out, stage, ctrl, flags, sh, pl, grid, st);
   if (sh.vec)
     return twoshot_vec_launch<D, W, kTBlock>(in, out, stage, ctrl, flags, sh, pl, grid, st);
-  hipLaunchKernelGGL((twoshot_elem<D, W>), dim3(grid), dim3(kBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
+  if (sh.bytes)
+    hipLaunchKernelGGL((twoshot_elem<D, W, true>), dim3(grid), dim3(kBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
+  else
+    hipLaunchKernelGGL((twoshot_elem<D, W, false>), dim3(grid), dim3(kBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
   return hipGetLastError();
 }
 
@@ -911,6 +985,10 @@ hipError_t launch_twoshot(const RankPtrs& in, int W, mr_dtype dt, char* out, cha
 // than a pack) ride with phase-1 tile 0 and phase-2 tile 0 of chunk 0.
 TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit, uint32_t shape) {
   TwoShotPlan pl{};
+  if (sh.vec && sh.realign) {  // realigned inputs: one build, last-arriver hand-off on wide tiles
+    sync = kSyncLast;
+    shape = kShapeWide;
+  }
   pl.chunks = static_cast<uint32_t>(W);
   const size_t units = sh.vec ? sh.npacks : sh.n;
   pl.chunk_units = (units + W - 1) / W;
@@ -924,7 +1002,7 @@ TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t s
   pl.t2 = static_cast<uint32_t>(t2);
   pl.sync = sync;
   pl.spin_limit = spin_limit;
-  if (twoshot_xcd_units(sh.vec, W, sh.npacks, sync, shape)) {  // XCD-local units replace the chunk tiles
+  if (!sh.realign && twoshot_xcd_units(sh.vec, W, sh.npacks, sync, shape)) {  // XCD-local units replace the chunk tiles
     constexpr size_t UP = static_cast<size_t>(kOneShotBlock) * 4;
     pl.xcd = 1;
     pl.units = sh.npacks ? (sh.npacks + UP - 1) / UP : 1;  // an edges-only call still has one unit

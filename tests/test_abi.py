@@ -128,7 +128,6 @@ def test_sdma_gather_argument_errors(L):
     assert f(src, 8, 4, None, 3, 0, out, None) == EINVAL
     assert f(src, 8, 4, sp, 3, 9, out, None) == EINVAL    # unknown dtype
     assert f(None, 8, 4, sp, 3, 0, out, None) == EINVAL
-    assert f(src + 1, 8, 4, sp, 3, 0, out, None) == EINVAL  # not a multiple of the element size
     zero = (ctypes.c_uint64 * 2)(0, 0)
     assert f(None, 8, 4, zero, 2, 0, None, None) == OK     # empty: no-op
     assert f(src, 8, 4, sp, 3, 0, src + 766, None) == EALIAS
@@ -309,21 +308,29 @@ def test_shard_gather_argument_errors(L):
     assert outs is not None
 
 
-def test_pointers_must_be_element_aligned(L):
-    """Every device pointer is a multiple of the element size; anything else is refused before launch."""
+def test_any_alignment_is_accepted(L):
+    """Pointers off the element grid are valid arguments: the reduce plans them on its byte-access path
+    (the layout read through the library's planning hook; no launch here) and the gathers plan in bytes.
+    Only null pointers, sizes and overlaps are refused."""
+    L.mrx_reduce_shape.restype = ctypes.c_int
+    L.mrx_reduce_shape.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int]
+    f = (ctypes.c_uint64 * 21)()
     a, b, out = 0x100000, 0x200000, 0x900000
-    assert L.mr_allreduce_sum(_ptrs(a + 1, b), 2, 64, 0, out, 0, None) == EINVAL      # bf16 buffer at odd byte
-    assert L.mr_allreduce_sum(_ptrs(a, b), 2, 64, 0, out + 1, 1, None) == EINVAL      # bf16 out at odd byte
-    assert L.mr_allreduce_sum(_ptrs(a, b + 2), 2, 64, 2, out, 0, None) == EINVAL      # fp32 buffer 2 bytes in
-    assert L.mr_reduce_scatter_sum(_ptrs(a, b + 1), 2, 64, 1, 0, out, None) == EINVAL
-    assert L.mr_reduce_scatter_sum(_ptrs(a, b), 2, 64, 2, 1, out + 2, None) == EINVAL
-    sp = (ctypes.c_uint64 * 2)(8, 16)
-    assert L.mr_allgather_param_contig(a + 1, 4, 2, sp, 2, 0, out, None) == EINVAL
-    assert L.mr_allgather_param_contig(a, 4, 2, sp, 2, 3, out + 2, None) == EINVAL    # int32 out 2 bytes in
-    shards = _ptrs(a, b, a + 0x1000, b + 0x1000 + 1)
-    assert L.mr_allgather_param_contig_shards(shards, 4, 2, sp, 2, 0, out, None) == EINVAL
-    assert L.mr_allgather_into_tensor(shards, 4, 24, 0, out, None) == EINVAL
-    good = _ptrs(a, b, a + 0x1000, b + 0x1000)
-    assert L.mr_allgather_into_tensor(good, 4, 24, 1, out + 1, None) == EINVAL
-    outs = _ptrs(out, out + 0x1000, out + 0x2000, out + 0x3000 + 2)
-    assert L.mr_allgather_list(good, 4, 24, 2, outs, None) == EINVAL                   # fp32 output 2 bytes in
+
+    def shape(ptrs, dt, o, n=64):
+        assert L.mrx_reduce_shape(_ptrs(*ptrs), len(ptrs), n, dt, o, f, 21) == 0
+        return {"vec": f[0], "realign": f[1], "bytes": f[2], "head": f[3], "npacks": f[4],
+                "shift": [f[5 + r] for r in range(len(ptrs))]}
+
+    assert shape((a, b), 0, out) == {"vec": 1, "realign": 0, "bytes": 0, "head": 0, "npacks": 8, "shift": [0, 0]}
+    s = shape((a + 2, b + 6), 0, out + 2)           # bf16, element-aligned, two phases: realigned packs
+    assert (s["vec"], s["realign"], s["bytes"], s["head"], s["shift"]) == (1, 1, 0, 7, [0, 4])
+    assert shape((a + 1, b), 0, out)["bytes"] == 1  # bf16 buffer at an odd byte: byte accesses
+    assert shape((a, b), 0, out + 1)["bytes"] == 1
+    assert shape((a, b + 2), 2, out)["bytes"] == 1  # fp32 buffer 2 bytes in
+    s = shape((a + 4, b + 12), 2, out + 8)          # fp32 on its grid, three phases
+    assert (s["realign"], s["bytes"], s["shift"]) == (1, 0, [12, 4])
+    # argument errors are still the documented ones
+    assert L.mr_allreduce_sum(_ptrs(a + 1, None), 2, 64, 0, out, 0, None) == EINVAL
+    assert L.mr_allreduce_sum(_ptrs(a + 1, b), 2, 64, 0, a + 3, 0, None) == EALIAS
