@@ -407,6 +407,22 @@ def main():
             log(f"[bench] twoshot ({sync}): {t2 * 1e6:.2f} us/launch, {algo / t2 / 1e9:.1f} GB/s (metric bytes), "
                 f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")
         mr.set_option("twoshot_sync", "auto")
+        # reference: the same two phases as two launches (one-shot into a stage tensor, then a plain copy
+        # of it into out by the gather kernel), same rotating sets -- what the in-kernel hand-off is
+        # measured against
+        stages = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in sets]
+        two_launch = []
+        for (b, o), stg in zip(sets, stages):
+            red = mr.prepare_allreduce(b, stg, "oneshot")
+            cp = mr.prepare_allgather_shards([stg], o)
+            two_launch.append(lambda red=red, cp=cp: (red(), cp()))
+        ms_tl = time_steps(two_launch, K, args.warmup, stream)
+        t_tl = ms_tl / K * 1e-3
+        paths["twoshot_two_launch_reference"] = {"us": t_tl * 1e6, "GBps_actual_bytes": actual2 / t_tl / 1e9,
+                                                 "note": "one-shot into a stage tensor, then a copy kernel; two "
+                                                         "launches per step, no in-kernel hand-off"}
+        log(f"[bench] two-launch reference (one-shot into a stage, then a copy): {t_tl * 1e6:.2f} us/step")
+        del stages, two_launch
         # param-contiguous scatter: W=8, G=4, P=64 log-uniform splits, bf16 random bits
         c4 = workloads.FSDP_SPLITS_W8_G4_P64
         splits = [int(x) for x in workloads.log_uniform_splits(c4["seed"], c4["P"])]

@@ -32,7 +32,7 @@ typedef struct ihipStream_t* mr_stream; /* == hipStream_t */
 
 typedef int mr_status;
 #define MR_OK 0
-#define MR_ERR_INVALID_ARG (-1) /* null or misaligned pointer, W/G/P out of range, size overflow */
+#define MR_ERR_INVALID_ARG (-1) /* null pointer, W/G/P out of range, size overflow */
 #define MR_ERR_DTYPE (-2)       /* dtype not supported by this operation */
 #define MR_ERR_ALIAS (-3)       /* output partially overlaps an input */
 #define MR_ERR_WORKSPACE (-4)   /* two-shot workspace missing or too small (barrier errors: mr_workspace_check) */
@@ -67,19 +67,28 @@ int mr_last_hip_error(void);
  * in both modes.
  *
  *  bufs   host array of W device pointers, each to n contiguous elements of `dtype` (read only).
- *         Pointers may repeat.  Every pointer (and out) must be a multiple of the element size, else
- *         MR_ERR_INVALID_ARG; beyond that any alignment is accepted: when every pointer and out have
- *         the same address modulo 16 the kernels use 16-byte loads, otherwise a slower element-wise
- *         path.
+ *         Pointers may repeat.  Any alignment is accepted.  When every pointer and out have the same
+ *         address modulo 16 the kernels use aligned 16-byte loads and stores; when they are all
+ *         multiples of the element size but their 16-byte phases differ, each input pack is realigned
+ *         in registers from the two aligned packs it straddles (slower: about 30 us instead of 25 us
+ *         for W=8 bf16 at 16 MiB); when some pointer is not a multiple of the element size, the call
+ *         runs element by element with single-byte loads and stores only (much slower), never an
+ *         unaligned multi-byte access.
  *  W      1 .. MR_MAX_W.
  *  n      elements per buffer; n == 0 is a successful no-op.
  *  dtype  MR_BF16, MR_FP16 or MR_FP32 (output has the same dtype); MR_INT32 -> MR_ERR_DTYPE.
  *  out    device pointer to n elements.  out == bufs[k] (exactly) is allowed (in place); any other
  *         overlap with an input -> MR_ERR_ALIAS.
  *  mode   MR_ONESHOT: one pass, W reads and one write per element.
- *         MR_TWOSHOT: phase 1 reduces each of the W chunks of ceil(n/W) elements (rounded up to 16
- *         bytes) into a stage buffer, an intra-GPU release/acquire flag barrier orders the phases,
- *         phase 2 copies the stage into out.  Needs a workspace (see below).
+ *         MR_TWOSHOT: phase 1 reduces the message into a stage buffer, share by share, an intra-GPU
+ *         flag hand-off orders the phases, phase 2 copies the stage into out; the result is the
+ *         same.  The shares are whole 16-byte packs of the aligned body (on out's 16-byte grid):
+ *         W chunks of ceil(packs/W) packs each (the last ones may be short or empty), or, for the
+ *         per-tile hand-off from 16 MiB per rank buffer (16-byte path, W <= 8), one run of 16 KiB
+ *         units per XCD; the few elements before out's first 16-byte boundary and after its last
+ *         whole pack are reduced with the first share.  (mr_reduce_scatter_sum's chunks, which are
+ *         defined on element indices, coincide with these when n is a multiple of 16 bytes and out
+ *         is 16-byte aligned.)  Needs a workspace (see below).
  *  stream hipStream_t to enqueue on.
  */
 mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out,
@@ -107,8 +116,10 @@ mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dt
  *          first is enqueued).
  *  dtype   any mr_dtype (element size 2 or 4 bytes).
  *  out     device pointer, W*T elements.  Any overlap with src -> MR_ERR_ALIAS.
- *  src and out must be multiples of the element size (else MR_ERR_INVALID_ARG); their 16-byte phases
- *  are free.  All offsets are 64-bit; buffers beyond 2^31 bytes are supported.
+ *  Any alignment of src and out is accepted: pieces whose source and destination share a 16-byte
+ *  phase are copied as aligned 16-byte packs, others as destination-aligned packs realigned in
+ *  registers, and pointers that are not multiples of the element size make the launch work in bytes
+ *  (byte-granular edges).  All offsets are 64-bit; buffers beyond 2^31 bytes are supported.
  */
 mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, const uint64_t* splits,
                                     int P, mr_dtype dtype, void* out, mr_stream stream);
@@ -182,7 +193,7 @@ mr_status mr_allreduce_sum_noalloc(const void* const* bufs, int W, size_t n, mr_
 /*
  * All-gathers from W separate rank shards (each a device buffer of T elements), one launch each.
  * Bit copies of any dtype; 1 <= W <= MR_MAX_TABLE_W; shards may not overlap any output (MR_ERR_ALIAS).
- * Every shard and output pointer must be a multiple of the element size (else MR_ERR_INVALID_ARG).
+ * Shard and output pointers may have any alignment (as for mr_allgather_param_contig).
  *
  * mr_allgather_into_tensor:  rank-major gather (torch.distributed.all_gather_into_tensor's layout):
  *                            out[r*T + j] = shards[r][j]; out holds W*T elements.
