@@ -74,16 +74,16 @@ std::map<std::pair<int, hipStream_t>, std::vector<char*>> g_retired;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Smallest workspace whose layout (barrier words, flags, stage) holds a stage of n elements plus 16
+// Smallest workspace whose layout (barrier words, flags, stage) holds a stage of n elements plus 256
 // bytes of alignment slack.  Its flag capacity (bytes/256 words) covers the largest plan for n: one
 // flag per 256-element tile on the element-wise path, plus one per chunk for ragged chunks.
 size_t ws_bytes_for(size_t n, int esize) {
-  const size_t base = mr::kCtrlBytes + n * static_cast<size_t>(esize) + 16 + 256;
+  const size_t base = mr::kCtrlBytes + n * static_cast<size_t>(esize) + mr::kStageSlack + 16;
   return round_up(base + base / 63 + 4096, 4096);
 }
 
 bool ws_fits(size_t bytes, size_t n, int esize, size_t flags_needed) {
-  return mr::ws_stage_offset(bytes) + n * static_cast<size_t>(esize) + 16 <= bytes &&
+  return mr::ws_stage_offset(bytes) + n * static_cast<size_t>(esize) + mr::kStageSlack <= bytes &&
          flags_needed <= mr::ws_flag_words(bytes);
 }
 
@@ -223,8 +223,11 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
       mr_status s = get_workspace(st, n, es, flags_needed, &ws);
       if (s != MR_OK) return s;
     }
-    // the stage shares out's 16-byte phase so that its body is 16-byte aligned too
-    char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (sh.vec ? (po & 15u) : 0);
+    // The stage shares out's 16-byte phase, so its body is 16-byte aligned too, and the body starts on a
+    // 256-byte boundary, so units of 16 KiB never share a cache line: each stage line is then loaded
+    // by one workgroup, once per launch.
+    const size_t hb = sh.vec ? sh.head * static_cast<size_t>(es) : 0;
+    char* stage = ws.base + mr::ws_stage_offset(ws.bytes) + (hb ? mr::kStageSlack - hb : 0);
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws.base + mr::kCtrlBytes);
     if (g_trace)
       std::fprintf(stderr, "[mr] allreduce twoshot W=%d n=%zu dtype=%d vec=%d sync=%u chunk=%zu tile=%u t1=%u t2=%u "

@@ -18,9 +18,11 @@ inline int elem_size(mr_dtype d) { return (d == MR_BF16 || d == MR_FP16) ? 2 : 4
 //   [0, 16 KiB)                 Ctrl: ticket counters and barrier words, one 256-byte line each
 //   [16 KiB, stage_off)         producer flags, one u32 per phase-1 tile (capacity bytes/256 tiles,
 //                               enough for the element-wise path's one tile per 256 elements)
-//   [stage_off, bytes)          stage buffer (n elements + 16 bytes of alignment slack)
+//   [stage_off, bytes)          stage buffer (n elements + kStageSlack bytes of alignment slack: the
+//                               stage's 16-byte body starts at stage_off + 256)
 // Every word before stage_off is zero between calls; the calls restore that themselves.
 constexpr size_t kCtrlBytes = 16384;
+constexpr size_t kStageSlack = 256;
 
 struct Ctrl {
   uint32_t claim[MR_MAX_W][64];  // per-chunk ticket counters (grid barrier: phase-1 tile pools)

@@ -20,7 +20,7 @@
 namespace {
 
 // Two-shot of up to MR_NOALLOC_MAX_BYTES per rank buffer: the workspace layout of that size fits
-// (barrier words 16 KiB, one flag word per 256 bytes, stage, 16 bytes of alignment slack).
+// (barrier words 16 KiB, one flag word per 256 bytes, stage, 256 bytes of alignment slack).
 constexpr size_t kScratchBytes = size_t(34) << 20;
 static_assert(MR_NOALLOC_MAX_BYTES == (size_t(32) << 20), "limit documented in mr.h");
 

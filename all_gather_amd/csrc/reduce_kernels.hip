@@ -622,8 +622,12 @@ __global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* 
 // waits until the XCD's L2 has acknowledged every one of them (vmcnt 0) and then publishes the unit by
 // exchanging its flag word for 1 + the XCC id it runs on (a relaxed agent-scope atomic).  A copier
 // polls the flags of its group; a flag holding 1 + its own XCC id means the unit sits in the L2 it
-// reads through, so it reads the stage with L1-bypassing (sc0) loads.  One L2 serves every CU of an XCD,
-// so that is all the ordering the copy needs; no whole-L2 write-back and no write-through stores.
+// reads through.  One L2 serves every CU of an XCD, so the stores need no write-back past it and no
+// write-through.  The copier's loads (sc0, workgroup-scope coherence) may be served by its CU's L1, but
+// no L1 can hold an old copy of the unit: stream order already makes a launch see every earlier write,
+// so an L1 could only return a stage line that the same CU loaded earlier in this launch, and every
+// stage line is loaded once per launch, by the copier of its unit, after the flag (units start on
+// 256-byte boundaries of the stage, so no cache line holds bytes of two units).
 //
 // Nothing rests on where the dispatcher places workgroups or in which order it starts them.  A unit
 // whose flag names another XCD, or whose producer has not published within the spin limit, is
@@ -641,7 +645,7 @@ __global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* 
 // load, and copies interleaved into the dispatch order after a lag of 24-192 units per run all
 // measured the same or slower; the interleaved copies wait and hold slots.
 constexpr uint32_t kTaken = 0xffffffffu;  // flag claimed by a copier that stopped waiting
-constexpr int kXcdStageLoadAux = 1;       // sc0: the stage is read through this XCD's L2, past the CU's L1
+constexpr int kXcdStageLoadAux = 1;       // sc0: workgroup-scope coherent stage loads (see above)
 
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t x;

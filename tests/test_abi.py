@@ -159,7 +159,7 @@ def test_workspace_rule_covers_every_two_shot_plan(L, es, dt):
             stage_off = 16384 + ((flags_cap * 4 + 255) // 256) * 256
             tiles = -(-(-(-n // W)) // 256)
             assert W * tiles <= flags_cap, (n, W)
-            assert stage_off + n * es + 16 <= b, (n, W)
+            assert stage_off + n * es + 256 <= b, (n, W)
 
 
 def test_options_validate_and_round_trip(L):

@@ -148,22 +148,33 @@ def test_oneshot_equals_twoshot_and_is_deterministic():
     assert mr.workspace_check() == 0
 
 
-@pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last", "tile:wide_pair"])
+@pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last", "tile:wide_pair", "tile:wide_pair:3"])
 def test_twoshot_stale_stage_is_never_read(sync):
     """Two input sets alternate on one caller-owned workspace, so when a call starts its stage still
     holds the previous call's (different) sums: a phase-2 copy that ran ahead of its phase-1 producer
-    would surface as a mismatch."""
+    would surface as a mismatch.  The last case shifts every pointer by 3 elements (a common 6-byte
+    phase: 16-byte body after an element-wise head), so the XCD-local kernel's units start 6 bytes
+    past a 16-byte boundary of out."""
     W, n = 8, 4_194_304 + 24
+    sync, _, shape = sync.partition(":")
+    shape, _, off = shape.partition(":")
+    off = int(off or 0)
     sets = [workloads.rank_buffers(15 + k, W, n, "bf16", "normal") for k in range(2)]
     wants = [oracle.allreduce_sum_ref(b, "bf16") for b in sets]
-    dsets = [[to_dev(b, "bf16") for b in s] for s in sets]
+    dsets = []
+    for s_ in sets:
+        views = []
+        for b in s_:
+            full = torch.empty(n + 8, dtype=torch.bfloat16, device=device())
+            full[off:off + n].copy_(to_dev(b, "bf16"))
+            views.append(full[off:off + n])
+        dsets.append(views)
     ws = torch.empty(mr.workspace_bytes(W, n, "bf16"), dtype=torch.uint8, device=device())
     mr.set_workspace(ws)
-    sync, _, shape = sync.partition(":")
     mr.set_option("twoshot_sync", sync)
     mr.set_option("tile_shape", shape or "auto")
     try:
-        outs = [torch.empty(n, dtype=torch.bfloat16, device=device()) for _ in range(2)]
+        outs = [torch.empty(n + 8, dtype=torch.bfloat16, device=device())[off:off + n] for _ in range(2)]
         for i in range(200):
             k = i % 2
             outs[k].fill_(0)
