@@ -172,9 +172,9 @@ mr::TwoShotPlan twoshot_plan_for(int W, const mr::ReduceShape& sh, int es, uint3
                                  bool wait_free) {
   uint32_t sync = mr::twoshot_sync_for(sh.n * static_cast<size_t>(es), sync_opt);
   uint32_t shape = shape_opt;
-  if (wait_free) {
+  if (wait_free) {  // the last arriver, on ticketed tiles or XCD-local units by size: nothing ever waits
     shape = mr::kShapeAuto;
-    sync = mr::twoshot_xcd_units(sh.vec, W, sh.npacks, mr::kSyncTile, shape) ? mr::kSyncTile : mr::kSyncLast;
+    sync = mr::kSyncLast;
   }
   return mr::plan_twoshot(W, sh, sync, g_spin_limit.load(), shape);
 }
@@ -182,9 +182,8 @@ mr::TwoShotPlan twoshot_plan_for(int W, const mr::ReduceShape& sh, int es, uint3
 // Alias check, 16-byte layout of the call, and the one-shot or two-shot launch.  `ins` are already
 // validated non-null.
 // `fixed`: a workspace the call must use instead of the stream's (the no-allocation entry point);
-// `wait_free`: take only the two-shot hand-offs that leave every barrier word and flag at zero when a
-// launch ends and never produce an invalid output (the last arriver, which never waits, and the
-// XCD-local units, which recompute instead of failing).
+// `wait_free`: take only the last-arriver hand-off (ticketed tiles or XCD-local units by size), in which
+// no workgroup ever waits: every word is back at zero when a launch ends and no output is ever invalid.
 mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype, char* out, mr_mode mode,
                         hipStream_t st, const Workspace* fixed = nullptr, bool wait_free = false) {
   const int es = mr::elem_size(dtype);
@@ -211,10 +210,8 @@ mr_status reduce_launch(const char* const* ins, int W, size_t n, mr_dtype dtype,
     e = mr::launch_oneshot(in, W, dtype, out, sh, shape, st);
   } else {
     const mr::TwoShotPlan pl = twoshot_plan_for(W, sh, es, g_twoshot_sync.load(), g_tile_shape.load(), wait_free);
-    const uint64_t grid = pl.xcd ? uint64_t{mr::kXcds} * (pl.run_padded + pl.run_padded / mr::kXcdGroup)
-                                 : static_cast<uint64_t>(pl.chunks) * (pl.t1 + pl.t2);
-    if (grid >= (1ull << 24)) return MR_ERR_INVALID_ARG;
-    const size_t flags_needed = pl.xcd ? pl.units : static_cast<size_t>(pl.chunks) * pl.t1;
+    if (mr::twoshot_grid(pl) >= (1ull << 24)) return MR_ERR_INVALID_ARG;
+    const size_t flags_needed = mr::twoshot_flag_words(pl);
     Workspace ws;
     if (fixed) {
       if (!ws_fits(fixed->bytes, n, es, flags_needed)) return MR_ERR_WORKSPACE;
@@ -439,7 +436,7 @@ const char* mr_status_string(mr_status s) {
 
 int mr_last_hip_error(void) { return g_last_hip_error; }
 
-int mr_version(void) { return 103; }
+int mr_version(void) { return 104; }
 
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
   if (W < 1 || W > MR_MAX_W || !is_float(dtype)) return 0;
@@ -595,11 +592,9 @@ int mrx_twoshot_plan(int W, size_t n, int dtype, uintptr_t out_addr, int same_ph
   const mr::ReduceShape sh = reduce_shape(n, es, out_addr, same_phase != 0);
   const mr::TwoShotPlan pl = twoshot_plan_for(W, sh, es, static_cast<uint32_t>(sync_opt), static_cast<uint32_t>(shape_opt),
                                               wait_free != 0);
-  const uint64_t grid = pl.xcd ? uint64_t{mr::kXcds} * (pl.run_padded + pl.run_padded / mr::kXcdGroup)
-                               : static_cast<uint64_t>(pl.chunks) * (pl.sync == mr::kSyncLast ? pl.t1 : pl.t1 + pl.t2);
   const uint64_t v[16] = {pl.xcd, pl.units, pl.run, pl.run_padded, pl.chunks, pl.chunk_units, pl.t1, pl.t2, pl.ratio,
-                          pl.unit1, pl.sync, static_cast<uint64_t>(sh.vec), sh.head, sh.npacks, grid,
-                          pl.xcd ? pl.units : static_cast<uint64_t>(pl.chunks) * pl.t1};
+                          pl.unit1, pl.sync, static_cast<uint64_t>(sh.vec), sh.head, sh.npacks, mr::twoshot_grid(pl),
+                          mr::twoshot_flag_words(pl)};
   for (int i = 0; i < 16; ++i) f[i] = v[i];
   return 0;
 }

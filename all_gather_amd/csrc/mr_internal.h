@@ -86,21 +86,34 @@ inline uint32_t twoshot_tile_packs(size_t npacks, uint32_t sync, uint32_t forced
                                                                           : kShapeNarrow;
   return shape == kShapeNarrow ? 64u : shape == kShapeMedium ? 256u : kTwoShotWideTile;
 }
-// The per-tile hand-off runs on XCD-local units (twoshot_xcd) on the 16-byte path for W <= 8, from
-// 1 Mi packs (16 MiB per rank buffer) up, or at any size under MR_TILE_WIDE_PAIR.  Below 16 MiB the
-// ticketed chunk tiles lead (8 MiB bf16: 20.1 against 21.6 us).
+// XCD-local units (twoshot_xcd, 16-byte path, W <= 8).  Under the last-arriver hand-off they lead from
+// 512 Ki packs (8 MiB per rank buffer) up; under per-tile flags (copier workgroups) from 1 Mi packs to
+// 4 Mi packs (16 to 64 MiB), beyond which the ticketed chunk tiles lead.  MR_TILE_WIDE_PAIR forces them
+// for either hand-off at any size.  Same-GPU A/B, W=8 bf16, rotating sets, best of three (us):
+//   per rank              4 MiB   8 MiB   16 MiB   32 MiB   64 MiB   256 MiB
+//   XCD, last arriver     12.72   17.46   31.85    62.38    122.2    463.2
+//   XCD, copiers          13.24   21.13   35.97    63.64    118.3    472.7
+//   ticketed, last        11.54   19.06   37.33    71.75    143.4    573.5
+//   ticketed, tile flags  15.51   19.87   35.63    66.37    124.1    454.6
+//   two launches          13.01   19.75   33.11    62.93    122.1    490.0
 constexpr uint32_t kXcds = 8;      // XCDs of an MI355X: one run of units each
 constexpr uint32_t kXcdGroup = 4;  // units per phase-2 copy
+#ifndef MR_XCD_LAST_GROUP
+#define MR_XCD_LAST_GROUP 4
+#endif
+constexpr uint32_t kXcdLastGroup = MR_XCD_LAST_GROUP;  // units per copy under the last-arriver hand-off
 inline bool twoshot_xcd_units(int vec, int W, size_t npacks, uint32_t sync, uint32_t forced) {
-  if (!vec || W > 8 || sync != kSyncTile) return false;
-  return forced == kShapeWidePair || (forced == kShapeAuto && npacks >= (size_t(1) << 20));
+  if (!vec || W > 8 || (sync != kSyncTile && sync != kSyncLast)) return false;
+  if (forced == kShapeWidePair) return true;
+  if (forced != kShapeAuto) return false;
+  if (sync == kSyncLast) return npacks >= (size_t(1) << 19);
+  return npacks >= (size_t(1) << 20) && npacks <= (size_t(1) << 22);
 }
-// Two-shot hand-off under MR_TWOSHOT_SYNC_AUTO: the last-arriver hand-off leads below 16 MiB per rank
-// (12.3 vs 16.4 us for per-tile flags at 4 MiB, W=8 bf16), per-tile flags above (125 vs 149 us at
-// 64 MiB).
+// Two-shot hand-off under MR_TWOSHOT_SYNC_AUTO: the last arriver up to 32 MiB per rank buffer (ticketed
+// tiles below 8 MiB, XCD-local units from 8 MiB), per-tile flags above (table above).
 inline uint32_t twoshot_sync_for(size_t bytes, uint32_t sync) {
   if (sync != kSyncAuto) return sync;
-  return bytes < (size_t(16) << 20) ? kSyncLast : kSyncTile;
+  return bytes <= (size_t(32) << 20) ? kSyncLast : kSyncTile;
 }
 
 struct RankPtrs {
@@ -142,6 +155,17 @@ struct TwoShotPlan {
   uint32_t run_padded;   // run rounded up to whole copy groups
   size_t units;          // units of the message (16 KiB of output each)
 };
+
+// Workgroups of a two-shot launch, and the flag words it uses (one per phase-1 tile; XCD-local units:
+// one per unit, or with the last-arriver hand-off one 64-bit arrival word per copy group of each run).
+inline uint64_t twoshot_grid(const TwoShotPlan& pl) {
+  if (pl.xcd) return uint64_t{kXcds} * (pl.sync == kSyncLast ? pl.run : pl.run_padded + pl.run_padded / kXcdGroup);
+  return uint64_t{pl.chunks} * (pl.sync == kSyncLast ? pl.t1 : pl.t1 + pl.t2);
+}
+inline size_t twoshot_flag_words(const TwoShotPlan& pl) {
+  if (pl.xcd) return pl.sync == kSyncLast ? 2 * size_t{kXcds} * ((pl.run + kXcdLastGroup - 1) / kXcdLastGroup) : pl.units;
+  return size_t{pl.chunks} * pl.t1;
+}
 
 hipError_t launch_oneshot(const RankPtrs& in, int W, mr_dtype dt, char* out, const ReduceShape& sh,
                           uint32_t shape, hipStream_t st);  // shape: TileShape, already resolved

@@ -679,19 +679,34 @@ __device__ __forceinline__ uint32_t settle_unit(Ctrl* ctrl, uint32_t* flags, siz
   return 2u;
 }
 
-template <typename D, int W>
+// Last-arriver form (LAST; no copier workgroups and no waiting): the 64-bit word g of run x in the flag
+// area is the arrival word of copy group g (kXcdLastGroup units) of that run.  Its low 8 bits count
+// the members that have published, and a 4-bit field per XCC (from bit 8) counts those that ran there.
+// The producer whose arrival completes the group re-arms the word and copies the group from the stage
+// at once; if some member ran on another XCC it recomputes the group from the rank buffers instead
+// (error word bit 2, output valid).
+__device__ __forceinline__ uint64_t xcd_arrival(uint32_t xcc) {
+  return 1u + (xcc < kXcds ? uint64_t{1} << (8 + 4 * xcc) : 0u);
+}
+static_assert(8 + 4 * kXcds <= 64 && kXcdLastGroup >= 1 && kXcdLastGroup <= 15, "arrival word fields");
+
+template <typename D, int W, bool LAST>
 __global__ __launch_bounds__(kOneShotBlock) void twoshot_xcd(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
                                                              uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
-  constexpr int B = kOneShotBlock, U = OneShotU<W>::value, R = static_cast<int>(kXcdGroup);
+  constexpr int B = kOneShotBlock, U = OneShotU<W>::value;
+  constexpr int R = static_cast<int>(LAST ? kXcdLastGroup : kXcdGroup);  // units per copy
   constexpr size_t UP = static_cast<size_t>(B) * U;  // packs per unit
   static_assert(U == 4, "wide units");
   const size_t hb = sh.head * D::kSize;
   const uint32_t x = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
   const size_t run0 = static_cast<size_t>(x) * pl.run;  // first unit of this run
+  const size_t in_run = run0 < pl.units ? (pl.units - run0 < pl.run ? pl.units - run0 : pl.run) : 0;
   u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
+  __shared__ uint32_t s_mode[R];
+  uint32_t g;  // copy group of this run
   if (s < pl.run_padded) {
     const size_t u = run0 + s;
-    if (s >= pl.run || u >= pl.units) return;  // padding
+    if (s >= in_run) return;  // padding
     const size_t first = u * UP;
     const i32x4 rs = make_rsrc(stage + hb + first * 16, static_cast<uint32_t>(UP * 16));
     reduce_tile<D, W, B, U>(in, hb, first, sh.npacks, [&](int, size_t i, const u32x4& o) {
@@ -700,19 +715,41 @@ __global__ __launch_bounds__(kOneShotBlock) void twoshot_xcd(RankPtrs in, char* 
     if (u == 0) reduce_edges<D, W, false>(in, out, sh);  // the few elements outside the packs: straight to out
     __builtin_amdgcn_s_waitcnt(0x0f70);                 // vmcnt(0): the L2 holds this lane's stage stores
     __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t old = __hip_atomic_exchange(&flags[u], 1u + xcc_id(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == kTaken) __hip_atomic_store(&flags[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (!LAST) {
+      if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_exchange(&flags[u], 1u + xcc_id(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == kTaken) __hip_atomic_store(&flags[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    } else {
+      g = s / R;
+      if (threadIdx.x == 0) {
+        const uint32_t members = in_run - static_cast<size_t>(g) * R < R ? static_cast<uint32_t>(in_run - static_cast<size_t>(g) * R) : R;
+        uint64_t* word = reinterpret_cast<uint64_t*>(flags) + static_cast<size_t>(x) * ((pl.run + R - 1) / R) + g;
+        const uint32_t me = xcc_id();
+        const uint64_t add = xcd_arrival(me);
+        const uint64_t old = __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t go = 0u;
+        if ((old & 0xffu) == members - 1) {  // every member has published: re-arm, then copy the group
+          __hip_atomic_store(word, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          go = me < kXcds && (((old + add) >> (8 + 4 * me)) & 15u) == members ? 1u : 2u;
+          if (go == 2u) __hip_atomic_fetch_or(&ctrl->err[0], 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) s_mode[r] = static_cast<uint32_t>(r) < members ? go : 0u;
+      }
+      __syncthreads();
+      if (s_mode[0] == 0u) return;
     }
-    return;
+  } else {
+    if constexpr (LAST) return;  // not launched: the last-arriver grid holds producers only
+    g = s - pl.run_padded;
+    if (threadIdx.x < R) {
+      const size_t i = static_cast<size_t>(g) * R + threadIdx.x;
+      s_mode[threadIdx.x] = i < in_run ? settle_unit(ctrl, flags, run0 + i, pl.spin_limit) : 0u;
+    }
+    __syncthreads();
   }
-  const uint32_t g = s - pl.run_padded;  // copy group of this run
-  __shared__ uint32_t s_mode[R];
-  if (threadIdx.x < R) {
-    const size_t i = static_cast<size_t>(g) * R + threadIdx.x;
-    s_mode[threadIdx.x] = (i < pl.run && run0 + i < pl.units) ? settle_unit(ctrl, flags, run0 + i, pl.spin_limit) : 0u;
-  }
-  __syncthreads();
   const size_t first = (run0 + static_cast<size_t>(g) * R) * UP;
   bool from_stage = true;
 #pragma unroll
@@ -903,13 +940,18 @@ template <typename D, int W>
 hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uint32_t* flags, const ReduceShape& sh,
                      const TwoShotPlan& pl, hipStream_t st) {
   if constexpr (W <= 8) {
+    if (sh.vec && pl.xcd && pl.sync == kSyncLast) {
+      hipLaunchKernelGGL((twoshot_xcd<D, W, true>), dim3(static_cast<unsigned>(twoshot_grid(pl))), dim3(kOneShotBlock),
+                         0, st, in, out, stage, ctrl, flags, sh, pl);
+      return hipGetLastError();
+    }
     if (sh.vec && pl.xcd) {
-      const unsigned g = kXcds * (pl.run_padded + pl.run_padded / kXcdGroup);
-      hipLaunchKernelGGL((twoshot_xcd<D, W>), dim3(g), dim3(kOneShotBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
+      hipLaunchKernelGGL((twoshot_xcd<D, W, false>), dim3(static_cast<unsigned>(twoshot_grid(pl))),
+                         dim3(kOneShotBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
       return hipGetLastError();
     }
   }
-  const unsigned grid = pl.chunks * (pl.sync == kSyncLast ? pl.t1 : pl.t1 + pl.t2);
+  const unsigned grid = static_cast<unsigned>(twoshot_grid(pl));
   if (sh.vec && sh.realign) {  // the planner fixes the last-arriver hand-off and wide tiles here
     hipLaunchKernelGGL((twoshot_vec<D, W, kTBlock, kSyncLast, true>), dim3(grid), dim3(kTBlock), 0, st, in, out, stage,
                        ctrl, flags, sh, pl);

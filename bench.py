@@ -390,10 +390,14 @@ def main():
                                          "elements": cnt}
         log(f"[bench] reduce_scatter (rank 0 share, {cnt} elements): {t_rs * 1e6:.2f} us/launch, "
             f"{rs_bytes / t_rs / 1e9:.1f} GB/s")
-        # two-shot, rotating sets, under each phase hand-off
+        # two-shot, rotating sets, under the default hand-off (at this size the last arriver on XCD-local
+        # units) and under each other one
         two = [mr.prepare_allreduce(b, o, "twoshot") for b, o in sets]
         actual2 = (W + 3) * n * s
-        for sync in ("tile", "chunk", "grid", "last"):
+        kernels = {"auto": "twoshot_xcd<last arriver> (XCD-local units, the default at this size)",
+                   "tile": "twoshot_xcd<copier workgroups> (XCD-local units)",
+                   "chunk": "twoshot_vec<chunk barrier>", "grid": "twoshot_vec<grid barrier>"}
+        for sync in ("auto", "tile", "chunk", "grid"):
             mr.set_option("twoshot_sync", sync)
             two[0]()
             torch.cuda.synchronize()
@@ -402,7 +406,7 @@ def main():
             paths[f"twoshot_{sync}"] = {"us": t2 * 1e6, "GBps_metric_bytes": algo / t2 / 1e9,
                                         "GBps_actual_bytes": actual2 / t2 / 1e9, "actual_bytes": actual2,
                                         "frac_actual_bytes": actual2 / t2 / 1e9 / PEAK_GBS,
-                                        "kernel": "twoshot_xcd (XCD-local units)" if sync == "tile" else "twoshot_vec",
+                                        "kernel": kernels[sync],
                                         "barrier_error_word": mr.workspace_check()}
             log(f"[bench] twoshot ({sync}): {t2 * 1e6:.2f} us/launch, {algo / t2 / 1e9:.1f} GB/s (metric bytes), "
                 f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")

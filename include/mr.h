@@ -83,10 +83,10 @@ int mr_last_hip_error(void);
  *         MR_TWOSHOT: phase 1 reduces the message into a stage buffer, share by share, an intra-GPU
  *         flag hand-off orders the phases, phase 2 copies the stage into out; the result is the
  *         same.  The shares are whole 16-byte packs of the aligned body (on out's 16-byte grid):
- *         W chunks of ceil(packs/W) packs each (the last ones may be short or empty), or, for the
- *         per-tile hand-off from 16 MiB per rank buffer (16-byte path, W <= 8), one run of 16 KiB
- *         units per XCD; the few elements before out's first 16-byte boundary and after its last
- *         whole pack are reduced with the first share.  (mr_reduce_scatter_sum's chunks, which are
+ *         W chunks of ceil(packs/W) packs each (the last ones may be short or empty), or, on the
+ *         16-byte path with W <= 8 (the last arriver from 8 MiB per rank buffer, per-tile flags
+ *         from 16 to 64 MiB), one run of 16 KiB units per XCD; the few elements before out's first
+ *         16-byte boundary and after its last whole pack are reduced with the first share.  (mr_reduce_scatter_sum's chunks, which are
  *         defined on element indices, coincide with these when n is a multiple of 16 bytes and out
  *         is 16-byte aligned.)  Needs a workspace (see below).
  *  stream hipStream_t to enqueue on.
@@ -178,10 +178,10 @@ mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dty
  *    ends; the first call on a device looks its address up and clears it on `stream`;
  *  - a rank buffer larger than MR_NOALLOC_MAX_BYTES (n * element size) -> MR_ERR_WORKSPACE, nothing
  *    enqueued;
- *  - the two-shot hand-off is always chosen from the message size (the last arriver below 16 MiB per
- *    rank buffer, the XCD-local units from 16 MiB on the 16-byte path with W <= 8), ignoring
- *    MR_OPT_TWOSHOT_SYNC and MR_OPT_TILE_SHAPE, because those hand-offs never leave a barrier word set
- *    after a launch and never produce an invalid output; there is no error word to check;
+ *  - the two-shot hand-off is always the last arriver (on chunk tiles below 8 MiB per rank buffer, on
+ *    XCD-local units from 8 MiB on the 16-byte path with W <= 8), ignoring MR_OPT_TWOSHOT_SYNC and
+ *    MR_OPT_TILE_SHAPE: no workgroup of it ever waits, so it never leaves a barrier word set after a
+ *    launch and never produces an invalid output; there is no error word to check;
  *  - every call on one GPU shares that GPU's array: two-shot calls that overlap in time on one GPU (on
  *    two streams, or from two host threads) race and give undefined output.  One-shot calls use no
  *    workspace and never race.
@@ -251,7 +251,8 @@ mr_status mr_allgather_param_contig_shards(const void* const* shards, int W, int
  *                     OR: 0 = no error; bit 0 = a phase-2 workgroup gave up waiting for phase 1, so
  *                     that call's output is not valid; bits 1 and 2 = the XCD-local two-shot
  *                     recomputed units from the rank buffers (after a wait gave up / because a
- *                     unit's producer ran on another XCD), output valid.  Returns MR_ERR_WORKSPACE if
+ *                     unit's producer ran on another XCD than the workgroup that copies it), output
+ *                     valid.  Returns MR_ERR_WORKSPACE if
  *                     there is no workspace for the stream.
  */
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype);
@@ -262,7 +263,7 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  * Process-wide options (thread-safe; they apply to calls made after the change).
  *
  * MR_OPT_TWOSHOT_SYNC  how a two-shot phase-2 tile waits for phase 1 (all give identical results):
- *   MR_TWOSHOT_SYNC_AUTO  (default) LAST below 16 MiB per rank buffer, TILE from 16 MiB up;
+ *   MR_TWOSHOT_SYNC_AUTO  (default) LAST up to 32 MiB per rank buffer, TILE above;
  *   MR_TWOSHOT_SYNC_TILE  per-tile producer flags: a phase-2 tile waits only for the
  *                         phase-1 tiles it copies (the per-block flag hand-off of the custom
  *                         allreduce page's block_barrier, applied to the two phases);
@@ -270,6 +271,8 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  *   MR_TWOSHOT_SYNC_GRID  grid barrier: waits for every phase-1 tile of every chunk;
  *   MR_TWOSHOT_SYNC_LAST  no waiting: each group of phase-1 tiles counts its releases, and the
  *                         workgroup whose release completes the group copies it.
+ *   Under TILE (16 to 64 MiB per rank buffer) and LAST (from 8 MiB) the 16-byte path with W <= 8
+ *   runs on XCD-local units (16 KiB of output each, one run per XCD); otherwise on W chunks.
  * MR_OPT_SPIN_LIMIT    polls a waiting workgroup makes before it gives up and sets the workspace error
  *                      word (see mr_workspace_check); default 2^22.  A value of 0 makes every wait
  *                      that is not already satisfied give up at once (for testing error handling).
@@ -283,7 +286,8 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  *   MR_TILE_MEDIUM one-shot 256 x 1, two-shot 256-pack tiles;
  *   MR_TILE_NARROW one-shot 64 x 1, two-shot 64-pack tiles;
  *   MR_TILE_WIDE_PAIR  one-shot: each workgroup reduces two wide tiles and stores both after the
- *                  second (W <= 8; wide for W > 8); two-shot as MR_TILE_WIDE.
+ *                  second (W <= 8; wide for W > 8); two-shot under TILE or LAST: XCD-local units
+ *                  at any size (W <= 8, 16-byte path), otherwise as MR_TILE_WIDE.
  * Unknown options or out-of-range values -> MR_ERR_INVALID_ARG.  Environment variables
  * MR_TWOSHOT_SYNC, MR_SPIN_LIMIT and MR_TILE_SHAPE set the initial values when the library loads; a
  * value that is not a whole number in the option's range is ignored.  MR_TRACE=1 makes every launch
@@ -305,7 +309,9 @@ mr_status mr_get_option(mr_option opt, int64_t* value);
 
 /* Library ABI version (major*100 + minor).  1.01 added MR_OPT_TILE_SHAPE, MR_TWOSHOT_SYNC_LAST and
  * MR_TWOSHOT_SYNC_AUTO (the new default hand-off); 1.02 added MR_TILE_WIDE_PAIR; 1.03 added
- * mr_allgather_param_contig_sdma, mr_sdma_engines and MR_ERR_ENGINE. */
+ * mr_allgather_param_contig_sdma, mr_sdma_engines and MR_ERR_ENGINE; 1.04 added
+ * mr_allreduce_sum_noalloc and the last-arriver hand-off on XCD-local units (the default from 8 to
+ * 32 MiB per rank buffer). */
 int mr_version(void);
 
 #ifdef __cplusplus

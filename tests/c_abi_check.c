@@ -19,7 +19,7 @@ int main(void) {
   uint64_t splits[3] = {8, 16, 24};
   int64_t v = -1;
   mr_stream stream = NULL;
-  CHECK(mr_version() == 103);
+  CHECK(mr_version() == 104);
   CHECK(strncmp(mr_status_string(MR_ERR_ALIAS), "MR_ERR_ALIAS", 12) == 0);
   CHECK(mr_allreduce_sum(bufs, 0, 16, MR_BF16, (void*)0x900000, MR_ONESHOT, stream) == MR_ERR_INVALID_ARG);
   CHECK(mr_allreduce_sum(bufs, 2, 16, MR_INT32, (void*)0x900000, MR_ONESHOT, stream) == MR_ERR_DTYPE);

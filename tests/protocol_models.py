@@ -274,3 +274,27 @@ def last_arriver_random(t1: int, ratio: int, rng: random.Random):
             copiers[q].append(k)
             ok = ok and arrived[q] == members
     return [len(c) for c in copiers], ok, counts
+
+
+# ------------------------------------------------------------------- XCD-local units, last arriver
+
+def xcd_last_random(members: int, xcc_of: list, rng: random.Random):
+    """The members of one copy group publish in a random order.  Each adds 1 + (1 << (8 + 4*xcc)) to the
+    group's 64-bit arrival word (xcc < 8; a larger id adds only the count); the one whose add completes
+    the count stores 0 and decides: copy the group from the stage when every member's field says they
+    ran on its own XCC, else recompute it.  Returns (copiers, decision, word at the end, whether every
+    member had published when the decision was taken)."""
+    word, published, copiers, decision, complete = 0, 0, [], None, False
+    for k in rng.sample(range(members), members):
+        xcc = xcc_of[k]
+        add = 1 + ((1 << (8 + 4 * xcc)) if xcc < 8 else 0)
+        old = word
+        word = (word + add) & ((1 << 64) - 1)
+        published += 1
+        if (old & 0xFF) == members - 1:
+            word = 0
+            copiers.append(k)
+            local = xcc < 8 and ((old + add) >> (8 + 4 * xcc)) & 15 == members
+            decision = "copy" if local else "recompute"
+            complete = published == members
+    return copiers, decision, word, complete

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mr_version() == 103
+    assert L.mr_version() == 104
     for code, name in mr.STATUS.items():
         assert L.mr_status_string(code).decode().startswith(name)
     assert b"unknown" in L.mr_status_string(-99)

@@ -148,7 +148,8 @@ def test_oneshot_equals_twoshot_and_is_deterministic():
     assert mr.workspace_check() == 0
 
 
-@pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last", "tile:wide_pair", "tile:wide_pair:3"])
+@pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last", "tile:wide_pair", "tile:wide_pair:3",
+                                  "last:wide_pair", "last:wide_pair:3"])
 def test_twoshot_stale_stage_is_never_read(sync):
     """Two input sets alternate on one caller-owned workspace, so when a call starts its stage still
     holds the previous call's (different) sums: a phase-2 copy that ran ahead of its phase-1 producer

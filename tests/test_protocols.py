@@ -35,6 +35,23 @@ def test_xcd_flag_every_interleaving(spin_limit, same_xcd):
         assert any(m == "copy" for _, m, _ in outcomes)
 
 
+# ------------------------------------------------------------------- XCD-local units, last arriver
+
+def test_xcd_last_arriver_copies_once_and_only_its_own_xcc():
+    rng = random.Random(13)
+    for _ in range(3000):
+        members = rng.randint(1, 15)
+        home = rng.randint(0, 9)
+        if rng.random() < 0.5:
+            xcc_of = [home] * members
+        else:
+            xcc_of = [rng.randint(0, 9) for _ in range(members)]
+        copiers, decision, word, complete = pm.xcd_last_random(members, xcc_of, rng)
+        assert len(copiers) == 1 and complete and word == 0
+        local = all(x == xcc_of[copiers[0]] for x in xcc_of) and xcc_of[copiers[0]] < 8
+        assert decision == ("copy" if local else "recompute"), (xcc_of, copiers, decision)
+
+
 # ---------------------------------------------------------------------------------- per-tile flags
 
 @pytest.mark.parametrize("spin_limit", [0, 1, 3])
@@ -137,8 +154,8 @@ def test_xcd_units_cover_every_pack_once(L):
     workgroup of the same run, every unit inside the message, and the flag words inside the
     workspace's flag area."""
     rng = random.Random(3)
-    cases = [(8, 8_388_608, "bf16", 0, "auto", "auto"), (8, 4_194_304, "fp32", 0, "auto", "auto"),
-             (8, 8_388_608 + 40, "bf16", 6, "tile", "auto"), (5, 33_554_432 + 3, "fp16", 2, "tile", "auto")]
+    cases = [(8, 8_388_608, "bf16", 0, "tile", "auto"), (8, 4_194_304, "fp32", 0, "tile", "auto"),
+             (8, 8_388_608 + 40, "bf16", 6, "tile", "auto"), (5, 33_554_432 + 3, "fp16", 2, "auto", "auto")]
     for _ in range(40):
         W = rng.randint(1, 8)
         dt = rng.choice(["bf16", "fp16", "fp32"])
@@ -172,17 +189,64 @@ def test_xcd_units_cover_every_pack_once(L):
         assert p["flags"] == units <= mr.workspace_bytes(W, n, dt) >> 8
 
 
+def test_xcd_last_arriver_groups_cover_every_unit_once(L):
+    """The last-arriver form on XCD-local units, as the kernel computes it from the workgroup index
+    (run x = b % 8, unit x*run + s, copy group s // 4 of the run, its 64-bit arrival word x*groups + g),
+    replayed over the library's plans: every unit produced once, each group's members all in one run,
+    one arrival word per group inside the flag area, and that area inside the workspace's."""
+    rng = random.Random(4)
+    cases = [(8, 8_388_608, "bf16", 0, "auto", "auto"), (8, 2_097_152, "fp32", 0, "auto", "auto"),
+             (8, 8_388_608 + 40, "bf16", 6, "last", "auto")]
+    for _ in range(40):
+        W = rng.randint(1, 8)
+        dt = rng.choice(["bf16", "fp16", "fp32"])
+        es = 2 if dt != "fp32" else 4
+        cases.append((W, rng.randint(1, 3_000_000), dt, es * rng.randint(0, 7), "last", "wide_pair"))
+    for W, n, dt, addr, sync, shape in cases:
+        p = _plan(L, W, n, dt, addr, sync, shape)
+        assert p["xcd"] == 1 and p["sync"] == 3, (W, n, dt, p)
+        units, run = p["units"], p["run"]
+        groups = -(-run // 4)
+        assert p["grid"] == 8 * run and run * 8 >= units
+        produced, words = {}, {}
+        for b in range(p["grid"]):
+            x, s = b % 8, b // 8
+            u = x * run + s
+            if u >= units:
+                continue
+            assert u not in produced
+            produced[u] = x
+            words.setdefault(x * groups + s // 4, set()).add(u)
+        assert set(produced) == set(range(units))
+        for w, us in words.items():
+            x, g = divmod(w, groups)
+            assert us == {x * run + g * 4 + r for r in range(4) if g * 4 + r < run and x * run + g * 4 + r < units}
+            assert max(us) // run == min(us) // run == x
+        assert p["flags"] == 2 * 8 * groups and p["flags"] <= mr.workspace_bytes(W, n, dt) >> 8
+
+
 def test_default_hand_off_choices(L):
-    # 16 MiB per rank and up on the 16-byte path with W <= 8: XCD-local units; below: last arriver
-    assert _plan(L, 8, 8_388_608, "bf16", 0, "auto", "auto")["xcd"] == 1
-    assert _plan(L, 8, 4_194_304, "bf16", 0, "auto", "auto")["sync"] == 3
-    assert _plan(L, 9, 8_388_608, "bf16", 0, "auto", "auto")["xcd"] == 0
-    assert _plan(L, 8, 8_388_608, "bf16", 0, "auto", "auto", same_phase=0)["xcd"] == 0
-    # the allocation-free entry point only takes hand-offs that cannot leave a word set
-    for W, n in ((8, 8_388_608), (8, 1000), (12, 8_388_608)):
+    def pick(W, n, dt="bf16", **kw):
+        p = _plan(L, W, n, dt, 0, "auto", "auto", **kw)
+        return p["sync"], p["xcd"]
+    # the last arriver up to 32 MiB per rank (XCD-local units from 8 MiB on the 16-byte path with W <= 8),
+    # per-tile flags above (XCD-local up to 64 MiB, then the chunk tiles)
+    assert pick(8, 2_097_152) == (3, 0)              # 4 MiB
+    assert pick(8, 4_194_304) == (3, 1)              # 8 MiB
+    assert pick(8, 8_388_608) == (3, 1)              # 16 MiB, the headline size
+    assert pick(8, 4_194_304, "fp32") == (3, 1)      # 16 MiB
+    assert pick(8, 16_777_216) == (3, 1)             # 32 MiB
+    assert pick(8, 16_777_216 + 8) == (0, 1)         # just over 32 MiB
+    assert pick(8, 33_554_432) == (0, 1)             # 64 MiB
+    assert pick(8, 134_217_728) == (0, 0)            # 256 MiB
+    assert pick(9, 8_388_608) == (3, 0)              # W > 8: chunk tiles
+    assert pick(8, 8_388_608, same_phase=0) == (3, 0)  # realigned inputs: chunk tiles
+    # the allocation-free entry point only takes the last arriver, in which nothing waits
+    for W, n in ((8, 8_388_608), (8, 1000), (12, 8_388_608), (8, 16_777_216)):
         for sync in ("chunk", "grid", "tile"):
             p = _plan(L, W, n, "bf16", 0, sync, "narrow", wait_free=1)
-            assert p["xcd"] == 1 or p["sync"] == 3, (W, n, sync, p)
+            assert p["sync"] == 3, (W, n, sync, p)
+            assert p["xcd"] == (1 if W <= 8 and n >= 4_194_304 else 0), (W, n, sync, p)
 
 
 def _pieces(W, splits, es):
