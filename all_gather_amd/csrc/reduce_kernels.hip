@@ -208,6 +208,18 @@ __device__ __forceinline__ void load_pack_pair(const RankPtrs& in, int r, size_t
   b = base[i + (d != 0 ? 1 : 0)];
 }
 
+// Neighbour packs on the realigned path.  In the wave-contiguous layout below, lane l's pack u is pack
+// i, and pack i + 1 is lane l + 1's pack u or, for lane 63, lane 0's pack u + 1: so the second aligned
+// pack an output pack straddles is moved over from the neighbouring lane instead of loaded again.
+// wave_shl:1 gives lane l the value of lane l + 1 and leaves lane 63 at `old`; wave_rol:1 gives lane 63
+// the value of lane 0.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), 0x130, 0xf, 0xf, false));
+}
+__device__ __forceinline__ uint32_t lane0_to_lane63(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x134, 0xf, 0xf, false));
+}
+
 // Wave-contiguous tile layout: a workgroup of B lanes owns B*P consecutive 16-byte packs starting at
 // `first`; wave w owns P*64 of them and lane l's u-th pack is first + w*64*P + u*64 + l, so each wave
 // instruction covers 1 KiB and a wave's P instructions for one rank cover P KiB contiguous.
@@ -216,10 +228,81 @@ __device__ __forceinline__ size_t wc_pack(size_t first, int u) {
   return first + static_cast<size_t>(threadIdx.x >> 6) * (64 * P) + static_cast<size_t>(u) * 64 + (threadIdx.x & 63);
 }
 
+// Realigned inputs, a full tile: every lane loads the aligned pack its output pack starts in (rank by
+// rank, all in flight), lane 63 also the one after its last pack; the second aligned pack of each is
+// then taken from the neighbouring lane (see from_next_lane).  A tile that reaches past the body's end
+// (one per launch at most), and every tile for W > 8 (whose loads would not fit the registers), loads
+// both aligned packs of every output pack, one row at a time.
+template <typename D, int W, int B, int P, typename Store>
+__device__ __forceinline__ void reduce_tile_realigned(const RankPtrs& in, size_t hb, size_t first, size_t end,
+                                                      Store st) {
+  if constexpr (W <= 8) {
+  if (first + static_cast<size_t>(B) * P <= end) {
+    const bool l63 = (threadIdx.x & 63) == 63;
+    u32x4 v[P][W];
+    u32x4 nxt[W];
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+      const uint32_t d = in.shift[r];
+      const u32x4* base = reinterpret_cast<const u32x4*>(in.p[r] + hb - d);
+#pragma unroll
+      for (int u = 0; u < P; ++u) v[u][r] = __builtin_nontemporal_load(base + wc_pack<B, P>(first, u));
+      nxt[r] = u32x4{0u, 0u, 0u, 0u};
+      // the pack after lane 63's last one holds bytes of that lane's output pack when d != 0
+      if (l63) nxt[r] = base[wc_pack<B, P>(first, P - 1) + (d != 0 ? 1 : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      auto pack = [&](int r) {
+        u32x4 b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          b[k] = from_next_lane(u + 1 < P ? lane0_to_lane63(v[u + 1 < P ? u + 1 : u][r][k]) : nxt[r][k], v[u][r][k]);
+        return realign_rt(v[u][r], b, in.shift[r]);
+      };
+      float acc[D::V];
+      D::widen(pack(0), acc);
+#pragma unroll
+      for (int r = 1; r < W; ++r) {
+        float t[D::V];
+        D::widen(pack(r), t);
+#pragma unroll
+        for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
+      }
+      st(u, wc_pack<B, P>(first, u), D::narrow(acc));
+    }
+    return;
+  }
+  }
+#pragma unroll 1
+  for (int u = 0; u < P; ++u) {
+    const size_t i = wc_pack<B, P>(first, u);
+    if (i < end) {
+      u32x4 a[W], b[W];
+#pragma unroll
+      for (int r = 0; r < W; ++r) load_pack_pair(in, r, hb, i, a[r], b[r]);
+      float acc[D::V];
+      D::widen(realign_rt(a[0], b[0], in.shift[0]), acc);
+#pragma unroll
+      for (int r = 1; r < W; ++r) {
+        float t[D::V];
+        D::widen(realign_rt(a[r], b[r], in.shift[r]), t);
+#pragma unroll
+        for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
+      }
+      st(u, i, D::narrow(acc));
+    }
+  }
+}
+
 // Reduce a wave-contiguous tile of B*P packs (i < end), PC packs at a time: all W*PC loads in flight,
 // rank by rank, before the adds; each result goes to st(u, i, pack).
 template <typename D, int W, int B, int P, typename Store, bool RA = false>
 __device__ __forceinline__ void reduce_tile(const RankPtrs& in, size_t hb, size_t first, size_t end, Store st) {
+  if constexpr (RA) {
+    reduce_tile_realigned<D, W, B, P, Store>(in, hb, first, end, st);
+    return;
+  }
   constexpr int PC = (W <= 8 || P == 1) ? P : 2;  // wide W: fewer packs in flight per lane
   static_assert(P % PC == 0, "pack groups");
 #pragma unroll
@@ -690,9 +773,10 @@ __device__ __forceinline__ uint64_t xcd_arrival(uint32_t xcc) {
 }
 static_assert(8 + 4 * kXcds <= 64 && kXcdLastGroup >= 1 && kXcdLastGroup <= 15, "arrival word fields");
 
-template <typename D, int W, bool LAST>
+template <typename D, int W, bool LAST, bool RA = false>
 __global__ __launch_bounds__(kOneShotBlock) void twoshot_xcd(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
                                                              uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
+  static_assert(LAST || !RA, "realigned inputs take the last-arriver hand-off only");
   constexpr int B = kOneShotBlock, U = OneShotU<W>::value;
   constexpr int R = static_cast<int>(LAST ? kXcdLastGroup : kXcdGroup);  // units per copy
   constexpr size_t UP = static_cast<size_t>(B) * U;  // packs per unit
@@ -709,9 +793,10 @@ __global__ __launch_bounds__(kOneShotBlock) void twoshot_xcd(RankPtrs in, char* 
     if (s >= in_run) return;  // padding
     const size_t first = u * UP;
     const i32x4 rs = make_rsrc(stage + hb + first * 16, static_cast<uint32_t>(UP * 16));
-    reduce_tile<D, W, B, U>(in, hb, first, sh.npacks, [&](int, size_t i, const u32x4& o) {
+    auto store = [&](int, size_t i, const u32x4& o) {
       raw_buffer_store_v4(__builtin_bit_cast(i32x4, o), rs, static_cast<int>((i - first) * 16), 0, 0);
-    });
+    };
+    reduce_tile<D, W, B, U, decltype(store), RA>(in, hb, first, sh.npacks, store);
     if (u == 0) reduce_edges<D, W, false>(in, out, sh);  // the few elements outside the packs: straight to out
     __builtin_amdgcn_s_waitcnt(0x0f70);                 // vmcnt(0): the L2 holds this lane's stage stores
     __syncthreads();
@@ -779,8 +864,10 @@ __global__ __launch_bounds__(kOneShotBlock) void twoshot_xcd(RankPtrs in, char* 
     const size_t f = first + r * UP;
     if (s_mode[r] == 1u)
       copy_group<D, B, U, kXcdStageLoadAux>(out, stage, sh, f, sh.npacks, false);
-    else if (s_mode[r] == 2u)
-      reduce_tile<D, W, B, U>(in, hb, f, sh.npacks, [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); });
+    else if (s_mode[r] == 2u) {
+      auto st = [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); };
+      reduce_tile<D, W, B, U, decltype(st), RA>(in, hb, f, sh.npacks, st);
+    }
   }
 }
 
@@ -890,9 +977,15 @@ hipError_t oneshot_pair_launch(const RankPtrs& in, char* out, const ReduceShape&
   return hipGetLastError();
 }
 
-// Realigned 16-byte path (inputs in other 16-byte phases than out): two aligned loads per pack per
-// realigned rank, so two packs per lane (one for W > 8) keep the registers of the wide tile's four.
-template <int W> struct RealignU { static constexpr int value = W <= 8 ? 2 : 1; };
+// Realigned 16-byte path (inputs in other 16-byte phases than out): the wide tile's four packs per lane
+// for W <= 8, the second aligned pack of each moved over from the neighbouring lane (reduce_tile_realigned;
+// 234 VGPRs, two waves per SIMD).  Same-GPU A/B, W=8, 16 MiB per rank, inputs at alternating phases:
+// two packs per lane with both aligned packs loaded 30.3 us (bf16); two packs per lane, neighbour moves
+// 27.4; four packs per lane, neighbour moves 26.2 (the aligned wide one-shot: 25.6).  One pack for W > 8.
+#ifndef MR_RA_U
+#define MR_RA_U 4
+#endif
+template <int W> struct RealignU { static constexpr int value = W <= 8 ? MR_RA_U : 1; };
 
 template <typename D, int W>
 hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, uint32_t shape, hipStream_t st) {
@@ -941,8 +1034,12 @@ hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uin
                      const TwoShotPlan& pl, hipStream_t st) {
   if constexpr (W <= 8) {
     if (sh.vec && pl.xcd && pl.sync == kSyncLast) {
-      hipLaunchKernelGGL((twoshot_xcd<D, W, true>), dim3(static_cast<unsigned>(twoshot_grid(pl))), dim3(kOneShotBlock),
-                         0, st, in, out, stage, ctrl, flags, sh, pl);
+      const dim3 g(static_cast<unsigned>(twoshot_grid(pl)));
+      if (sh.realign)
+        hipLaunchKernelGGL((twoshot_xcd<D, W, true, true>), g, dim3(kOneShotBlock), 0, st, in, out, stage, ctrl, flags,
+                           sh, pl);
+      else
+        hipLaunchKernelGGL((twoshot_xcd<D, W, true>), g, dim3(kOneShotBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
       return hipGetLastError();
     }
     if (sh.vec && pl.xcd) {
@@ -1031,9 +1128,9 @@ hipError_t launch_twoshot(const RankPtrs& in, int W, mr_dtype dt, char* out, cha
 // than a pack) ride with phase-1 tile 0 and phase-2 tile 0 of chunk 0.
 TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t spin_limit, uint32_t shape) {
   TwoShotPlan pl{};
-  if (sh.vec && sh.realign) {  // realigned inputs: one build, last-arriver hand-off on wide tiles
+  if (sh.vec && sh.realign) {  // realigned inputs: the last-arriver hand-off, on XCD-local units or wide tiles
     sync = kSyncLast;
-    shape = kShapeWide;
+    if (!twoshot_xcd_units(sh.vec, W, sh.npacks, sync, shape)) shape = kShapeWide;
   }
   pl.chunks = static_cast<uint32_t>(W);
   const size_t units = sh.vec ? sh.npacks : sh.n;
@@ -1048,7 +1145,7 @@ TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t s
   pl.t2 = static_cast<uint32_t>(t2);
   pl.sync = sync;
   pl.spin_limit = spin_limit;
-  if (!sh.realign && twoshot_xcd_units(sh.vec, W, sh.npacks, sync, shape)) {  // XCD-local units replace the chunk tiles
+  if (twoshot_xcd_units(sh.vec, W, sh.npacks, sync, shape)) {  // XCD-local units replace the chunk tiles
     constexpr size_t UP = static_cast<size_t>(kOneShotBlock) * 4;
     pl.xcd = 1;
     pl.units = sh.npacks ? (sh.npacks + UP - 1) / UP : 1;  // an edges-only call still has one unit

@@ -240,7 +240,10 @@ def test_default_hand_off_choices(L):
     assert pick(8, 33_554_432) == (0, 1)             # 64 MiB
     assert pick(8, 134_217_728) == (0, 0)            # 256 MiB
     assert pick(9, 8_388_608) == (3, 0)              # W > 8: chunk tiles
-    assert pick(8, 8_388_608, same_phase=0) == (3, 0)  # realigned inputs: chunk tiles
+    assert pick(8, 8_388_608, same_phase=0) == (3, 1)  # realigned inputs: always the last arriver
+    assert pick(8, 33_554_432, same_phase=0) == (3, 1)
+    assert pick(8, 2_097_152, same_phase=0) == (3, 0)
+    assert pick(12, 8_388_608, same_phase=0) == (3, 0)
     # the allocation-free entry point only takes the last arriver, in which nothing waits
     for W, n in ((8, 8_388_608), (8, 1000), (12, 8_388_608), (8, 16_777_216)):
         for sync in ("chunk", "grid", "tile"):
