@@ -138,7 +138,9 @@ mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, co
  * Arguments, limits and errors as mr_allgather_param_contig, plus MR_ERR_ENGINE.  Unlike every other
  * entry point this call is synchronous: it waits until `stream` has finished its earlier work (the
  * engines are not ordered by the stream), then copies, and returns once every copy is complete; work
- * enqueued on any stream afterwards sees the result.  Not capturable in a HIP graph.
+ * enqueued on any stream afterwards sees the result.  Not capturable in a HIP graph.  The first call
+ * on a device initialises the HSA runtime and creates one HSA signal that the library keeps for that
+ * device until the process ends.
  *
  * mr_sdma_engines: number of SDMA engines the current device offers for its own memory; 0 if none or
  * the HSA runtime is unavailable, and then mr_last_hip_error() gives the HSA runtime's hsa_status_t.
