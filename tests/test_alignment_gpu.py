@@ -84,6 +84,23 @@ def test_reduce_at_odd_byte_offsets(dtype, mode):
         assert mr.workspace_check() == 0
 
 
+@pytest.mark.parametrize("mode", ["oneshot", "twoshot", "twoshot:tile", "twoshot:chunk"])
+def test_reduce_at_odd_byte_offsets_large(mode):
+    """The byte path at 8 MiB per rank buffer (its two-shot plan needs a flag per 1024-element tile of
+    every chunk, so this also checks the workspace sizing), outputs sampled against the oracle."""
+    kind, _, sync = mode.partition(":")
+    W, n = 8, 4_194_304 + 5
+    bufs = workloads.rank_buffers(47, W, n, "bf16", "uniform")
+    idx = np.linspace(0, n - 1, 1 << 16).astype(np.int64)
+    want = oracle.allreduce_sum_ref([b[idx] for b in bufs], "bf16")
+    offs = [1, 2, 7, 0, 4, 9, 15, 3]
+    print(f"[case] odd offsets large {mode} W={W} n={n}", flush=True)
+    got = _reduce(bufs, "bf16", offs, 5, kind, sync or "auto")
+    assert_reduce_equal(got[idx], want, "bf16", f"odd offsets large {mode}")
+    if kind == "twoshot":
+        assert mr.workspace_check() == 0
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 def test_reduce_mixed_phases_realigned(dtype):
     """Element-aligned pointers, every rank at its own 16-byte phase (the realigned 16-byte path), in

@@ -377,9 +377,10 @@ def test_w8_size_sweep(dtype, per_rank):
     assert mr.workspace_check() == 0
 
 
-def test_twoshot_elementwise_path_large():
-    """Pointers with different 16-byte phases take the element-wise path, whose two-shot plan needs a
-    producer flag per 256 elements; a large call checks that the workspace sizing covers it."""
+def test_twoshot_realigned_path_large():
+    """Element-aligned pointers with different 16-byte phases take the realigned 16-byte path: a large
+    call (past 32 MiB per rank buffer, so the default hand-off is no longer the last arriver) checked
+    on sampled outputs, one-shot and two-shot under the hand-offs that then apply."""
     W, n = 8, 20_000_003
     bufs = workloads.rank_buffers(19, W, n + 8, "bf16", "uniform")
     offs = [r % 8 for r in range(W)]
@@ -389,7 +390,7 @@ def test_twoshot_elementwise_path_large():
     want = oracle.allreduce_sum_ref([bufs[r][offs[r]:offs[r] + n][idx] for r in range(W)], "bf16")
     for mode in ("oneshot", "twoshot:tile", "twoshot:chunk"):
         got = to_bits(_run(views, "bf16", n, mode))
-        assert_reduce_equal(got[idx], want, "bf16", f"element path {mode}")
+        assert_reduce_equal(got[idx], want, "bf16", f"realigned path {mode}")
     assert mr.workspace_check() == 0
 
 
