@@ -34,6 +34,11 @@ int main(void) {
   CHECK(mr_allgather_param_contig_sdma((const void*)0x100000, 8, 4, splits, 3, MR_FP16, (void*)0x1002FE, stream) ==
         MR_ERR_ALIAS);
   CHECK(strncmp(mr_status_string(MR_ERR_ENGINE), "MR_ERR_ENGINE", 13) == 0);
+  CHECK(mr_allreduce_sum_noalloc(bufs, 0, 16, MR_BF16, (void*)0x900000, MR_TWOSHOT, stream) == MR_ERR_INVALID_ARG);
+  CHECK(mr_allreduce_sum_noalloc(bufs, 2, 16, MR_INT32, (void*)0x900000, MR_TWOSHOT, stream) == MR_ERR_DTYPE);
+  CHECK(mr_allreduce_sum_noalloc(bufs, 2, MR_NOALLOC_MAX_BYTES / 2 + 1, MR_BF16, (void*)0x90000000, MR_TWOSHOT,
+                                 stream) == MR_ERR_WORKSPACE);
+  CHECK(mr_allreduce_sum_noalloc(NULL, 2, 0, MR_FP32, NULL, MR_ONESHOT, stream) == MR_OK);
   CHECK(mr_workspace_bytes(8, 1 << 20, MR_BF16) > (2u << 20));
   CHECK(mr_get_option(MR_OPT_TWOSHOT_SYNC, &v) == MR_OK && v == MR_TWOSHOT_SYNC_AUTO);
   CHECK(mr_set_option(MR_OPT_TWOSHOT_SYNC, 7) == MR_ERR_INVALID_ARG);

@@ -18,11 +18,15 @@ HOST_SAN = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined -Xar
 
 @pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANG)), reason="ROCm toolchain not present")
 def test_c_abi_under_asan_and_ubsan(tmp_path):
-    base = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-fno-gpu-flush-denormals-to-zero",
-            "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include")] + HOST_SAN.split()
+    from all_gather_amd import _build
+
+    # every source of the library; debug info on the host side only (device code as usual, minus -O3)
+    base = ["--offload-arch=gfx950", "-O1", "-Xarch_host", "-g", "-std=c++17", "-fPIC",
+            "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang",
+            "-packed-fp32-ops", "-I", os.path.join(ROOT, "include")] + HOST_SAN.split()
+    names = [os.path.splitext(src)[0] for src in _build.SOURCES]
     procs = []
-    for name in ("api", "reduce_kernels", "gather_kernels"):
+    for name in names:
         procs.append(subprocess.Popen([HIPCC, *base, "-c", os.path.join(CSRC, name + ".hip"), "-o",
                                        str(tmp_path / (name + ".o"))], stdout=subprocess.PIPE, stderr=subprocess.PIPE))
     for p in procs:
@@ -30,7 +34,7 @@ def test_c_abi_under_asan_and_ubsan(tmp_path):
         assert p.returncode == 0, err.decode()[-2000:]
     lib = tmp_path / "libmr.so"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_SAN.split(),
-                        *[str(tmp_path / (n + ".o")) for n in ("api", "reduce_kernels", "gather_kernels")],
+                        *[str(tmp_path / (n + ".o")) for n in names], "-lhsa-runtime64",
                         "-o", str(lib)], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     exe = tmp_path / "check"
