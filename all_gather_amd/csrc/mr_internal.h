@@ -86,12 +86,13 @@ inline uint32_t twoshot_tile_packs(size_t npacks, uint32_t sync, uint32_t forced
                                                                           : kShapeNarrow;
   return shape == kShapeNarrow ? 64u : shape == kShapeMedium ? 256u : kTwoShotWideTile;
 }
-// XCD-local units (twoshot_xcd, 16-byte path, W <= 8).  Under the last-arriver hand-off they lead from
-// 512 Ki packs (8 MiB per rank buffer) up; under per-tile flags (copier workgroups) from 1 Mi packs to
-// 4 Mi packs (16 to 64 MiB), beyond which the ticketed chunk tiles lead.  MR_TILE_WIDE_PAIR forces them
-// for either hand-off at any size.  Same-GPU A/B, W=8 bf16, rotating sets, best of three (us):
+// XCD-local units (twoshot_xcd, 16-byte path, W <= 8).  Under the last-arriver hand-off they lead at
+// every size (narrow or medium units below 8 MiB per rank buffer, twoshot_xcd_unit_packs); under per-tile
+// flags (copier workgroups) from 1 Mi packs to 4 Mi packs (16 to 64 MiB), beyond which the ticketed chunk
+// tiles lead.  MR_TILE_WIDE_PAIR forces them, on wide units, for either hand-off at any size.
+// Same-GPU A/B, W=8 bf16, rotating sets, best of three (us; eager launches):
 //   per rank              4 MiB   8 MiB   16 MiB   32 MiB   64 MiB   256 MiB
-//   XCD, last arriver     12.72   17.46   31.85    62.38    122.2    463.2
+//   XCD, last arriver     12.72   17.46   31.85    62.38    122.2    463.2     (wide units)
 //   XCD, copiers          13.24   21.13   35.97    63.64    118.3    472.7
 //   ticketed, last        11.54   19.06   37.33    71.75    143.4    573.5
 //   ticketed, tile flags  15.51   19.87   35.63    66.37    124.1    454.6
@@ -106,11 +107,20 @@ inline bool twoshot_xcd_units(int vec, int W, size_t npacks, uint32_t sync, uint
   if (!vec || W > 8 || (sync != kSyncTile && sync != kSyncLast)) return false;
   if (forced == kShapeWidePair) return true;
   if (forced != kShapeAuto) return false;
-  if (sync == kSyncLast) return npacks >= (size_t(1) << 19);
+  if (sync == kSyncLast) return true;
   return npacks >= (size_t(1) << 20) && npacks <= (size_t(1) << 22);
 }
-// Two-shot hand-off under MR_TWOSHOT_SYNC_AUTO: the last arriver up to 32 MiB per rank buffer (ticketed
-// tiles below 8 MiB, XCD-local units from 8 MiB), per-tile flags above (table above).
+// Packs per XCD-local unit: wide (256 lanes x 4 packs) for the copier workgroups, under MR_TILE_WIDE_PAIR,
+// and from 512 Ki packs (8 MiB per rank buffer); below that the last arriver takes narrow units (64 x 1)
+// under 64 Ki packs and medium ones (256 x 1) above.  Graph-replayed, W=8 bf16, us (narrow / medium /
+// wide units; ticketed last arriver): 256 KiB 4.11 / 4.29 / 7.56; 5.34.  1 MiB 6.13 / 5.55 / 9.03; 6.85.
+// 2 MiB 7.83 / 7.67 / 10.17; 8.92.  4 MiB 11.6 / 11.9 / 12.4; 12.1.
+inline size_t twoshot_xcd_unit_packs(size_t npacks, uint32_t sync, uint32_t forced) {
+  if (sync != kSyncLast || forced == kShapeWidePair || npacks >= (size_t(1) << 19)) return 1024;
+  return npacks < (size_t(1) << 16) ? 64 : 256;
+}
+// Two-shot hand-off under MR_TWOSHOT_SYNC_AUTO: the last arriver on XCD-local units up to 32 MiB per rank
+// buffer, per-tile flags above (tables above).
 inline uint32_t twoshot_sync_for(size_t bytes, uint32_t sync) {
   if (sync != kSyncAuto) return sync;
   return bytes <= (size_t(32) << 20) ? kSyncLast : kSyncTile;

@@ -773,14 +773,17 @@ __device__ __forceinline__ uint64_t xcd_arrival(uint32_t xcc) {
 }
 static_assert(8 + 4 * kXcds <= 64 && kXcdLastGroup >= 1 && kXcdLastGroup <= 15, "arrival word fields");
 
-template <typename D, int W, bool LAST, bool RA = false>
-__global__ __launch_bounds__(kOneShotBlock) void twoshot_xcd(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
-                                                             uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
+// B lanes x U packs per unit: the wide tile (256 x 4, 16 KiB of output) from 8 MiB per rank buffer,
+// and for the last arriver on smaller messages the medium (256 x 1) or narrow (64 x 1) tile, so that a
+// small message still spreads over every CU (twoshot_xcd_unit_packs picks it).
+template <typename D, int W, bool LAST, bool RA = false, int B = kOneShotBlock, int U = 4>
+__global__ __launch_bounds__(B) void twoshot_xcd(RankPtrs in, char* out, char* stage, Ctrl* ctrl,
+                                                 uint32_t* flags, ReduceShape sh, TwoShotPlan pl) {
   static_assert(LAST || !RA, "realigned inputs take the last-arriver hand-off only");
-  constexpr int B = kOneShotBlock, U = OneShotU<W>::value;
+  static_assert(LAST || (B == kOneShotBlock && U == 4), "copier workgroups run on wide units");
   constexpr int R = static_cast<int>(LAST ? kXcdLastGroup : kXcdGroup);  // units per copy
   constexpr size_t UP = static_cast<size_t>(B) * U;  // packs per unit
-  static_assert(U == 4, "wide units");
+  static_assert(UP * 16 % 256 == 0, "units start on 256-byte boundaries of the stage body");
   const size_t hb = sh.head * D::kSize;
   const uint32_t x = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
   const size_t run0 = static_cast<size_t>(x) * pl.run;  // first unit of this run
@@ -1035,11 +1038,27 @@ hipError_t twoshot_w(const RankPtrs& in, char* out, char* stage, Ctrl* ctrl, uin
   if constexpr (W <= 8) {
     if (sh.vec && pl.xcd && pl.sync == kSyncLast) {
       const dim3 g(static_cast<unsigned>(twoshot_grid(pl)));
-      if (sh.realign)
-        hipLaunchKernelGGL((twoshot_xcd<D, W, true, true>), g, dim3(kOneShotBlock), 0, st, in, out, stage, ctrl, flags,
-                           sh, pl);
-      else
-        hipLaunchKernelGGL((twoshot_xcd<D, W, true>), g, dim3(kOneShotBlock), 0, st, in, out, stage, ctrl, flags, sh, pl);
+      if (sh.realign) {
+        if (pl.unit1 == 64)
+          hipLaunchKernelGGL((twoshot_xcd<D, W, true, true, 64, 1>), g, dim3(64), 0, st, in, out, stage, ctrl, flags,
+                             sh, pl);
+        else if (pl.unit1 == 256)
+          hipLaunchKernelGGL((twoshot_xcd<D, W, true, true, 256, 1>), g, dim3(256), 0, st, in, out, stage, ctrl, flags,
+                             sh, pl);
+        else
+          hipLaunchKernelGGL((twoshot_xcd<D, W, true, true>), g, dim3(kOneShotBlock), 0, st, in, out, stage, ctrl,
+                             flags, sh, pl);
+      } else {
+        if (pl.unit1 == 64)
+          hipLaunchKernelGGL((twoshot_xcd<D, W, true, false, 64, 1>), g, dim3(64), 0, st, in, out, stage, ctrl, flags,
+                             sh, pl);
+        else if (pl.unit1 == 256)
+          hipLaunchKernelGGL((twoshot_xcd<D, W, true, false, 256, 1>), g, dim3(256), 0, st, in, out, stage, ctrl,
+                             flags, sh, pl);
+        else
+          hipLaunchKernelGGL((twoshot_xcd<D, W, true>), g, dim3(kOneShotBlock), 0, st, in, out, stage, ctrl, flags, sh,
+                             pl);
+      }
       return hipGetLastError();
     }
     if (sh.vec && pl.xcd) {
@@ -1146,7 +1165,8 @@ TwoShotPlan plan_twoshot(int W, const ReduceShape& sh, uint32_t sync, uint32_t s
   pl.sync = sync;
   pl.spin_limit = spin_limit;
   if (twoshot_xcd_units(sh.vec, W, sh.npacks, sync, shape)) {  // XCD-local units replace the chunk tiles
-    constexpr size_t UP = static_cast<size_t>(kOneShotBlock) * 4;
+    const size_t UP = twoshot_xcd_unit_packs(sh.npacks, sync, shape);
+    pl.unit1 = static_cast<uint32_t>(UP);
     pl.xcd = 1;
     pl.units = sh.npacks ? (sh.npacks + UP - 1) / UP : 1;  // an edges-only call still has one unit
     pl.run = static_cast<uint32_t>((pl.units + kXcds - 1) / kXcds);

@@ -84,11 +84,12 @@ int mr_last_hip_error(void);
  *         flag hand-off orders the phases, phase 2 copies the stage into out; the result is the
  *         same.  The shares are whole 16-byte packs of the aligned body (on out's 16-byte grid):
  *         W chunks of ceil(packs/W) packs each (the last ones may be short or empty), or, on the
- *         16-byte path with W <= 8 (the last arriver from 8 MiB per rank buffer, per-tile flags
- *         from 16 to 64 MiB), one run of 16 KiB units per XCD; the few elements before out's first
- *         16-byte boundary and after its last whole pack are reduced with the first share.  (mr_reduce_scatter_sum's chunks, which are
- *         defined on element indices, coincide with these when n is a multiple of 16 bytes and out
- *         is 16-byte aligned.)  Needs a workspace (see below).
+ *         16-byte path with W <= 8 (the last arriver at any size, per-tile flags from 16 to
+ *         64 MiB), one run of units per XCD (1, 4 or 16 KiB of output each, by size); the few
+ *         elements before out's first 16-byte boundary and after its last whole pack are reduced
+ *         with the first share.  (mr_reduce_scatter_sum's chunks, which are defined on element
+ *         indices, coincide with the W chunks when n is a multiple of 16 bytes and out is 16-byte
+ *         aligned.)  Needs a workspace (see below).
  *  stream hipStream_t to enqueue on.
  */
 mr_status mr_allreduce_sum(const void* const* bufs, int W, size_t n, mr_dtype dtype, void* out,
@@ -180,8 +181,8 @@ mr_status mr_reduce_scatter_sum(const void* const* bufs, int W, size_t n, mr_dty
  *    ends; the first call on a device looks its address up and clears it on `stream`;
  *  - a rank buffer larger than MR_NOALLOC_MAX_BYTES (n * element size) -> MR_ERR_WORKSPACE, nothing
  *    enqueued;
- *  - the two-shot hand-off is always the last arriver (on chunk tiles below 8 MiB per rank buffer, on
- *    XCD-local units from 8 MiB on the 16-byte path with W <= 8), ignoring MR_OPT_TWOSHOT_SYNC and
+ *  - the two-shot hand-off is always the last arriver (on XCD-local units on the 16-byte path with
+ *    W <= 8, else on chunk tiles), ignoring MR_OPT_TWOSHOT_SYNC and
  *    MR_OPT_TILE_SHAPE: no workgroup of it ever waits, so it never leaves a barrier word set after a
  *    launch and never produces an invalid output; there is no error word to check;
  *  - every call on one GPU shares that GPU's array: two-shot calls that overlap in time on one GPU (on
@@ -273,8 +274,9 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  *   MR_TWOSHOT_SYNC_GRID  grid barrier: waits for every phase-1 tile of every chunk;
  *   MR_TWOSHOT_SYNC_LAST  no waiting: each group of phase-1 tiles counts its releases, and the
  *                         workgroup whose release completes the group copies it.
- *   Under TILE (16 to 64 MiB per rank buffer) and LAST (from 8 MiB) the 16-byte path with W <= 8
- *   runs on XCD-local units (16 KiB of output each, one run per XCD); otherwise on W chunks.
+ *   Under TILE (16 to 64 MiB per rank buffer) and LAST (any size) the 16-byte path with W <= 8 runs
+ *   on XCD-local units (16 KiB of output each from 8 MiB per rank buffer, 4 or 1 KiB below; one run
+ *   per XCD) unless MR_OPT_TILE_SHAPE forces a tile shape; otherwise on W chunks.
  * MR_OPT_SPIN_LIMIT    polls a waiting workgroup makes before it gives up and sets the workspace error
  *                      word (see mr_workspace_check); default 2^22.  A value of 0 makes every wait
  *                      that is not already satisfied give up at once (for testing error handling).
@@ -312,8 +314,8 @@ mr_status mr_get_option(mr_option opt, int64_t* value);
 /* Library ABI version (major*100 + minor).  1.01 added MR_OPT_TILE_SHAPE, MR_TWOSHOT_SYNC_LAST and
  * MR_TWOSHOT_SYNC_AUTO (the new default hand-off); 1.02 added MR_TILE_WIDE_PAIR; 1.03 added
  * mr_allgather_param_contig_sdma, mr_sdma_engines and MR_ERR_ENGINE; 1.04 added
- * mr_allreduce_sum_noalloc and the last-arriver hand-off on XCD-local units (the default from 8 to
- * 32 MiB per rank buffer). */
+ * mr_allreduce_sum_noalloc and the last-arriver hand-off on XCD-local units (the default up to 32 MiB
+ * per rank buffer). */
 int mr_version(void);
 
 #ifdef __cplusplus

@@ -196,7 +196,8 @@ def test_xcd_last_arriver_groups_cover_every_unit_once(L):
     one arrival word per group inside the flag area, and that area inside the workspace's."""
     rng = random.Random(4)
     cases = [(8, 8_388_608, "bf16", 0, "auto", "auto"), (8, 2_097_152, "fp32", 0, "auto", "auto"),
-             (8, 8_388_608 + 40, "bf16", 6, "last", "auto")]
+             (8, 8_388_608 + 40, "bf16", 6, "last", "auto"), (8, 131_072, "bf16", 0, "auto", "auto"),
+             (5, 600_001, "fp16", 4, "auto", "auto"), (3, 7, "fp32", 0, "auto", "auto")]
     for _ in range(40):
         W = rng.randint(1, 8)
         dt = rng.choice(["bf16", "fp16", "fp32"])
@@ -218,6 +219,8 @@ def test_xcd_last_arriver_groups_cover_every_unit_once(L):
             produced[u] = x
             words.setdefault(x * groups + s // 4, set()).add(u)
         assert set(produced) == set(range(units))
+        up = p["unit1"]
+        assert up in (64, 256, 1024) and (units - 1) * up < max(p["npacks"], 1) <= units * up
         for w, us in words.items():
             x, g = divmod(w, groups)
             assert us == {x * run + g * 4 + r for r in range(4) if g * 4 + r < run and x * run + g * 4 + r < units}
@@ -229,9 +232,10 @@ def test_default_hand_off_choices(L):
     def pick(W, n, dt="bf16", **kw):
         p = _plan(L, W, n, dt, 0, "auto", "auto", **kw)
         return p["sync"], p["xcd"]
-    # the last arriver up to 32 MiB per rank (XCD-local units from 8 MiB on the 16-byte path with W <= 8),
-    # per-tile flags above (XCD-local up to 64 MiB, then the chunk tiles)
-    assert pick(8, 2_097_152) == (3, 0)              # 4 MiB
+    # the last arriver on XCD-local units up to 32 MiB per rank (16-byte path, W <= 8), per-tile flags
+    # above (XCD-local up to 64 MiB, then the chunk tiles)
+    assert pick(8, 1000) == (3, 1)
+    assert pick(8, 2_097_152) == (3, 1)              # 4 MiB
     assert pick(8, 4_194_304) == (3, 1)              # 8 MiB
     assert pick(8, 8_388_608) == (3, 1)              # 16 MiB, the headline size
     assert pick(8, 4_194_304, "fp32") == (3, 1)      # 16 MiB
@@ -242,14 +246,20 @@ def test_default_hand_off_choices(L):
     assert pick(9, 8_388_608) == (3, 0)              # W > 8: chunk tiles
     assert pick(8, 8_388_608, same_phase=0) == (3, 1)  # realigned inputs: always the last arriver
     assert pick(8, 33_554_432, same_phase=0) == (3, 1)
-    assert pick(8, 2_097_152, same_phase=0) == (3, 0)
+    assert pick(8, 2_097_152, same_phase=0) == (3, 1)
     assert pick(12, 8_388_608, same_phase=0) == (3, 0)
+    # unit size of the last arriver's XCD-local units: narrow (64 packs) below 64 Ki packs, medium (256)
+    # below 512 Ki, wide (1024) from there; copier workgroups and MR_TILE_WIDE_PAIR always wide
+    for n, want in ((1000, 64), (524_287, 64), (524_288, 256), (4_194_303, 256), (4_194_304, 1024)):
+        assert _plan(L, 8, n, "bf16", 0, "auto", "auto")["unit1"] == want, n
+    assert _plan(L, 8, 1000, "bf16", 0, "last", "wide_pair")["unit1"] == 1024
+    assert _plan(L, 8, 16_777_216 + 8, "bf16", 0, "auto", "auto")["unit1"] == 1024
     # the allocation-free entry point only takes the last arriver, in which nothing waits
     for W, n in ((8, 8_388_608), (8, 1000), (12, 8_388_608), (8, 16_777_216)):
         for sync in ("chunk", "grid", "tile"):
             p = _plan(L, W, n, "bf16", 0, sync, "narrow", wait_free=1)
             assert p["sync"] == 3, (W, n, sync, p)
-            assert p["xcd"] == (1 if W <= 8 and n >= 4_194_304 else 0), (W, n, sync, p)
+            assert p["xcd"] == (1 if W <= 8 else 0), (W, n, sync, p)
 
 
 def _pieces(W, splits, es):
