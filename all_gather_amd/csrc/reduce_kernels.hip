@@ -694,8 +694,9 @@ __global__ __launch_bounds__(TB) void twoshot_vec(RankPtrs in, char* out, char* 
 // XCD-local two-shot with per-unit producer flags (16-byte path, W <= 8; the per-tile hand-off from
 // 16 MiB per rank buffer).
 //
-// Units.  The message is cut into units of one wide tile (256 lanes x 4 packs, 16 KiB of output) and
-// the units into kXcds runs of `run` consecutive units, one run per XCD.  Workgroup b belongs to run
+// Units.  The message is cut into units of one wide tile (256 lanes x 4 packs, 16 KiB of output; the
+// last-arriver form takes 4 KiB or 1 KiB units below 8 MiB per rank buffer) and the units into kXcds
+// runs of `run` consecutive units, one run per XCD.  Workgroup b belongs to run
 // x = b % kXcds, because workgroups are dealt to the XCDs in turn; its index s = b / kXcds inside the
 // run gives its role: s < run_padded reduces unit s of the run into the stage (phase 1), larger s copy
 // a group of kXcdGroup consecutive units of the run from the stage to out (phase 2, always units that

@@ -37,10 +37,15 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """sha256 (first 16 hex digits) of the reduce kernels' source with comments and blank space taken out,
+    so that a change to the code, not to its comments, marks the committed counters as stale."""
     h = hashlib.sha256()
     for path in KERNEL_SRC:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
