@@ -155,7 +155,7 @@ struct TwoShotPlan {
   uint32_t t1;           // phase-1 tiles per chunk
   uint32_t t2;           // phase-2 tiles per chunk
   uint32_t ratio;        // phase-1 tiles per phase-2 tile
-  uint32_t unit1;        // units per phase-1 tile
+  uint32_t unit1;        // units per phase-1 tile; XCD-local units: 16-byte packs per unit (64, 256 or 1024)
   uint32_t unit2;        // units per phase-2 tile
   uint32_t sync;         // TwoShotSync
   uint32_t spin_limit;   // bounded wait (polls)

@@ -38,8 +38,9 @@ int mrx_stream_mix(const void* const* reads, int K, void* out, size_t bytes, int
  * mrx_twoshot_plan -- the plan mr_allreduce_sum would launch for a two-shot call: W rank buffers of n
  * elements of `dtype`, out at address out_addr, all pointers at out's 16-byte phase if same_phase,
  * options sync_opt / shape_opt (MR_TWOSHOT_SYNC_*, MR_TILE_*), wait_free as mr_allreduce_sum_noalloc.
- * f[0..15] receive: xcd, units, run, run_padded, chunks, chunk_units, t1, t2, ratio, unit1, sync, vec,
- * head, npacks, grid (workgroups), flag words used.  Returns 0, or -1 for invalid arguments.
+ * f[0..15] receive: xcd, units, run, run_padded, chunks, chunk_units, t1, t2, ratio, unit1 (packs per
+ * phase-1 tile, or per XCD-local unit when xcd is 1), sync, vec, head, npacks, grid (workgroups), flag
+ * words used.  Returns 0, or -1 for invalid arguments.
  */
 int mrx_twoshot_plan(int W, size_t n, int dtype, uintptr_t out_addr, int same_phase, int sync_opt, int shape_opt,
                      int wait_free, uint64_t* f, int nf);
