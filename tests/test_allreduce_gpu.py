@@ -193,12 +193,13 @@ def test_twoshot_stale_stage_is_never_read(sync):
 @pytest.mark.parametrize("sync", ["tile", "chunk", "grid", "last"])
 def test_twoshot_poisoned_stage_stress(sync):
     """Before every launch, a fill on the launch stream overwrites the whole stage (and out) with 0xFF
-    bytes, a NaN in every element; 80 launches per tile shape, at sizes whose grids differ, must all
+    bytes, a NaN in every element; 80 launches per tile shape, at sizes whose grids differ (under the
+    last arriver, auto takes XCD-local units of 1 KiB and 4 KiB at the two auto sizes), must all
     match the oracle bit for bit.  A phase-2 copy that ran ahead of its producer, or a phase-1 tile
     that was never written, would publish the poison."""
     W = 8
     cases = [("narrow", 30_011), ("medium", 1_000_003), ("wide", 4_194_304 + 8), ("auto", 2_500_001),
-             ("wide_pair", 8_388_608 + 24)]
+             ("auto", 300_017), ("wide_pair", 8_388_608 + 24)]
     n_max = max(n for _, n in cases)
     ws = torch.empty(mr.workspace_bytes(W, n_max, "bf16"), dtype=torch.uint8, device=device())
     flags_cap = ws.numel() >> 8
