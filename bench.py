@@ -380,122 +380,134 @@ def main():
 
     paths = {}
     if not args.only_headline:
-        # cache-resident one-shot: the same set every step (labelled: not an HBM figure)
-        ms_w = time_steps(one[:1], K, args.warmup, stream)
-        paths["oneshot_cache_resident"] = {"us": ms_w / K * 1e3, "GBps_algorithmic": algo / (ms_w / K * 1e-3) / 1e9,
-                                           "note": "one buffer set reused; served partly from cache, not HBM"}
-        # reduce-scatter: rank 0's 1/W share, rotating sets
-        off, cnt = mr.reduce_scatter_chunk(n, W, dtype, 0)
-        rs_out = [torch.empty(cnt, dtype=torch.bfloat16, device=dev) for _ in sets]
-        rs = [mr.prepare_reduce_scatter(b, 0, o) for (b, _), o in zip(sets, rs_out)]
-        ms_rs = time_steps(rs, K, args.warmup, stream)
-        t_rs = ms_rs / K * 1e-3
-        rs_bytes = (W + 1) * cnt * s
-        paths["reduce_scatter_rank0"] = {"us": t_rs * 1e6, "GBps": rs_bytes / t_rs / 1e9, "bytes": rs_bytes,
-                                         "elements": cnt}
-        log(f"[bench] reduce_scatter (rank 0 share, {cnt} elements): {t_rs * 1e6:.2f} us/launch, "
-            f"{rs_bytes / t_rs / 1e9:.1f} GB/s")
-        # two-shot, rotating sets, under the default hand-off (at this size the last arriver on XCD-local
-        # units) and under each other one
-        two = [mr.prepare_allreduce(b, o, "twoshot") for b, o in sets]
-        actual2 = (W + 3) * n * s
-        kernels = {"auto": "twoshot_xcd<last arriver> (XCD-local units, the default at this size)",
-                   "tile": "twoshot_xcd<copier workgroups> (XCD-local units)",
-                   "chunk": "twoshot_vec<chunk barrier>", "grid": "twoshot_vec<grid barrier>"}
-        for sync in ("auto", "tile", "chunk", "grid"):
-            mr.set_option("twoshot_sync", sync)
-            two[0]()
-            torch.cuda.synchronize()
-            ms2 = time_steps(two, K, args.warmup, stream)
-            t2 = ms2 / K * 1e-3
-            paths[f"twoshot_{sync}"] = {"us": t2 * 1e6, "GBps_metric_bytes": algo / t2 / 1e9,
-                                        "GBps_actual_bytes": actual2 / t2 / 1e9, "actual_bytes": actual2,
-                                        "frac_actual_bytes": actual2 / t2 / 1e9 / PEAK_GBS,
-                                        "kernel": kernels[sync],
-                                        "barrier_error_word": mr.workspace_check()}
-            log(f"[bench] twoshot ({sync}): {t2 * 1e6:.2f} us/launch, {algo / t2 / 1e9:.1f} GB/s (metric bytes), "
-                f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")
-        mr.set_option("twoshot_sync", "auto")
-        # reference: the same two phases as two launches (one-shot into a stage tensor, then a plain copy
-        # of it into out by the gather kernel), same rotating sets -- what the in-kernel hand-off is
-        # measured against
-        stages = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in sets]
-        two_launch = []
-        for (b, o), stg in zip(sets, stages):
-            red = mr.prepare_allreduce(b, stg, "oneshot")
-            cp = mr.prepare_allgather_shards([stg], o)
-            two_launch.append(lambda red=red, cp=cp: (red(), cp()))
-        ms_tl = time_steps(two_launch, K, args.warmup, stream)
-        t_tl = ms_tl / K * 1e-3
-        paths["twoshot_two_launch_reference"] = {"us": t_tl * 1e6, "GBps_actual_bytes": actual2 / t_tl / 1e9,
-                                                 "note": "one-shot into a stage tensor, then a copy kernel; two "
-                                                         "launches per step, no in-kernel hand-off"}
-        log(f"[bench] two-launch reference (one-shot into a stage, then a copy): {t_tl * 1e6:.2f} us/step")
-        del stages, two_launch
-        # param-contiguous scatter: W=8, G=4, P=64 log-uniform splits, bf16 random bits
-        c4 = workloads.FSDP_SPLITS_W8_G4_P64
-        splits = [int(x) for x in workloads.log_uniform_splits(c4["seed"], c4["P"])]
-        T = sum(splits)
-        gsets = []
-        for k in range(2):
-            src = torch.randint(-32768, 32767, (c4["W"] * T,), dtype=torch.int16, device=dev).view(torch.bfloat16)
-            gsets.append(mr.prepare_allgather_param_contig(src, c4["W"], c4["G"], splits, torch.empty_like(src)))
-        gbytes = 2 * c4["W"] * T * 2
-        Kg = max(20, K // 10)
-        msg = time_steps(gsets, Kg, max(2, args.warmup // 10), stream)
-        tg = msg / Kg * 1e-3
-        paths["param_contig"] = {"us": tg * 1e6, "GBps": gbytes / tg / 1e9, "bytes": gbytes, "W": c4["W"],
-                                 "G": c4["G"], "P": c4["P"], "T": T, "dtype": "bf16",
-                                 "frac": gbytes / tg / 1e9 / PEAK_GBS}
-        paths["param_contig"].update(_same_bytes_copy(mr, gsets, Kg, args.warmup, stream, gbytes, gbytes / tg / 1e9))
-        log(f"[bench] param_contig: {tg * 1e6:.1f} us/launch, {gbytes / tg / 1e9:.1f} GB/s ({gbytes} B); plain copy of "
-            f"the same bytes {paths['param_contig']['copy_same_bytes_GBps']:.1f} GB/s")
-        # the same gather on the SDMA copy engines (synchronous calls; no compute units)
-        sdma_sets = [mr.prepare_allgather_param_contig_sdma(c.keepalive[1], c4["W"], c4["G"], splits, c.keepalive[2])
-                     for c in gsets]
-        Ks = 10
-        mss = time_steps(sdma_sets, Ks, 2, stream)
-        ts = mss / Ks * 1e-3
-        paths["param_contig_sdma"] = {"us": ts * 1e6, "GBps": gbytes / ts / 1e9, "bytes": gbytes, "dtype": "bf16",
-                                      "engines": mr.sdma_engines(),
-                                      "note": "SDMA copy engines through the HSA runtime; synchronous calls, "
-                                              "host-observed time per call"}
-        log(f"[bench] param_contig on {mr.sdma_engines()} SDMA engines: {ts * 1e6:.1f} us/call, {gbytes / ts / 1e9:.1f} GB/s")
-        # the same splits in fp32 (4-byte elements: twice the bytes of the bf16 case)
-        fsets = []
-        for k in range(2):
-            src = torch.randint(-2 ** 31, 2 ** 31 - 1, (c4["W"] * T,), dtype=torch.int32, device=dev).view(torch.float32)
-            fsets.append(mr.prepare_allgather_param_contig(src, c4["W"], c4["G"], splits, torch.empty_like(src)))
-        fbytes = 2 * c4["W"] * T * 4
-        msf = time_steps(fsets, Kg, max(2, args.warmup // 10), stream)
-        tf = msf / Kg * 1e-3
-        paths["param_contig_fp32"] = {"us": tf * 1e6, "GBps": fbytes / tf / 1e9, "bytes": fbytes, "W": c4["W"],
-                                      "G": c4["G"], "P": c4["P"], "T": T, "dtype": "fp32",
-                                      "frac": fbytes / tf / 1e9 / PEAK_GBS}
-        paths["param_contig_fp32"].update(_same_bytes_copy(mr, fsets, Kg, args.warmup, stream, fbytes, fbytes / tf / 1e9))
-        log(f"[bench] param_contig fp32: {tf * 1e6:.1f} us/launch, {fbytes / tf / 1e9:.1f} GB/s "
-            f"({fbytes / tf / 1e9 / PEAK_GBS:.1%} of peak)")
-        del fsets
-        torch.cuda.empty_cache()
-        # the same gathers written straight from W separate shard buffers
-        shard_sets = []
-        for k in range(2):
-            shards = [torch.randint(-32768, 32767, (T,), dtype=torch.int16, device=dev).view(torch.bfloat16)
-                      for _ in range(c4["W"])]
-            shard_sets.append((shards, torch.empty(c4["W"] * T, dtype=torch.bfloat16, device=dev)))
-        for name, kw in (("allgather_into_tensor", {}), ("param_contig_shards", {"G": c4["G"], "splits": splits})):
-            calls = [mr.prepare_allgather_shards(sh, o, **kw) for sh, o in shard_sets]
-            msx = time_steps(calls, Kg, max(2, args.warmup // 10), stream)
-            tx = msx / Kg * 1e-3
-            paths[name] = {"us": tx * 1e6, "GBps": gbytes / tx / 1e9, "bytes": gbytes, "W": c4["W"], "T": T}
-            log(f"[bench] {name}: {tx * 1e6:.1f} us/launch, {gbytes / tx / 1e9:.1f} GB/s")
-        del shard_sets
-        torch.cuda.empty_cache()
-        paths["contention"] = contention_leg(mr, torch, dev, stream, gsets, gbytes, sdma_sets)
-        del gsets, sdma_sets
-        torch.cuda.empty_cache()
-        if not args.no_sweep:
-            paths["sweep_w8"] = sweep_leg(mr, torch, dev)
+        # secondary legs: a failure in one of them is recorded in the line instead of losing the
+        # headline measured above
+        try:
+            # cache-resident one-shot: the same set every step (labelled: not an HBM figure)
+            ms_w = time_steps(one[:1], K, args.warmup, stream)
+            paths["oneshot_cache_resident"] = {"us": ms_w / K * 1e3, "GBps_algorithmic": algo / (ms_w / K * 1e-3) / 1e9,
+                                               "note": "one buffer set reused; served partly from cache, not HBM"}
+            # reduce-scatter: rank 0's 1/W share, rotating sets
+            off, cnt = mr.reduce_scatter_chunk(n, W, dtype, 0)
+            rs_out = [torch.empty(cnt, dtype=torch.bfloat16, device=dev) for _ in sets]
+            rs = [mr.prepare_reduce_scatter(b, 0, o) for (b, _), o in zip(sets, rs_out)]
+            ms_rs = time_steps(rs, K, args.warmup, stream)
+            t_rs = ms_rs / K * 1e-3
+            rs_bytes = (W + 1) * cnt * s
+            paths["reduce_scatter_rank0"] = {"us": t_rs * 1e6, "GBps": rs_bytes / t_rs / 1e9, "bytes": rs_bytes,
+                                             "elements": cnt}
+            log(f"[bench] reduce_scatter (rank 0 share, {cnt} elements): {t_rs * 1e6:.2f} us/launch, "
+                f"{rs_bytes / t_rs / 1e9:.1f} GB/s")
+            # two-shot, rotating sets, under the default hand-off (at this size the last arriver on XCD-local
+            # units) and under each other one
+            two = [mr.prepare_allreduce(b, o, "twoshot") for b, o in sets]
+            actual2 = (W + 3) * n * s
+            kernels = {"auto": "twoshot_xcd<last arriver> (XCD-local units, the default at this size)",
+                       "tile": "twoshot_xcd<copier workgroups> (XCD-local units)",
+                       "chunk": "twoshot_vec<chunk barrier>", "grid": "twoshot_vec<grid barrier>"}
+            for sync in ("auto", "tile", "chunk", "grid"):
+                mr.set_option("twoshot_sync", sync)
+                two[0]()
+                torch.cuda.synchronize()
+                ms2 = time_steps(two, K, args.warmup, stream)
+                t2 = ms2 / K * 1e-3
+                paths[f"twoshot_{sync}"] = {"us": t2 * 1e6, "GBps_metric_bytes": algo / t2 / 1e9,
+                                            "GBps_actual_bytes": actual2 / t2 / 1e9, "actual_bytes": actual2,
+                                            "frac_actual_bytes": actual2 / t2 / 1e9 / PEAK_GBS,
+                                            "kernel": kernels[sync],
+                                            "barrier_error_word": mr.workspace_check()}
+                log(f"[bench] twoshot ({sync}): {t2 * 1e6:.2f} us/launch, {algo / t2 / 1e9:.1f} GB/s (metric bytes), "
+                    f"{actual2 / t2 / 1e9:.1f} GB/s (actual)")
+            mr.set_option("twoshot_sync", "auto")
+            # reference: the same two phases as two launches (one-shot into a stage tensor, then a plain copy
+            # of it into out by the gather kernel), same rotating sets -- what the in-kernel hand-off is
+            # measured against
+            stages = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in sets]
+            two_launch = []
+            for (b, o), stg in zip(sets, stages):
+                red = mr.prepare_allreduce(b, stg, "oneshot")
+                cp = mr.prepare_allgather_shards([stg], o)
+                two_launch.append(lambda red=red, cp=cp: (red(), cp()))
+            ms_tl = time_steps(two_launch, K, args.warmup, stream)
+            t_tl = ms_tl / K * 1e-3
+            paths["twoshot_two_launch_reference"] = {"us": t_tl * 1e6, "GBps_actual_bytes": actual2 / t_tl / 1e9,
+                                                     "note": "one-shot into a stage tensor, then a copy kernel; two "
+                                                             "launches per step, no in-kernel hand-off"}
+            log(f"[bench] two-launch reference (one-shot into a stage, then a copy): {t_tl * 1e6:.2f} us/step")
+            del stages, two_launch
+            # param-contiguous scatter: W=8, G=4, P=64 log-uniform splits, bf16 random bits
+            c4 = workloads.FSDP_SPLITS_W8_G4_P64
+            splits = [int(x) for x in workloads.log_uniform_splits(c4["seed"], c4["P"])]
+            T = sum(splits)
+            gsets = []
+            for k in range(2):
+                src = torch.randint(-32768, 32767, (c4["W"] * T,), dtype=torch.int16, device=dev).view(torch.bfloat16)
+                gsets.append(mr.prepare_allgather_param_contig(src, c4["W"], c4["G"], splits, torch.empty_like(src)))
+            gbytes = 2 * c4["W"] * T * 2
+            Kg = max(20, K // 10)
+            msg = time_steps(gsets, Kg, max(2, args.warmup // 10), stream)
+            tg = msg / Kg * 1e-3
+            paths["param_contig"] = {"us": tg * 1e6, "GBps": gbytes / tg / 1e9, "bytes": gbytes, "W": c4["W"],
+                                     "G": c4["G"], "P": c4["P"], "T": T, "dtype": "bf16",
+                                     "frac": gbytes / tg / 1e9 / PEAK_GBS}
+            paths["param_contig"].update(_same_bytes_copy(mr, gsets, Kg, args.warmup, stream, gbytes, gbytes / tg / 1e9))
+            log(f"[bench] param_contig: {tg * 1e6:.1f} us/launch, {gbytes / tg / 1e9:.1f} GB/s ({gbytes} B); plain copy of "
+                f"the same bytes {paths['param_contig']['copy_same_bytes_GBps']:.1f} GB/s")
+            # the same gather on the SDMA copy engines (synchronous calls; no compute units), if the device
+            # offers engines for its own memory
+            sdma_sets = None
+            if mr.sdma_engines() > 0:
+                sdma_sets = [mr.prepare_allgather_param_contig_sdma(c.keepalive[1], c4["W"], c4["G"], splits,
+                                                                    c.keepalive[2]) for c in gsets]
+                Ks = 10
+                mss = time_steps(sdma_sets, Ks, 2, stream)
+                ts = mss / Ks * 1e-3
+                paths["param_contig_sdma"] = {"us": ts * 1e6, "GBps": gbytes / ts / 1e9, "bytes": gbytes,
+                                              "dtype": "bf16", "engines": mr.sdma_engines(),
+                                              "note": "SDMA copy engines through the HSA runtime; synchronous calls, "
+                                                      "host-observed time per call"}
+                log(f"[bench] param_contig on {mr.sdma_engines()} SDMA engines: {ts * 1e6:.1f} us/call, "
+                    f"{gbytes / ts / 1e9:.1f} GB/s")
+            else:
+                paths["param_contig_sdma"] = {"skipped": "no SDMA engines offered for device-local copies"}
+            # the same splits in fp32 (4-byte elements: twice the bytes of the bf16 case)
+            fsets = []
+            for k in range(2):
+                src = torch.randint(-2 ** 31, 2 ** 31 - 1, (c4["W"] * T,), dtype=torch.int32, device=dev).view(torch.float32)
+                fsets.append(mr.prepare_allgather_param_contig(src, c4["W"], c4["G"], splits, torch.empty_like(src)))
+            fbytes = 2 * c4["W"] * T * 4
+            msf = time_steps(fsets, Kg, max(2, args.warmup // 10), stream)
+            tf = msf / Kg * 1e-3
+            paths["param_contig_fp32"] = {"us": tf * 1e6, "GBps": fbytes / tf / 1e9, "bytes": fbytes, "W": c4["W"],
+                                          "G": c4["G"], "P": c4["P"], "T": T, "dtype": "fp32",
+                                          "frac": fbytes / tf / 1e9 / PEAK_GBS}
+            paths["param_contig_fp32"].update(_same_bytes_copy(mr, fsets, Kg, args.warmup, stream, fbytes, fbytes / tf / 1e9))
+            log(f"[bench] param_contig fp32: {tf * 1e6:.1f} us/launch, {fbytes / tf / 1e9:.1f} GB/s "
+                f"({fbytes / tf / 1e9 / PEAK_GBS:.1%} of peak)")
+            del fsets
+            torch.cuda.empty_cache()
+            # the same gathers written straight from W separate shard buffers
+            shard_sets = []
+            for k in range(2):
+                shards = [torch.randint(-32768, 32767, (T,), dtype=torch.int16, device=dev).view(torch.bfloat16)
+                          for _ in range(c4["W"])]
+                shard_sets.append((shards, torch.empty(c4["W"] * T, dtype=torch.bfloat16, device=dev)))
+            for name, kw in (("allgather_into_tensor", {}), ("param_contig_shards", {"G": c4["G"], "splits": splits})):
+                calls = [mr.prepare_allgather_shards(sh, o, **kw) for sh, o in shard_sets]
+                msx = time_steps(calls, Kg, max(2, args.warmup // 10), stream)
+                tx = msx / Kg * 1e-3
+                paths[name] = {"us": tx * 1e6, "GBps": gbytes / tx / 1e9, "bytes": gbytes, "W": c4["W"], "T": T}
+                log(f"[bench] {name}: {tx * 1e6:.1f} us/launch, {gbytes / tx / 1e9:.1f} GB/s")
+            del shard_sets
+            torch.cuda.empty_cache()
+            paths["contention"] = contention_leg(mr, torch, dev, stream, gsets, gbytes, sdma_sets)
+            del gsets, sdma_sets
+            torch.cuda.empty_cache()
+            if not args.no_sweep:
+                paths["sweep_w8"] = sweep_leg(mr, torch, dev)
+        except Exception as e:  # noqa: BLE001 -- reported, not hidden
+            paths["error"] = f"{type(e).__name__}: {e}"
+            log(f"[bench] secondary legs stopped: {paths['error']}")
 
     cpu = None
     if not args.no_cpu_baseline:
