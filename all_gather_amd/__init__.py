@@ -26,7 +26,7 @@ STATUS = {
 }
 DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2, "int32": 3}
 MODE_CODE = {"oneshot": 0, "twoshot": 1}
-OPTION_CODE = {"twoshot_sync": 0, "spin_limit": 1, "tile_shape": 2}
+OPTION_CODE = {"twoshot_sync": 0, "spin_limit": 1, "tile_shape": 2, "sdma_cu_below": 3}
 TWOSHOT_SYNC = {"tile": 0, "chunk": 1, "grid": 2, "last": 3, "auto": 4}
 TILE_SHAPE = {"auto": 0, "wide": 1, "medium": 2, "narrow": 3, "wide_pair": 4}
 MAX_W = 16
@@ -319,8 +319,8 @@ def workspace_check(stream=None) -> int:
 
 
 def set_option(name: str, value) -> None:
-    """Set a process-wide option: ``twoshot_sync`` ("auto", "tile", "chunk", "grid", "last"), ``spin_limit`` (int)
-    or ``tile_shape`` ("auto", "wide", "medium", "narrow")."""
+    """Set a process-wide option: ``twoshot_sync`` ("auto", "tile", "chunk", "grid", "last"), ``spin_limit`` (int),
+    ``tile_shape`` ("auto", "wide", "medium", "narrow", "wide_pair") or ``sdma_cu_below`` (bytes)."""
     if name == "twoshot_sync" and isinstance(value, str):
         value = TWOSHOT_SYNC[value]
     if name == "tile_shape" and isinstance(value, str):

@@ -30,10 +30,23 @@ uint32_t env_u32(const char* name, uint32_t dflt, unsigned long lo, unsigned lon
   return (end && *end == 0 && x >= lo && x <= hi) ? static_cast<uint32_t>(x) : dflt;
 }
 
+// Piece size (bytes per rank of one parameter) below which mr_allgather_param_contig_sdma copies a
+// parameter with the param-contiguous kernel instead of the engines (MR_OPT_SDMA_CU_BELOW).  An engine
+// spends about 15 us on every copy beyond its bytes (2 KiB to 256 KiB pieces all took 15-17 us per copy
+// per engine) and moves about 51 GB/s, so a 1 MiB piece costs it 15 + 20 us.  Same-GPU A/B, W=8 G=4
+// P=64 FSDP-style splits bf16, per call alone / beside bf16 8192^3 GEMMs: every piece on the engines
+// 1076-1093 / 1101-1107 us, below 256 KiB on the kernel 796-804 / 871-875, below 1 MiB 689-696 / 873-876,
+// below 4 MiB 300-310 / 881-883; the GEMM's rate was the same in every case.  Beside the GEMM the
+// kernel part waits for compute units that the GEMM's workgroups hold, which sets the call's time.
+#ifndef MR_SDMA_CU_BELOW_DEFAULT
+#define MR_SDMA_CU_BELOW_DEFAULT (1u << 20)
+#endif
+
 // Process-wide options (mr_set_option); defaults may be overridden by the environment at load.
 std::atomic<uint32_t> g_spin_limit{env_u32("MR_SPIN_LIMIT", 1u << 22, 0, 0xffffffffUL)};
 std::atomic<uint32_t> g_twoshot_sync{env_u32("MR_TWOSHOT_SYNC", mr::kSyncAuto, MR_TWOSHOT_SYNC_TILE, MR_TWOSHOT_SYNC_AUTO)};
 std::atomic<uint32_t> g_tile_shape{env_u32("MR_TILE_SHAPE", mr::kShapeAuto, MR_TILE_AUTO, MR_TILE_WIDE_PAIR)};
+std::atomic<uint32_t> g_sdma_cu_below{env_u32("MR_SDMA_CU_BELOW", MR_SDMA_CU_BELOW_DEFAULT, 0, 0xffffffffUL)};
 const bool g_trace = env_u32("MR_TRACE", 0, 0, 1) != 0;
 
 mr_status hip_fail(hipError_t e) {
@@ -256,8 +269,10 @@ bool needs_realign(uint16_t mask, uintptr_t d) { return (mask & ~(1u << (d & 15u
 // output); otherwise per (node-block, parameter, slot) segment (the list output's separate buffers).
 // bytes: plan the same placement on bytes (element size 1, every count times the dtype's size), for
 // pointers that are not multiples of the element size.
+// cu_below: only parameters whose per-rank piece is smaller than this many bytes get tiles (the others
+// keep their offsets but no tile maps to them, so a launch copies the small parameters alone).
 mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, bool span, GatherPlan* gp,
-                      bool bytes = false) {
+                      bool bytes = false, uint64_t cu_below = UINT64_MAX) {
   if (G < 1 || W % G != 0) return MR_ERR_INVALID_ARG;
   if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return MR_ERR_INVALID_ARG;
@@ -280,7 +295,7 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
     uint64_t O = 0;
     for (int s = 0; s < P; ++s) {
       const uint64_t E = splits[s] * scale;
-      for (int r = 0; E && r < W; ++r) {
+      for (int r = 0; E && E * es < cu_below && r < W; ++r) {
         const uint64_t dst_off = (O * W + static_cast<uint64_t>(r) * E) * es;
         if (r < 16) gp->rm_mask |= static_cast<uint16_t>(1u << ((dst_off - (static_cast<uint64_t>(r) * T + O) * es) & 15u));
         if (r < static_cast<int>(gp->rank_mask.size()))
@@ -305,8 +320,9 @@ mr_status gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtyp
       a.O[i] = base;
       a.tile_prefix[i] = static_cast<uint32_t>(tiles);
       const uint64_t E = splits[s0 + i] * scale;
-      tiles += span ? mr::gather_tiles_per_segment(E * static_cast<uint64_t>(W), static_cast<uint32_t>(es))
-                    : static_cast<uint64_t>(G) * mr::gather_tiles_per_segment(E, static_cast<uint32_t>(es));
+      if (E * es < cu_below)
+        tiles += span ? mr::gather_tiles_per_segment(E * static_cast<uint64_t>(W), static_cast<uint32_t>(es))
+                      : static_cast<uint64_t>(G) * mr::gather_tiles_per_segment(E, static_cast<uint32_t>(es));
       base += E;
       if (tiles >= (1ull << 31)) return MR_ERR_INVALID_ARG;
     }
@@ -328,6 +344,7 @@ struct CachedPlan {
   bool used = false;
   bool span = false;
   bool bytes = false;
+  uint64_t cu_below = UINT64_MAX;
   int W = 0, G = 0, P = 0;
   mr_dtype dtype = MR_BF16;
   std::vector<uint64_t> splits;
@@ -338,11 +355,12 @@ thread_local CachedPlan t_plans[kPlanSlots];
 thread_local int t_plan_next = 0;
 
 mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dtype dtype, bool span,
-                             const GatherPlan** out, bool bytes = false) {
+                             const GatherPlan** out, bool bytes = false, uint64_t cu_below = UINT64_MAX) {
   if (P < 1 || !splits) return MR_ERR_INVALID_ARG;
   const size_t key_bytes = static_cast<size_t>(P) * sizeof(uint64_t);
   for (const CachedPlan& c : t_plans)
-    if (c.used && c.span == span && c.bytes == bytes && c.W == W && c.G == G && c.P == P && c.dtype == dtype &&
+    if (c.used && c.span == span && c.bytes == bytes && c.cu_below == cu_below && c.W == W && c.G == G && c.P == P &&
+        c.dtype == dtype &&
         std::memcmp(c.splits.data(), splits, key_bytes) == 0) {
       *out = &c.plan;
       return MR_OK;
@@ -350,10 +368,11 @@ mr_status cached_gather_plan(int W, int G, const uint64_t* splits, int P, mr_dty
   CachedPlan& c = t_plans[t_plan_next];
   t_plan_next = (t_plan_next + 1) % kPlanSlots;
   c.used = false;
-  const mr_status s = gather_plan(W, G, splits, P, dtype, span, &c.plan, bytes);
+  const mr_status s = gather_plan(W, G, splits, P, dtype, span, &c.plan, bytes, cu_below);
   if (s != MR_OK) return s;
   c.span = span;
   c.bytes = bytes;
+  c.cu_below = cu_below;
   c.W = W;
   c.G = G;
   c.P = P;
@@ -436,7 +455,7 @@ const char* mr_status_string(mr_status s) {
 
 int mr_last_hip_error(void) { return g_last_hip_error; }
 
-int mr_version(void) { return 104; }
+int mr_version(void) { return 105; }
 
 size_t mr_workspace_bytes(int W, size_t n, mr_dtype dtype) {
   if (W < 1 || W > MR_MAX_W || !is_float(dtype)) return 0;
@@ -459,6 +478,10 @@ mr_status mr_set_option(mr_option opt, int64_t value) {
       if (value < MR_TILE_AUTO || value > MR_TILE_WIDE_PAIR) return MR_ERR_INVALID_ARG;
       g_tile_shape.store(static_cast<uint32_t>(value));
       return MR_OK;
+    case MR_OPT_SDMA_CU_BELOW:
+      if (value < 0 || value > 0xffffffffll) return MR_ERR_INVALID_ARG;
+      g_sdma_cu_below.store(static_cast<uint32_t>(value));
+      return MR_OK;
     default:
       return MR_ERR_INVALID_ARG;
   }
@@ -470,6 +493,7 @@ mr_status mr_get_option(mr_option opt, int64_t* value) {
     case MR_OPT_TWOSHOT_SYNC: *value = g_twoshot_sync.load(); return MR_OK;
     case MR_OPT_SPIN_LIMIT: *value = g_spin_limit.load(); return MR_OK;
     case MR_OPT_TILE_SHAPE: *value = g_tile_shape.load(); return MR_OK;
+    case MR_OPT_SDMA_CU_BELOW: *value = g_sdma_cu_below.load(); return MR_OK;
     default: return MR_ERR_INVALID_ARG;
   }
 }
@@ -546,23 +570,29 @@ mr_status mr_allgather_param_contig(const void* src, int W, int G, const uint64_
 mr_status mr_allgather_param_contig_sdma(const void* src, int W, int G, const uint64_t* splits, int P, mr_dtype dtype,
                                          void* out, mr_stream stream) {
   if (W < 1 || W > 65535) return MR_ERR_INVALID_ARG;
+  const uint64_t cu_below = g_sdma_cu_below.load();
   const GatherPlan* gp = nullptr;
-  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp);  // engines copy bytes: any alignment
+  // the plan gives the kernel the tiles of the parameters below cu_below and the engines their offsets
+  mr_status s = cached_gather_plan(W, G, splits, P, dtype, P > 1, &gp, !gather_on_grid(dtype, {src, out}), cu_below);
   if (s != MR_OK || gp->T == 0) return s;
   if (!src || !out) return MR_ERR_INVALID_ARG;
   const uint64_t total_bytes = static_cast<uint64_t>(W) * gp->T * gp->es;
   if (overlap(reinterpret_cast<uintptr_t>(src), total_bytes, reinterpret_cast<uintptr_t>(out), total_bytes))
     return MR_ERR_ALIAS;
-  // one piece per (parameter, rank), in the order of the page's node-block -> split -> slot loop;
-  // pieces that continue the previous one on both sides are merged (one parameter: a single copy)
+  // one piece per (parameter, rank) of the other parameters, in the order of the page's node-block ->
+  // split -> slot loop; pieces that continue the previous one on both sides are merged (one parameter:
+  // a single copy)
   std::vector<mr::CopyPiece> pieces;
   const char* sb = static_cast<const char*>(src);
   char* ob = static_cast<char*>(out);
   const uint64_t es = gp->es, T = gp->T;
+  bool cu_part = false;
+  for (const mr::GatherArgs& g : gp->groups) cu_part = cu_part || g.total_tiles != 0;
   for (int m = 0; m < W / G; ++m)
     for (const mr::GatherArgs& g : gp->groups)
       for (uint32_t i = 0; i < g.P; ++i) {
         const uint64_t O = g.O[i], E = g.O[i + 1] - O;
+        if (E * es < cu_below) continue;  // copied by the kernel
         for (int gg = 0; E && gg < G; ++gg) {
           const uint64_t r = static_cast<uint64_t>(m) * G + gg;
           const mr::CopyPiece c{sb + (r * T + O) * es, ob + (O * W + r * E) * es, E * es};
@@ -573,14 +603,28 @@ mr_status mr_allgather_param_contig_sdma(const void* src, int W, int G, const ui
             pieces.push_back(c);
         }
       }
-  const hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));  // src is ready
+  int hsa = 0;
+  if (mr::sdma_engine_count(&hsa) == 0) {  // before anything is enqueued
+    g_last_hip_error = hsa;
+    return MR_ERR_ENGINE;
+  }
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(st);  // src is ready
   if (e != hipSuccess) return hip_fail(e);
+  if (cu_part) {  // the small parameters' kernel runs on the stream beside the engine copies
+    s = gather_launch(*gp, [&](mr::GatherArgs& a) {
+      a.src = sb;
+      a.out = ob;
+    }, needs_realign(gp->rm_mask, reinterpret_cast<uintptr_t>(src) - reinterpret_cast<uintptr_t>(out)), st);
+    if (s != MR_OK) return s;
+  }
   const int rc = mr::sdma_copy(pieces.data(), pieces.size());
+  e = cu_part ? hipStreamSynchronize(st) : hipSuccess;
   if (rc != 0) {
     g_last_hip_error = rc;
     return MR_ERR_ENGINE;
   }
-  return MR_OK;
+  return e == hipSuccess ? MR_OK : hip_fail(e);
 }
 
 // ------------------------------------------------------------------------ planning hooks (mr_probe.h)
@@ -633,6 +677,17 @@ int mrx_gather_phase_masks(int W, int G, const uint64_t* splits, int P, int dtyp
 
 int mrx_needs_realign(uint16_t mask, uint64_t base_difference) {
   return needs_realign(mask, static_cast<uintptr_t>(base_difference)) ? 1 : 0;
+}
+
+int mrx_gather_tiles(int W, int G, const uint64_t* splits, int P, int dtype, uint64_t cu_below, uint32_t* prefix,
+                     int n_prefix, uint16_t* rm_mask) {
+  if (W < 1 || W > 65535 || P > static_cast<int>(mr::kMaxParams) || !prefix || n_prefix < P + 1 || !rm_mask) return -1;
+  GatherPlan gp;
+  const mr_status s = gather_plan(W, G, splits, P, static_cast<mr_dtype>(dtype), P > 1, &gp, false, cu_below);
+  if (s != MR_OK) return s;
+  *rm_mask = gp.rm_mask;
+  for (int i = 0; i <= P; ++i) prefix[i] = gp.groups.empty() ? 0 : gp.groups[0].tile_prefix[i];
+  return 0;
 }
 
 int mr_sdma_engines(void) {

@@ -64,6 +64,16 @@ int mrx_gather_phase_masks(int W, int G, const uint64_t* splits, int P, int dtyp
                            uint16_t* rank_masks, int n_rank_masks);
 int mrx_needs_realign(uint16_t mask, uint64_t base_difference);
 
+/*
+ * mrx_gather_tiles -- the tile table the gather planner builds for a split table of at most 128
+ * parameters when only parameters whose per-rank piece is smaller than cu_below bytes are copied by the
+ * kernel (the SDMA gather's compute-unit part; UINT64_MAX: every parameter): prefix[s] = tiles of the
+ * parameters before s, s = 0..P (n_prefix >= P + 1), and *rm_mask the rank-major phase mask over those
+ * parameters' pieces.  Returns 0 or an mr_status (-1 for a table too small or P > 128).
+ */
+int mrx_gather_tiles(int W, int G, const uint64_t* splits, int P, int dtype, uint64_t cu_below, uint32_t* prefix,
+                     int n_prefix, uint16_t* rm_mask);
+
 #ifdef __cplusplus
 }
 #endif

@@ -173,12 +173,24 @@ def _same_bytes_copy(mr, prepared, K, warmup, stream, nbytes, gbs):
     return {"copy_same_bytes_us": t * 1e6, "copy_same_bytes_GBps": copy, "frac_of_copy_same_bytes": gbs / copy}
 
 
+def _with_option(mr, name, value, call):
+    """`call` made with option `name` set to `value`, and the option's previous value restored after it."""
+    def run():
+        prev = mr.get_option(name)
+        mr.set_option(name, value)
+        try:
+            call()
+        finally:
+            mr.set_option(name, prev)
+    return run
+
+
 def _probe_ok(rc):
     if rc != 0:
         raise RuntimeError(f"mrx_stream_mix failed: {rc}")
 
 
-def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes, sdma_sets=None):
+def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes, sdma_legs=()):
     """Ops alone and beside bf16 8192^3 GEMMs on a second stream (default priority): W=8 fp32 one-shot
     and two-shot at 512 MiB per rank, and the param-contiguous scatter at the FSDP-style splits.  GB/s of the op and
     TFLOP/s of the GEMM, alone and together."""
@@ -198,8 +210,8 @@ def contention_leg(mr, torch, dev, stream, gather_sets, gather_bytes, sdma_sets=
     legs = [("reduce_oneshot_fp32_512MiB", mr.prepare_allreduce(bufs, out, "oneshot"), algo, 20, 24),
             ("reduce_twoshot_fp32_512MiB", mr.prepare_allreduce(bufs, out, "twoshot"), algo, 20, 24),
             ("scatter_fsdp_splits_bf16", gather_sets[0], gather_bytes, 100, 24)]
-    if sdma_sets:
-        legs.append(("scatter_fsdp_splits_bf16_sdma", sdma_sets[0], gather_bytes, 12, 24))
+    for name, call in sdma_legs:
+        legs.append((name, call, gather_bytes, 12, 24))
     for name, call, nbytes, R, G in legs:
         t_op, t_gemm, t_op_c, t_gemm_c = _overlap(torch, stream, side, call, R, gemm, G)
         r = {"op_GBps_alone": nbytes / t_op / 1e9, "op_GBps_with_gemm": nbytes / t_op_c / 1e9,
@@ -455,19 +467,30 @@ def main():
                 f"the same bytes {paths['param_contig']['copy_same_bytes_GBps']:.1f} GB/s")
             # the same gather on the SDMA copy engines (synchronous calls; no compute units), if the device
             # offers engines for its own memory
-            sdma_sets = None
+            sdma_legs = []
             if mr.sdma_engines() > 0:
+                cu_below = mr.get_option("sdma_cu_below")
                 sdma_sets = [mr.prepare_allgather_param_contig_sdma(c.keepalive[1], c4["W"], c4["G"], splits,
                                                                     c.keepalive[2]) for c in gsets]
+                engines_only = [_with_option(mr, "sdma_cu_below", 0, c) for c in sdma_sets]
+                big = [E for E in splits if E * 2 >= cu_below]
+                split_note = (f"parameters with pieces of {cu_below} B and more on the engines "
+                              f"({c4['W'] * sum(-(-E * 2 // (4 << 20)) for E in big)} copies), the other "
+                              f"{c4['P'] - len(big)} parameters ({c4['W'] * 2 * (T - sum(big))} B) on one "
+                              f"compute-unit launch beside them")
                 Ks = 10
-                mss = time_steps(sdma_sets, Ks, 2, stream)
-                ts = mss / Ks * 1e-3
-                paths["param_contig_sdma"] = {"us": ts * 1e6, "GBps": gbytes / ts / 1e9, "bytes": gbytes,
-                                              "dtype": "bf16", "engines": mr.sdma_engines(),
-                                              "note": "SDMA copy engines through the HSA runtime; synchronous calls, "
-                                                      "host-observed time per call"}
-                log(f"[bench] param_contig on {mr.sdma_engines()} SDMA engines: {ts * 1e6:.1f} us/call, "
-                    f"{gbytes / ts / 1e9:.1f} GB/s")
+                for key, sets_, note in (("param_contig_sdma", sdma_sets, split_note),
+                                         ("param_contig_sdma_engines_only", engines_only, "every piece on the engines")):
+                    mss = time_steps(sets_, Ks, 2, stream)
+                    ts = mss / Ks * 1e-3
+                    paths[key] = {"us": ts * 1e6, "GBps": gbytes / ts / 1e9, "bytes": gbytes, "dtype": "bf16",
+                                  "engines": mr.sdma_engines(), "sdma_cu_below": cu_below if sets_ is sdma_sets else 0,
+                                  "note": "SDMA copy engines through the HSA runtime; synchronous calls, host-observed "
+                                          "time per call; " + note}
+                    log(f"[bench] {key} ({mr.sdma_engines()} SDMA engines): {ts * 1e6:.1f} us/call, "
+                        f"{gbytes / ts / 1e9:.1f} GB/s")
+                sdma_legs = [("scatter_fsdp_splits_bf16_sdma", sdma_sets[0]),
+                             ("scatter_fsdp_splits_bf16_sdma_engines_only", engines_only[0])]
             else:
                 paths["param_contig_sdma"] = {"skipped": "no SDMA engines offered for device-local copies"}
             # the same splits in fp32 (4-byte elements: twice the bytes of the bf16 case)
@@ -500,8 +523,8 @@ def main():
                 log(f"[bench] {name}: {tx * 1e6:.1f} us/launch, {gbytes / tx / 1e9:.1f} GB/s")
             del shard_sets
             torch.cuda.empty_cache()
-            paths["contention"] = contention_leg(mr, torch, dev, stream, gsets, gbytes, sdma_sets)
-            del gsets, sdma_sets
+            paths["contention"] = contention_leg(mr, torch, dev, stream, gsets, gbytes, sdma_legs)
+            del gsets, sdma_legs
             torch.cuda.empty_cache()
             if not args.no_sweep:
                 paths["sweep_w8"] = sweep_leg(mr, torch, dev)

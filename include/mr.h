@@ -133,8 +133,11 @@ mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, co
  * GEMM keeps the compute units (page "ccl: hierarchical cross-node AllGather (intra-node SDMA +
  * inter-node RDMA) #441", PR summary: copy engines against CU contention).  Here every (parameter,
  * rank) piece -- src[r*T + O_s .. + splits[s]) to out[O_s*W + r*splits[s] ..) -- is one 1-D engine copy
- * (pieces above 4 MiB are cut), spread over every SDMA engine the device reports.  Output bits are
- * those of mr_allgather_param_contig.
+ * (pieces above 4 MiB are cut), spread over every SDMA engine the device reports.  An engine spends
+ * several microseconds on every copy whatever its size, so parameters whose pieces are smaller than
+ * MR_OPT_SDMA_CU_BELOW bytes are copied instead by one launch of the param-contiguous kernel on
+ * `stream`, which runs beside the engine copies (the same page later moves a copy step from the
+ * engines to a compute-unit kernel).  Output bits are those of mr_allgather_param_contig.
  *
  * Arguments, limits and errors as mr_allgather_param_contig, plus MR_ERR_ENGINE.  Unlike every other
  * entry point this call is synchronous: it waits until `stream` has finished its earlier work (the
@@ -292,12 +295,23 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  *   MR_TILE_WIDE_PAIR  one-shot: each workgroup reduces two wide tiles and stores both after the
  *                  second (W <= 8; wide for W > 8); two-shot under TILE or LAST: XCD-local units
  *                  at any size (W <= 8, 16-byte path), otherwise as MR_TILE_WIDE.
+ * MR_OPT_SDMA_CU_BELOW mr_allgather_param_contig_sdma: a parameter whose per-rank piece is smaller than
+ *                      this many bytes is copied by the compute-unit kernel, the others by the engines;
+ *                      0 puts every piece on the engines.  0 .. 2^32-1, default 1048576 (1 MiB).  The
+ *                      kernel part needs free compute units: beside a kernel that holds them all, the
+ *                      call returns only after that kernel has made room, so a caller that must not
+ *                      wait on other work sets 0.
  * Unknown options or out-of-range values -> MR_ERR_INVALID_ARG.  Environment variables
- * MR_TWOSHOT_SYNC, MR_SPIN_LIMIT and MR_TILE_SHAPE set the initial values when the library loads; a
- * value that is not a whole number in the option's range is ignored.  MR_TRACE=1 makes every launch
- * print its plan (path, shape, grid) to stderr.
+ * MR_TWOSHOT_SYNC, MR_SPIN_LIMIT, MR_TILE_SHAPE and MR_SDMA_CU_BELOW set the initial values when the
+ * library loads; a value that is not a whole number in the option's range is ignored.  MR_TRACE=1 makes
+ * every launch print its plan (path, shape, grid) to stderr.
  */
-typedef enum mr_option { MR_OPT_TWOSHOT_SYNC = 0, MR_OPT_SPIN_LIMIT = 1, MR_OPT_TILE_SHAPE = 2 } mr_option;
+typedef enum mr_option {
+  MR_OPT_TWOSHOT_SYNC = 0,
+  MR_OPT_SPIN_LIMIT = 1,
+  MR_OPT_TILE_SHAPE = 2,
+  MR_OPT_SDMA_CU_BELOW = 3
+} mr_option;
 #define MR_TWOSHOT_SYNC_TILE 0
 #define MR_TWOSHOT_SYNC_CHUNK 1
 #define MR_TWOSHOT_SYNC_GRID 2
@@ -315,7 +329,8 @@ mr_status mr_get_option(mr_option opt, int64_t* value);
  * MR_TWOSHOT_SYNC_AUTO (the new default hand-off); 1.02 added MR_TILE_WIDE_PAIR; 1.03 added
  * mr_allgather_param_contig_sdma, mr_sdma_engines and MR_ERR_ENGINE; 1.04 added
  * mr_allreduce_sum_noalloc and the last-arriver hand-off on XCD-local units (the default up to 32 MiB
- * per rank buffer). */
+ * per rank buffer); 1.05 added MR_OPT_SDMA_CU_BELOW (small parameters of the SDMA gather on the
+ * compute units). */
 int mr_version(void);
 
 #ifdef __cplusplus

@@ -19,7 +19,7 @@ int main(void) {
   uint64_t splits[3] = {8, 16, 24};
   int64_t v = -1;
   mr_stream stream = NULL;
-  CHECK(mr_version() == 104);
+  CHECK(mr_version() == 105);
   CHECK(strncmp(mr_status_string(MR_ERR_ALIAS), "MR_ERR_ALIAS", 12) == 0);
   CHECK(mr_allreduce_sum(bufs, 0, 16, MR_BF16, (void*)0x900000, MR_ONESHOT, stream) == MR_ERR_INVALID_ARG);
   CHECK(mr_allreduce_sum(bufs, 2, 16, MR_INT32, (void*)0x900000, MR_ONESHOT, stream) == MR_ERR_DTYPE);
@@ -42,6 +42,8 @@ int main(void) {
   CHECK(mr_workspace_bytes(8, 1 << 20, MR_BF16) > (2u << 20));
   CHECK(mr_get_option(MR_OPT_TWOSHOT_SYNC, &v) == MR_OK && v == MR_TWOSHOT_SYNC_AUTO);
   CHECK(mr_set_option(MR_OPT_TWOSHOT_SYNC, 7) == MR_ERR_INVALID_ARG);
+  CHECK(mr_get_option(MR_OPT_SDMA_CU_BELOW, &v) == MR_OK && v == 1048576);
+  CHECK(mr_set_option(MR_OPT_SDMA_CU_BELOW, -1) == MR_ERR_INVALID_ARG);
   CHECK(mr_last_hip_error() == 0);
   printf("c abi ok\n");
   return 0;

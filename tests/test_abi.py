@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mr_version() == 104
+    assert L.mr_version() == 105
     for code, name in mr.STATUS.items():
         assert L.mr_status_string(code).decode().startswith(name)
     assert b"unknown" in L.mr_status_string(-99)
@@ -181,27 +181,34 @@ def test_options_validate_and_round_trip(L):
     for shape in ("wide", "medium", "narrow", "wide_pair", "auto"):
         mr.set_option("tile_shape", shape)
         assert mr.get_option("tile_shape") == shape
+    assert L.mr_get_option(3, ctypes.byref(v)) == OK and v.value == 1 << 20  # SDMA gather: small pieces on CUs
+    assert L.mr_set_option(3, -1) == EINVAL and L.mr_set_option(3, 2 ** 32) == EINVAL
+    for b in (0, 2 ** 32 - 1, 1 << 20):
+        mr.set_option("sdma_cu_below", b)
+        assert mr.get_option("sdma_cu_below") == b
 
 
 def test_environment_sets_initial_options(tmp_path):
-    """MR_TWOSHOT_SYNC, MR_SPIN_LIMIT and MR_TILE_SHAPE give the options' values when the library loads
-    (in a fresh process; malformed values fall back to the defaults)."""
+    """MR_TWOSHOT_SYNC, MR_SPIN_LIMIT, MR_TILE_SHAPE and MR_SDMA_CU_BELOW give the options' values when the
+    library loads (in a fresh process; malformed values fall back to the defaults)."""
     import subprocess
     import sys
     code = ("import sys; sys.path.insert(0, %r); import all_gather_amd as mr; "
-            "print(mr.get_option('twoshot_sync'), mr.get_option('spin_limit'), mr.get_option('tile_shape'))"
+            "print(mr.get_option('twoshot_sync'), mr.get_option('spin_limit'), mr.get_option('tile_shape'), "
+            "mr.get_option('sdma_cu_below'))"
             % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
-    env = dict(os.environ, MR_TWOSHOT_SYNC="2", MR_SPIN_LIMIT="77", MR_TILE_SHAPE="3")
+    env = dict(os.environ, MR_TWOSHOT_SYNC="2", MR_SPIN_LIMIT="77", MR_TILE_SHAPE="3", MR_SDMA_CU_BELOW="0")
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.split() == ["grid", "77", "narrow"]
-    for bad in (dict(MR_TWOSHOT_SYNC="x", MR_SPIN_LIMIT="", MR_TILE_SHAPE="3z"),
-                dict(MR_TWOSHOT_SYNC="9", MR_SPIN_LIMIT="-1", MR_TILE_SHAPE="5"),
-                dict(MR_TWOSHOT_SYNC="-2", MR_SPIN_LIMIT="4294967296", MR_TILE_SHAPE="0x10")):
+    assert out.stdout.split() == ["grid", "77", "narrow", "0"]
+    for bad in (dict(MR_TWOSHOT_SYNC="x", MR_SPIN_LIMIT="", MR_TILE_SHAPE="3z", MR_SDMA_CU_BELOW="1k"),
+                dict(MR_TWOSHOT_SYNC="9", MR_SPIN_LIMIT="-1", MR_TILE_SHAPE="5", MR_SDMA_CU_BELOW="-1"),
+                dict(MR_TWOSHOT_SYNC="-2", MR_SPIN_LIMIT="4294967296", MR_TILE_SHAPE="0x10",
+                     MR_SDMA_CU_BELOW="4294967296")):
         out = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, **bad), capture_output=True,
                              text=True, timeout=120)
         assert out.returncode == 0, out.stderr
-        assert out.stdout.split() == ["auto", str(1 << 22), "auto"], bad
+        assert out.stdout.split() == ["auto", str(1 << 22), "auto", str(1 << 20)], bad
 
 
 def test_binding_rejects_host_tensors():

@@ -136,10 +136,16 @@ def test_gathers_at_odd_byte_offsets(dtype):
         assert L.mr_allgather_param_contig(src.ptr, W, G, sp, len(splits), mr.DTYPE_CODE[dtype], out.ptr, _stream()) == 0
         torch.cuda.synchronize()
         assert np.array_equal(out.get(dtype), want), f"param_contig src+{so} out+{oo}"
-        out2 = ByteBuf(W * T * es, oo)
-        assert L.mr_allgather_param_contig_sdma(src.ptr, W, G, sp, len(splits), mr.DTYPE_CODE[dtype], out2.ptr,
-                                                _stream()) == 0
-        assert np.array_equal(out2.get(dtype), want), f"sdma src+{so} out+{oo}"
+        prev = mr.get_option("sdma_cu_below")
+        for cu_below in (0, 256 << 10):  # every piece on the engines; the smaller parameters on the kernel
+            mr.set_option("sdma_cu_below", cu_below)
+            out2 = ByteBuf(W * T * es, oo)
+            try:
+                assert L.mr_allgather_param_contig_sdma(src.ptr, W, G, sp, len(splits), mr.DTYPE_CODE[dtype],
+                                                        out2.ptr, _stream()) == 0
+            finally:
+                mr.set_option("sdma_cu_below", prev)
+            assert np.array_equal(out2.get(dtype), want), f"sdma src+{so} out+{oo} cu_below={cu_below}"
     # from separate shards at odd offsets: param-contiguous, rank-major and list outputs
     shards_bits = [src_bits[r * T:(r + 1) * T] for r in range(W)]
     shards = []

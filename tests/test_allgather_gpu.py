@@ -198,9 +198,10 @@ def test_reused_plan_slot_keeps_no_stale_phase_bits():
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32", "int32"])
 def test_sdma_engines_match_the_oracle(dtype):
-    """mr_allgather_param_contig_sdma (copy engines, no compute units) gives the oracle's bits on the
-    FSDP-style splits, on ragged splits with empty and odd pieces, and with one parameter (a single
-    merged copy); the output is read back both by the host and by a kernel (torch compare) after it."""
+    """mr_allgather_param_contig_sdma gives the oracle's bits on the FSDP-style splits, on ragged splits with
+    empty and odd pieces, and with one parameter (a single merged copy), with every piece on the engines,
+    with the small parameters on the compute-unit kernel (below 8 KiB and 1 MiB pieces), and with every
+    parameter on the kernel; the output is read back both by the host and by a kernel (torch compare)."""
     n_eng = mr.sdma_engines()
     print(f"[case] SDMA engines: {n_eng}", flush=True)
     assert n_eng > 0, f"no SDMA engines offered for device-local copies (HSA status {mr.lib().mr_last_hip_error()})"
@@ -214,13 +215,20 @@ def test_sdma_engines_match_the_oracle(dtype):
         src_bits = workloads.gather_source(60 + len(splits), W, T, dtype)
         want = oracle.allgather_param_contig_ref(src_bits, W, G, splits)
         src = to_dev(src_bits, dtype)
-        out = torch.empty_like(src)
-        out.view(torch.uint8).fill_(0xA5)
-        torch.cuda.synchronize()
-        mr.allgather_param_contig_sdma(src, W, G, splits, out)
-        bad = np.flatnonzero(to_bits(out) != want)
-        assert bad.size == 0, f"sdma {name} {dtype}: {bad.size} mismatches, first at {bad[:8].tolist()}"
         ref = torch.empty_like(src)
         mr.allgather_param_contig(src, W, G, splits, ref)  # the kernel path, compared on the device
         it = torch.int16 if src.element_size() == 2 else torch.int32
-        assert torch.equal(out.view(it), ref.view(it)), f"sdma {name} {dtype}: differs from the kernel gather"
+        out = torch.empty_like(src)
+        prev = mr.get_option("sdma_cu_below")
+        try:
+            for cu_below in (0, 8192, 1 << 20, 2 ** 32 - 1):
+                print(f"[case] sdma {name} {dtype} cu_below={cu_below}", flush=True)
+                mr.set_option("sdma_cu_below", cu_below)
+                out.view(torch.uint8).fill_(0xA5)
+                torch.cuda.synchronize()
+                mr.allgather_param_contig_sdma(src, W, G, splits, out)
+                bad = np.flatnonzero(to_bits(out) != want)
+                assert bad.size == 0, f"sdma {name} {dtype} {cu_below}: {bad.size} mismatches, first at {bad[:8].tolist()}"
+                assert torch.equal(out.view(it), ref.view(it)), f"sdma {name} {dtype} {cu_below}: differs from the kernel"
+        finally:
+            mr.set_option("sdma_cu_below", prev)

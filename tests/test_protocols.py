@@ -133,6 +133,10 @@ def L():
                                            ctypes.POINTER(ctypes.c_uint16), ctypes.c_int]
     lib.mrx_needs_realign.restype = ctypes.c_int
     lib.mrx_needs_realign.argtypes = [ctypes.c_uint16, ctypes.c_uint64]
+    lib.mrx_gather_tiles.restype = ctypes.c_int
+    lib.mrx_gather_tiles.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_uint16)]
     return lib
 
 
@@ -300,3 +304,61 @@ def test_gather_phase_masks_match_brute_force(L):
         for d in range(16):  # base difference src - out, mod 16
             brute = any((dst - src_rm - d) % 16 != 0 for _, dst, src_rm, _ in _pieces(W, splits, es))
             assert L.mrx_needs_realign(rm.value, d) == int(brute), (trial, d)
+
+
+def _tile_param(prefix, P, t):
+    """The param-contiguous kernel's tile -> parameter search: the last s with prefix[s] <= t."""
+    lo, hi = 0, P
+    while hi - lo > 1:
+        mid = (lo + hi) >> 1
+        if prefix[mid] <= t:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def test_sdma_gather_kernel_part_covers_exactly_the_small_parameters(L):
+    """The SDMA gather's compute-unit part plans the whole split table but gives tiles only to parameters
+    whose per-rank piece is below the threshold.  Each such parameter keeps the tile count of the full
+    plan, every other parameter gets none, the kernel's tile search sends every tile to a kept parameter
+    and each kept parameter receives exactly its own tiles, and the phase mask covers the kept pieces
+    only (brute force)."""
+    rng = random.Random(33)
+    UMAX = 2 ** 64 - 1
+    for trial in range(300):
+        W = rng.choice([1, 2, 4, 6, 8, 16])
+        G = rng.choice([d for d in range(1, W + 1) if W % d == 0])
+        dt = rng.choice(["bf16", "fp16", "fp32", "int32"])
+        es = 2 if dt in ("bf16", "fp16") else 4
+        P = rng.randint(2, 128)
+        splits = [rng.choice([0, 1, 7, 8, 9, 1000, 4095, 4096, 4097, 20_000, 131_071, 131_072, 600_000])
+                  for _ in range(P)]
+        if sum(splits) == 0:
+            splits[-1] = 9
+        cu_below = rng.choice([0, 1, 2, 8192, 8190, 262_144, 262_142, 10 ** 6, UMAX])
+        sp = (ctypes.c_uint64 * P)(*splits)
+        full, cut = (ctypes.c_uint32 * (P + 1))(), (ctypes.c_uint32 * (P + 1))()
+        m_full, m_cut = ctypes.c_uint16(0), ctypes.c_uint16(0)
+        assert L.mrx_gather_tiles(W, G, sp, P, mr.DTYPE_CODE[dt], UMAX, full, P + 1, ctypes.byref(m_full)) == 0
+        assert L.mrx_gather_tiles(W, G, sp, P, mr.DTYPE_CODE[dt], cu_below, cut, P + 1, ctypes.byref(m_cut)) == 0
+        kept = [E * es < cu_below for E in splits]
+        for s_ in range(P):
+            n_full, n_cut = full[s_ + 1] - full[s_], cut[s_ + 1] - cut[s_]
+            assert n_cut == (n_full if kept[s_] else 0), (trial, s_, splits[s_], cu_below)
+        got = [0] * P
+        for t in range(cut[P]):
+            s_ = _tile_param(cut, P, t)
+            assert kept[s_] and cut[s_] <= t < cut[s_ + 1], (trial, t)
+            got[s_] += 1
+        assert got == [cut[i + 1] - cut[i] for i in range(P)]
+        want, O, T = 0, 0, sum(splits)
+        for s_, E in enumerate(splits):
+            if E and kept[s_]:
+                for r in range(min(W, 16)):  # the phase repeats with period 16 in the rank
+                    want |= 1 << (((O * W + r * E) - (r * T + O)) * es % 16)
+            O += E
+        assert m_cut.value == want, (trial, splits, cu_below)
+    tiny = (ctypes.c_uint32 * 2)()
+    m = ctypes.c_uint16(0)
+    assert L.mrx_gather_tiles(8, 4, (ctypes.c_uint64 * 1)(5), 1, 0, UMAX, tiny, 1, ctypes.byref(m)) == -1
