@@ -61,7 +61,7 @@ bool overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
   return na && nb && a < b + nb && b < a + na;
 }
 
-// Every device pointer of a call must be a multiple of the element size.
+// Is the pointer a multiple of the element size?  (Pointers that are not take the byte paths.)
 bool elem_aligned(const void* p, uint64_t es) { return reinterpret_cast<uintptr_t>(p) % es == 0; }
 
 // ------------------------------------------------------------------------------ workspace registry
