@@ -36,11 +36,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the reduce kernels' source with comments and blank space taken out,
-    so that a change to the code, not to its comments, marks the committed counters as stale."""
+def kernel_source_hash(paths=None) -> str:
+    """sha256 (first 16 hex digits) of the reduce kernels' source (or of `paths`) with comments and blank
+    space taken out, so that a change to the code, not to its comments, marks the committed counters as
+    stale."""
     h = hashlib.sha256()
-    for path in KERNEL_SRC:
+    for path in paths or KERNEL_SRC:
         with open(path, encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
