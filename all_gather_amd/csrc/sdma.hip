@@ -118,8 +118,14 @@ int engines_for(int dev, Engines** out) {
 
 }  // namespace
 
-// Copies larger than this are cut so that every engine gets a share of a large gather.
-constexpr uint64_t kSdmaChunk = uint64_t(4) << 20;
+// Copies larger than this are cut so that every engine gets a share of a large gather.  Same-GPU A/B
+// (alternating processes, W=8 G=4 P=64 FSDP-style splits with parameters under 1 MiB per rank on the
+// kernel / one 430 MB parameter), per call: cuts at 2 MiB 736-754 / 787-809 us, 4 MiB 682-698 / 771-775,
+// 8 MiB 664-685 / 752-759 (scheduling model below in each case).
+#ifndef MR_SDMA_CHUNK_MIB
+#define MR_SDMA_CHUNK_MIB 8
+#endif
+constexpr uint64_t kSdmaChunk = uint64_t(MR_SDMA_CHUNK_MIB) << 20;
 #ifndef MR_SDMA_LPT
 #define MR_SDMA_LPT 1
 #endif
@@ -127,14 +133,22 @@ constexpr uint64_t kSdmaChunk = uint64_t(4) << 20;
 #define MR_SDMA_QUIET 1
 #endif
 // Scheduling model of one engine: a copy costs its bytes at kEngineBytesPerUs plus kCopyUs (each
-// copy command costs an engine several microseconds beyond its bytes).  Copies are dealt longest first
-// to the engine that frees up first, and only each engine's last copy signals the waited signal (the
-// others a quiet one: no completion interrupt per copy).  Same-GPU A/B, W=8, G=4, P=64 bf16 (536 copies
-// on 14 engines), per call: bytes dealt round-robin by bytes, every copy on the waited signal 1335 us;
-// longest first 1196 us; quiet signals 1131 us; both 1080 us.  One 430 MB parameter (103 copies):
-// 792 -> 772 us.
-constexpr double kEngineBytesPerUs = 40000.0;
-constexpr double kCopyUs = 10.0;
+// copy command costs an engine about 15 us beyond its bytes: 448 copies of 2 KiB to 256 KiB over 14
+// engines took 15-17 us per copy per engine, and 4 MiB copies ran at about 51 GB/s past that).  Copies
+// are dealt longest first to the engine that frees up first, and only each engine's last copy signals
+// the waited signal (the others a quiet one: no completion interrupt per copy).  Same-GPU A/B, W=8, G=4,
+// P=64 bf16, every piece on the engines (536 copies on 14 engines), per call: bytes dealt round-robin by
+// bytes, every copy on the waited signal 1335 us; longest first 1196 us; quiet signals 1131 us; both
+// 1080 us.  One 430 MB parameter (103 copies): 792 -> 772 us.  The fitted model (51 GB/s, 15 us)
+// against the first guess (40 GB/s, 10 us), 8 MiB cuts: 664-685 against 668-685 us with the default split.
+#ifndef MR_SDMA_ENGINE_BYTES_PER_US
+#define MR_SDMA_ENGINE_BYTES_PER_US 51000.0
+#endif
+#ifndef MR_SDMA_COPY_US
+#define MR_SDMA_COPY_US 15.0
+#endif
+constexpr double kEngineBytesPerUs = MR_SDMA_ENGINE_BYTES_PER_US;
+constexpr double kCopyUs = MR_SDMA_COPY_US;
 
 // A signal that only the engines decrement and nobody waits on (no completion interrupt): the
 // completion signal of every copy but the last one on each engine.  One per device, kept for the

@@ -476,7 +476,7 @@ def main():
                 engines_only = [_with_option(mr, "sdma_cu_below", 0, c) for c in sdma_sets]
                 big = [E for E in splits if E * 2 >= cu_below]
                 split_note = (f"parameters with pieces of {cu_below} B and more on the engines "
-                              f"({c4['W'] * sum(-(-E * 2 // (4 << 20)) for E in big)} copies), the other "
+                              f"({c4['W'] * sum(-(-E * 2 // (8 << 20)) for E in big)} copies, cut at 8 MiB), the other "
                               f"{c4['P'] - len(big)} parameters ({c4['W'] * 2 * (T - sum(big))} B) on one "
                               f"compute-unit launch beside them")
                 Ks = 10

@@ -133,7 +133,7 @@ mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, co
  * GEMM keeps the compute units (page "ccl: hierarchical cross-node AllGather (intra-node SDMA +
  * inter-node RDMA) #441", PR summary: copy engines against CU contention).  Here every (parameter,
  * rank) piece -- src[r*T + O_s .. + splits[s]) to out[O_s*W + r*splits[s] ..) -- is one 1-D engine copy
- * (pieces above 4 MiB are cut), spread over every SDMA engine the device reports.  An engine spends
+ * (pieces above 8 MiB are cut), spread over every SDMA engine the device reports.  An engine spends
  * several microseconds on every copy whatever its size, so parameters whose pieces are smaller than
  * MR_OPT_SDMA_CU_BELOW bytes are copied instead by one launch of the param-contiguous kernel on
  * `stream`, which runs beside the engine copies (the same page later moves a copy step from the
