@@ -232,3 +232,33 @@ def test_sdma_engines_match_the_oracle(dtype):
                 assert torch.equal(out.view(it), ref.view(it)), f"sdma {name} {dtype} {cu_below}: differs from the kernel"
         finally:
             mr.set_option("sdma_cu_below", prev)
+
+
+def test_sdma_gather_waits_for_earlier_stream_work():
+    """The engines are not ordered by the stream, so the copy-engine gather waits for the stream's earlier
+    work before its copies start: here the source and the output are both written by kernels enqueued
+    just before the call, with no host synchronisation in between (FSDP-style splits, bf16, every piece
+    on the engines and the default split)."""
+    c = workloads.FSDP_SPLITS_W8_G4_P64
+    W, G = c["W"], c["G"]
+    splits = [int(x) for x in workloads.log_uniform_splits(c["seed"], c["P"])]
+    T = sum(splits)
+    src_bits = workloads.gather_source(77, W, T, "bf16")
+    want = oracle.allgather_param_contig_ref(src_bits, W, G, splits)
+    staged = to_dev(src_bits, "bf16")
+    src = torch.empty_like(staged)
+    out = torch.empty_like(staged)
+    prev = mr.get_option("sdma_cu_below")
+    try:
+        for cu_below in (0, prev):
+            print(f"[case] sdma after stream work cu_below={cu_below}", flush=True)
+            mr.set_option("sdma_cu_below", cu_below)
+            src.view(torch.int16).fill_(0)
+            torch.cuda.synchronize()
+            src.copy_(staged)                      # about 0.1 ms of kernel work, still running at the call
+            out.view(torch.int16).fill_(-1)        # a fill that must land before the copies, not after
+            mr.allgather_param_contig_sdma(src, W, G, splits, out)
+            bad = np.flatnonzero(to_bits(out) != want)
+            assert bad.size == 0, f"cu_below={cu_below}: {bad.size} mismatches, first at {bad[:8].tolist()}"
+    finally:
+        mr.set_option("sdma_cu_below", prev)
