@@ -1,7 +1,8 @@
 """Seeded random combinations of every argument the entry points take, each checked against the CPU
 oracle through the C ABI: for the sum-reduce W, n (tiny, ragged and multi-tile), dtype, mode, two-shot
 hand-off, tile shape and a per-pointer element offset (which mixes 16-byte phases); for the gathers W,
-G, P, split sizes (empty ones included), dtype, entry point and base offsets."""
+G, P, split sizes (empty ones included), dtype, entry point (the copy-engine gather with a random split
+between engines and kernel included) and base offsets."""
 import numpy as np
 import pytest
 import torch
@@ -60,17 +61,29 @@ def test_random_gather_cases(block):
         splits = [int(x) for x in rng.choice([0, 1, 3, 8, 100, 1023, 4096, 20_001], size=P)]
         T = sum(splits)
         dtype = str(rng.choice(["bf16", "fp16", "fp32", "int32"]))
-        entry = str(rng.choice(["rank_major", "shards", "into_tensor", "list"]))
+        entry = str(rng.choice(["rank_major", "shards", "into_tensor", "list", "sdma"]))
+        if entry == "sdma" and mr.sdma_engines() == 0:
+            entry = "rank_major"
+        cu_below = int(rng.choice([0, 64, 8192, 1 << 20, 2 ** 32 - 1]))  # the SDMA gather's kernel part
         if entry in ("into_tensor", "list"):
             splits, P = [T], 1
         off = int(rng.integers(0, 5))
-        what = f"block {block} case {case}: {entry} W={W} G={G} P={P} T={T} {dtype} off={off}"
+        what = f"block {block} case {case}: {entry} W={W} G={G} P={P} T={T} {dtype} off={off}" + (
+            f" cu_below={cu_below}" if entry == "sdma" else "")
         print(f"[case] {what}", flush=True)
         src = workloads.gather_source(int(rng.integers(1 << 30)), W, T, dtype)
         shards = [src[r * T:(r + 1) * T] for r in range(W)]
         out = _view(np.zeros(W * T, dtype=src.dtype), dtype, off)
         if entry == "rank_major":
             mr.allgather_param_contig(_view(src, dtype, off), W, G, splits, out)
+            want = oracle.allgather_param_contig_ref(src, W, G, splits)
+        elif entry == "sdma":
+            prev = mr.get_option("sdma_cu_below")
+            mr.set_option("sdma_cu_below", cu_below)
+            try:
+                mr.allgather_param_contig_sdma(_view(src, dtype, off), W, G, splits, out)
+            finally:
+                mr.set_option("sdma_cu_below", prev)
             want = oracle.allgather_param_contig_ref(src, W, G, splits)
         elif entry == "shards":
             mr.allgather_param_contig_shards([_view(x, dtype, off + r % 3) for r, x in enumerate(shards)], G,
