@@ -9,7 +9,9 @@
  *
  * Semantics shared by every entry point:
  *  - Work is enqueued asynchronously on `stream`; no call synchronises the host except
- *    mr_workspace_check.  Kernel faults surface at the caller's next synchronisation (HIP convention).
+ *    mr_workspace_check, mr_set_workspace when it frees library-owned buffers, and the copy-engine
+ *    gather mr_allgather_param_contig_sdma (see there).  Kernel faults surface at the caller's next
+ *    synchronisation (HIP convention).
  *  - Arguments are validated before any HIP call; an invalid call enqueues nothing.
  *  - The caller owns every buffer it passes and keeps it alive until the stream work completes (with
  *    a caching allocator and side streams, record the buffer on the stream).  The library never frees
@@ -71,9 +73,9 @@ int mr_last_hip_error(void);
  *         address modulo 16 the kernels use aligned 16-byte loads and stores; when they are all
  *         multiples of the element size but their 16-byte phases differ, each input pack is realigned
  *         in registers from the two aligned packs it straddles (slightly slower: about 26 us instead
- *         of 25 us one-shot, 36 us instead of 32 us two-shot, for W=8 bf16 at 16 MiB); when some pointer is not a multiple of the element size, the call
- *         runs element by element with single-byte loads and stores only (much slower), never an
- *         unaligned multi-byte access.
+ *         of 25 us one-shot, 36 us instead of 32 us two-shot, for W=8 bf16 at 16 MiB); when some
+ *         pointer is not a multiple of the element size, the call runs element by element with
+ *         single-byte loads and stores only (much slower), never an unaligned multi-byte access.
  *  W      1 .. MR_MAX_W.
  *  n      elements per buffer; n == 0 is a successful no-op.
  *  dtype  MR_BF16, MR_FP16 or MR_FP32 (output has the same dtype); MR_INT32 -> MR_ERR_DTYPE.
@@ -134,14 +136,15 @@ mr_status mr_allgather_param_contig(const void* src_rank_major, int W, int G, co
  * inter-node RDMA) #441", PR summary: copy engines against CU contention).  Here every (parameter,
  * rank) piece -- src[r*T + O_s .. + splits[s]) to out[O_s*W + r*splits[s] ..) -- is one 1-D engine copy
  * (pieces above 8 MiB are cut), spread over every SDMA engine the device reports.  An engine spends
- * several microseconds on every copy whatever its size, so parameters whose pieces are smaller than
+ * about 15 microseconds on every copy beyond its bytes, so parameters whose pieces are smaller than
  * MR_OPT_SDMA_CU_BELOW bytes are copied instead by one launch of the param-contiguous kernel on
  * `stream`, which runs beside the engine copies (the same page later moves a copy step from the
  * engines to a compute-unit kernel).  Output bits are those of mr_allgather_param_contig.
  *
  * Arguments, limits and errors as mr_allgather_param_contig, plus MR_ERR_ENGINE.  Unlike every other
  * entry point this call is synchronous: it waits until `stream` has finished its earlier work (the
- * engines are not ordered by the stream), then copies, and returns once every copy is complete; work
+ * engines are not ordered by the stream), then copies (the kernel part, if any, enqueued on `stream`),
+ * and returns once every copy is complete, the kernel part's included; work
  * enqueued on any stream afterwards sees the result.  Not capturable in a HIP graph.  The first call
  * on a device initialises the HSA runtime and creates one HSA signal that the library keeps for that
  * device until the process ends.
