@@ -56,10 +56,11 @@ enum TileShape : uint32_t { kShapeAuto = 0, kShapeWide = 1, kShapeMedium = 2, kS
 // Auto choices, from graph-replayed sweeps at W=8 over 64 KiB .. 64 MiB per rank (bf16 and fp32):
 // the narrow one-shot tile halves the time of messages below 1 MiB against the wide one (3.0 vs
 // 5.4 us at 64 KiB), the medium one leads from 1 to 2-4 MiB, and the wide one from 4 MiB (fp32) or
-// 8 MiB (bf16) up.  For two-shot, 256-pack tiles lead below 2 MiB and 1024-pack tiles above.  Wide
-// tiles in pairs (one workgroup, results held until both are reduced) lead from 16 to 64 MiB per rank:
-// 512 pairs fill two workgroup slots per CU at 16 MiB, where 1024 single tiles leave a tail on the
-// 768 slots the wide kernel's registers allow.
+// 8 MiB (bf16) up.  For two-shot, 256-pack tiles lead below 2 MiB and 1024-pack tiles above.  From 16
+// to 64 MiB per rank (kShapeWidePair) the one-shot runs its wide tiles pipelined on a persistent grid
+// of resident workgroups, each storing one tile's results while the next tile's loads are in flight
+// (it first held pairs of tiles per workgroup, hence the name); one wide tile per workgroup leads again
+// from 128 MiB.
 inline uint32_t oneshot_shape(size_t npacks, int elem_size, uint32_t forced) {
   if (forced != kShapeAuto) return forced;
   const size_t wide_from = elem_size == 4 ? (size_t(1) << 18) : (size_t(1) << 19);

@@ -9,6 +9,8 @@
 // lane per rank buffer, all of a lane's loads issued before any arithmetic, large workgroups (fewer
 // groups to dispatch and drain), non-temporal hints because no byte is touched twice.  No LDS, no MFMA.
 
+#include <atomic>
+
 #include "mr_internal.h"
 
 namespace mr {
@@ -402,34 +404,70 @@ __global__ __launch_bounds__(B) void oneshot_vec(RankPtrs in, char* out, ReduceS
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
 
-// Wide tiles in pairs: workgroup g reduces wide tiles 2g and 2g+1 (consecutive packs), holds the
-// first tile's results in registers while the second one's loads are in flight, then stores both.
-// Same-GPU A/B at W=8 against one wide tile per workgroup, graph-replayed, best of three, on two GPUs:
-// bf16 16 MiB per rank 26.69 -> 25.96 and 26.38 -> 25.87 us, 24 MiB 39.16 -> 38.36, 32 MiB 51.36 ->
-// 50.28, 48 MiB 77.26 -> 75.79, 64 MiB 102.6 -> 100.6; fp32 16 MiB 25.98 -> 25.49, 64 MiB 102.2 ->
-// 100.4.  It loses at 8 MiB (14.08 -> 14.92: 256 pairs leave half the slots empty) and from 128 MiB
-// (203.4 -> 207.1: 170 VGPRs allow two waves per SIMD against the wide kernel's three), so the host
-// picks it from 16 to 64 MiB per rank.
+// One pack's sum over the W ranks: widened to fp32, added in rank order, narrowed (the arithmetic of
+// reduce_tile, for kernels that issue their loads apart from the sums).
+template <typename D, int W>
+__device__ __forceinline__ u32x4 sum_ranks(const u32x4 (&v)[W]) {
+  float acc[D::V];
+  D::widen(v[0], acc);
+#pragma unroll
+  for (int r = 1; r < W; ++r) {
+    float t[D::V];
+    D::widen(v[r], t);
+#pragma unroll
+    for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
+  }
+  return D::narrow(acc);
+}
+
+// Wide tiles, pipelined (W <= 8, 16 to 64 MiB per rank buffer): a persistent grid of as many
+// workgroups as are resident on the chip at once (161 VGPRs at W=8: three per CU); workgroup b walks
+// tiles b, b + grid, ...  For each tile it issues every load, then stores the previous tile's results
+// while those loads are in flight, then sums.  It replaced pairs of tiles per workgroup (first tile's
+// results held until the second was summed; 170 VGPRs, two per CU), which had beaten one tile per
+// workgroup by 2-3% from 16 to 64 MiB.  Same-GPU A/B against the pairs, alternating processes, best of
+// three, two GPUs: W=8 bf16 16 MiB per rank 24.89-24.92 -> 24.55-24.67 us and 24.94-25.08 -> 24.67-24.73,
+// 24 MiB 37.09-37.24 -> 36.33-36.38, 32 MiB 49.01-49.16 -> 48.04-48.28 and 48.95-49.09 -> 48.23-48.36,
+// 64 MiB 99.4-100.0 -> 98.7-99.2 and 98.8-99.5 -> 99.4-99.7; fp32 16 MiB 24.75-24.81 -> 24.61-24.68;
+// W=4 bf16 16 MiB 15.16-15.21 -> 15.06-15.07.  With 640 workgroups (not every slot filled) it lost 5%,
+// with XCD-contiguous tiles it lost at 24 MiB and beyond, and at 256 MiB it lost to one tile per
+// workgroup (411 -> 419 us).
 template <typename D, int W, int B, int U>
-__global__ __launch_bounds__(B) void oneshot_pair(RankPtrs in, char* out, ReduceShape sh, size_t npairs, int xcd) {
+__global__ __launch_bounds__(B) void oneshot_pipe(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
   const size_t hb = sh.head * D::kSize;
   u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
-  for (size_t b = blockIdx.x; b < npairs; b += gridDim.x) {
-    const size_t g = xcd ? xcd_tile(b, npairs) : b;
-    u32x4 res[2][U];
+  u32x4 res[U];
+  size_t prev = ~size_t(0);  // first pack of the tile whose results res holds
+  for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const size_t first = t * (B * U);
+    u32x4 v[U][W];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      reduce_tile<D, W, B, U>(in, hb, (2 * g + h) * (B * U), sh.npacks,
-                              [&](int u, size_t, const u32x4& o) { res[h][u] = o; });
-      __asm__ volatile("" ::: "memory");  // compiler barrier between the two tiles (the measured build)
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int r = 0; r < W; ++r)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const size_t i = wc_pack<B, U>((2 * g + h) * (B * U), u);
-        if (i < sh.npacks) __builtin_nontemporal_store(res[h][u], dst + i);
+        const size_t i = wc_pack<B, U>(first, u);
+        if (i < sh.npacks) v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
       }
+    __asm__ volatile("" ::: "memory");  // the loads are issued before the stores below (the measured order)
+    if (prev != ~size_t(0)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t i = wc_pack<B, U>(prev, u);
+        if (i < sh.npacks) __builtin_nontemporal_store(res[u], dst + i);
+      }
+    }
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (wc_pack<B, U>(first, u) < sh.npacks) res[u] = sum_ranks<D, W>(v[u]);
+    prev = first;
+  }
+  if (prev != ~size_t(0)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = wc_pack<B, U>(prev, u);
+      if (i < sh.npacks) __builtin_nontemporal_store(res[u], dst + i);
+    }
   }
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
@@ -969,15 +1007,36 @@ hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& 
   return hipGetLastError();
 }
 
+// Workgroups of `kernel` (B lanes, no dynamic LDS) resident on the current device at once: its
+// occupancy per CU times the CUs, looked up once per device; 0 if the runtime cannot say.
+template <typename K>
+size_t resident_workgroups(K kernel, int B) {
+  constexpr int kDevices = 64;
+  static std::atomic<long long> cache[kDevices];  // 0: not looked up yet, -1: unknown
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kDevices) {
+    const long long c = cache[dev].load(std::memory_order_relaxed);
+    if (c) return c > 0 ? static_cast<size_t>(c) : 0;
+  }
+  int per_cu = 0, cus = 0;
+  long long n = -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, B, 0) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 && cus > 0)
+    n = static_cast<long long>(per_cu) * cus;
+  if (dev < kDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n > 0 ? static_cast<size_t>(n) : 0;
+}
+
 template <typename D, int W>
-hipError_t oneshot_pair_launch(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
+hipError_t oneshot_pipe_launch(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
   constexpr int B = kOneShotBlock, U = OneShotU<W>::value;
-  const size_t npairs = (sh.npacks + 2 * B * U - 1) / (2 * B * U);
-  size_t grid = npairs < kMaxGrid ? npairs : kMaxGrid;
+  const size_t ntiles = (sh.npacks + B * U - 1) / (B * U);
+  const size_t resident = resident_workgroups(oneshot_pipe<D, W, B, U>, B);
+  size_t grid = resident && resident < ntiles ? resident : ntiles;
+  if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid == 0) grid = 1;  // edges only
-  const int xcd = grid == npairs && npairs <= 512 ? 1 : 0;  // XCD-contiguous order as for small wide grids
-  hipLaunchKernelGGL((oneshot_pair<D, W, B, U>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh,
-                     npairs, xcd);
+  hipLaunchKernelGGL((oneshot_pipe<D, W, B, U>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh, ntiles);
   return hipGetLastError();
 }
 
@@ -996,7 +1055,7 @@ hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, uint3
   if (sh.vec && sh.realign) return oneshot_vec_launch<D, W, kOneShotBlock, RealignU<W>::value, true>(in, out, sh, st);
   if (sh.vec) {
     if constexpr (W <= 8) {
-      if (shape == kShapeWidePair) return oneshot_pair_launch<D, W>(in, out, sh, st);
+      if (shape == kShapeWidePair) return oneshot_pipe_launch<D, W>(in, out, sh, st);
     }
     switch (shape) {
       case kShapeNarrow: return oneshot_vec_launch<D, W, 64, 1>(in, out, sh, st);

@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0  # MI355X HBM3E, 8.0e12 B/s
-PROFILE_PMC = os.path.join(ROOT, "profiles", "oneshot_pair_bf16_w8_16MiB_pmc.txt")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "oneshot_pipe_bf16_w8_16MiB_pmc.txt")
 # the reduce kernels and the header that picks their launch shapes
 KERNEL_SRC = (os.path.join(ROOT, "all_gather_amd", "csrc", "reduce_kernels.hip"),
               os.path.join(ROOT, "all_gather_amd", "csrc", "mr_internal.h"))
@@ -581,7 +581,7 @@ def main():
         "verified_vs_oracle": verified,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "oneshot_pair<Bf16, 8>", "bytes_per_launch": algo,
+                     "kernel": "oneshot_pipe<Bf16, 8>", "bytes_per_launch": algo,
                      "avg_launch_us": round(t_launch * 1e6, 3), "traffic_source": traffic_src,
                      "traffic_GBps": round(traffic / t_launch / 1e9, 1) if traffic else None,
                      "stream_mix_ceiling_GBps": round(mix_gbs, 1),

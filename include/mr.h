@@ -288,16 +288,17 @@ mr_status mr_workspace_check(mr_stream stream, uint32_t* flags);
  *                      that is not already satisfied give up at once (for testing error handling).
  * MR_OPT_TILE_SHAPE    tile shape of the sum-reduce kernels (results are identical for every shape):
  *   MR_TILE_AUTO   (default) chosen from the message size and dtype: narrow below 64 Ki packs
- *                  of 16 B, medium below 256 Ki (fp32) or 512 Ki (16-bit types) packs, wide pair
- *                  from 1 Mi to 4 Mi packs (16 to 64 MiB per rank buffer) when W <= 8, wide
- *                  otherwise; two-shot: 64-pack tiles below 8 Ki packs, 256 below 128 Ki, 1024 above;
+ *                  of 16 B, medium below 256 Ki (fp32) or 512 Ki (16-bit types) packs,
+ *                  MR_TILE_WIDE_PAIR from 1 Mi to 4 Mi packs (16 to 64 MiB per rank buffer) when
+ *                  W <= 8, wide otherwise; two-shot: 64-pack tiles below 8 Ki packs, 256 below 128 Ki, 1024 above;
  *   MR_TILE_WIDE   one-shot 256 lanes x 4 packs of 16 B (256 x 1 for W > 8), two-shot phase-1
  *                  tiles of 1024 packs;
  *   MR_TILE_MEDIUM one-shot 256 x 1, two-shot 256-pack tiles;
  *   MR_TILE_NARROW one-shot 64 x 1, two-shot 64-pack tiles;
- *   MR_TILE_WIDE_PAIR  one-shot: each workgroup reduces two wide tiles and stores both after the
- *                  second (W <= 8; wide for W > 8); two-shot under TILE or LAST: XCD-local units
- *                  at any size (W <= 8, 16-byte path), otherwise as MR_TILE_WIDE.
+ *   MR_TILE_WIDE_PAIR  one-shot: wide tiles pipelined on a persistent grid of resident workgroups,
+ *                  each storing one tile's sums while the next tile's loads are in flight (W <= 8;
+ *                  wide for W > 8); two-shot under TILE or LAST: XCD-local units at any size
+ *                  (W <= 8, 16-byte path), otherwise as MR_TILE_WIDE.
  * MR_OPT_SDMA_CU_BELOW mr_allgather_param_contig_sdma: a parameter whose per-rank piece is smaller than
  *                      this many bytes is copied by the compute-unit kernel, the others by the engines;
  *                      0 puts every piece on the engines.  0 .. 2^32-1, default 1048576 (1 MiB).  The

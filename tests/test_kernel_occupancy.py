@@ -77,8 +77,8 @@ def test_register_use_keeps_the_tuned_occupancy(tmp_path):
         elif wm and int(wm.group(1)) <= 8 and "oneshot_vec" in name and name.endswith(
                 tuple(["Li256ELi4ELb0EEEvNS_8RankPtrsEPcNS_11ReduceShapeEmi"])):
             want = 3  # the wide one-shot tile keeps 4 packs x W ranks in flight per lane (tuned that way)
-        elif wm and int(wm.group(1)) <= 8 and "oneshot_pair" in name:
-            want = 2  # two wide tiles per workgroup, the first one's results held (measured at 2 per SIMD)
+        elif wm and int(wm.group(1)) <= 8 and "oneshot_pipe" in name:
+            want = 3  # pipelined wide tiles: three resident workgroups per CU at W=8 (measured that way)
         elif ("Lb1E" in name and ("oneshot_vec" in name or "twoshot_vec" in name)) or (
                 "twoshot_xcd" in name and "Lb1ELb1E" in name):
             want = 2  # realigned inputs (neighbour packs moved between lanes): no spills, 2+ waves (measured)
