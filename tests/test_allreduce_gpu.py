@@ -57,6 +57,16 @@ def test_w8_bf16_16MiB_normal():
     _check_modes(workloads.rank_buffers(c["seed"], c["W"], c["n"], c["dtype"], c["dist"]), "bf16", "W=8 bf16 16 MiB")
 
 
+@pytest.mark.parametrize("W,n,dtype", [(8, 8_388_608 + 4_099, "bf16"), (5, 4_194_304 + 77, "fp32"),
+                                       (8, 33_554_432 - 13, "fp16")])
+def test_pipelined_oneshot_ragged(W, n, dtype):
+    """Sizes in the pipelined one-shot's range (1 to 4 Mi packs of 16 bytes) with more tiles than resident
+    workgroups, so workgroups walk several tiles and hold one tile's sums while the next loads, with a
+    partial last tile and an element tail; every element against the oracle, both modes."""
+    bufs = workloads.rank_buffers(200 + W, W, n, dtype, "uniform")
+    _check_modes(bufs, dtype, f"pipelined range {dtype} W={W} n={n}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("W", [1, 2, 3, 5, 8, 11, 16])
 def test_dtypes_W_and_ragged_sizes(dtype, W):
