@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -245,5 +246,26 @@ int sdma_engine_count(int* status);  // status: the hsa_status_t of finding the 
 // realign: some span's source and destination differ in 16-byte phase (selects the kernel build)
 hipError_t launch_param_contig(const GatherArgs& a, bool realign, hipStream_t st);
 uint64_t gather_tiles_per_segment(uint64_t E, uint32_t elem);
+
+// Workgroups of `kernel` (B lanes, no dynamic LDS) resident on the current device at once: its
+// occupancy per CU times the CUs, looked up once per device; 0 if the runtime cannot say.
+template <typename K>
+size_t resident_workgroups(K kernel, int B) {
+  constexpr int kDevices = 64;
+  static std::atomic<long long> cache[kDevices];  // 0: not looked up yet, -1: unknown
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kDevices) {
+    const long long c = cache[dev].load(std::memory_order_relaxed);
+    if (c) return c > 0 ? static_cast<size_t>(c) : 0;
+  }
+  int per_cu = 0, cus = 0;
+  long long n = -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, B, 0) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 && cus > 0)
+    n = static_cast<long long>(per_cu) * cus;
+  if (dev < kDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n > 0 ? static_cast<size_t>(n) : 0;
+}
 
 }  // namespace mr

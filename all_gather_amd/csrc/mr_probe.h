@@ -22,15 +22,18 @@ extern "C" {
  * access pattern and none of its arithmetic.
  *
  * reads   host array of K device pointers (1 <= K <= 8), each to `bytes` bytes, 16-byte aligned.
- * out     device pointer to `bytes` bytes, 16-byte aligned.  With write != 0 every 16-byte word of
+ * out     device pointer to `bytes` bytes, 16-byte aligned.  With write 1 or 2 every 16-byte word of
  *         out receives the XOR of the K words at the same offset; with write == 0 the kernel loads
  *         the K streams and stores a word only where the XOR equals one fixed 64-bit pattern (so the
  *         loads cannot be dropped), which leaves out unspecified but within its bytes.
  * bytes   a multiple of 16; 0 is a no-op.
- * Lane layout: 256-lane workgroups, each lane four 16-byte words per stream (1024 words per
- * workgroup, wave-contiguous), every load of a lane in flight before the XOR, non-temporal loads and
- * stores -- the wide one-shot tile.  Returns 0 (hipSuccess), the hipError_t of a failed launch, or -1
- * for invalid arguments (nothing is enqueued then).
+ * write   0: reads only; 1: reads and the write, one tile per workgroup; 2: reads and the write on
+ *         the pipelined one-shot's schedule (a persistent grid of resident workgroups, each issuing a
+ *         tile's loads before storing the previous tile's XOR).  Other values -> -1.
+ * Lane layout: 256-lane workgroups, each lane four 16-byte words per stream (1024 words per tile,
+ * wave-contiguous), every load of a lane in flight before the XOR, non-temporal loads and stores --
+ * the wide one-shot tile.  Returns 0 (hipSuccess), the hipError_t of a failed launch, or -1 for
+ * invalid arguments (nothing is enqueued then).
  */
 int mrx_stream_mix(const void* const* reads, int K, void* out, size_t bytes, int write, void* stream);
 

@@ -9,8 +9,6 @@
 // lane per rank buffer, all of a lane's loads issued before any arithmetic, large workgroups (fewer
 // groups to dispatch and drain), non-temporal hints because no byte is touched twice.  No LDS, no MFMA.
 
-#include <atomic>
-
 #include "mr_internal.h"
 
 namespace mr {
@@ -431,43 +429,45 @@ __device__ __forceinline__ u32x4 sum_ranks(const u32x4 (&v)[W]) {
 // 64 MiB 99.4-100.0 -> 98.7-99.2 and 98.8-99.5 -> 99.4-99.7; fp32 16 MiB 24.75-24.81 -> 24.61-24.68;
 // W=4 bf16 16 MiB 15.16-15.21 -> 15.06-15.07.  With 640 workgroups (not every slot filled) it lost 5%,
 // with XCD-contiguous tiles it lost at 24 MiB and beyond, and at 256 MiB it lost to one tile per
-// workgroup (411 -> 419 us).
+// workgroup (411 -> 419 us).  Full tiles without bounds checks (below) then gained 0.3-1.5%: W=8 bf16
+// 16 MiB 24.77-24.83 -> 24.55-24.57 us, 64 MiB 99.8-101.0 -> 98.3-99.5, W=4 bf16 16 MiB 15.09-15.14 ->
+// 14.86-14.90.
 template <typename D, int W, int B, int U>
 __global__ __launch_bounds__(B) void oneshot_pipe(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
   const size_t hb = sh.head * D::kSize;
   u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
+  const size_t nfull = sh.npacks / (B * U);  // tiles wholly inside the packs
   u32x4 res[U];
-  size_t prev = ~size_t(0);  // first pack of the tile whose results res holds
-  for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  size_t prev = ~size_t(0);  // first pack of the tile whose sums res holds
+  size_t t = blockIdx.x;
+  // Full tiles need no per-lane bounds checks, so the loop is straight-line code: the compiler then
+  // waits for each rank's packs in turn (the sums start while later ranks' loads are in flight) and
+  // never for the previous tile's stores.  With the checks it waited for everything before summing.
+  for (; t < nfull; t += gridDim.x) {
     const size_t first = t * (B * U);
     u32x4 v[U][W];
 #pragma unroll
     for (int r = 0; r < W; ++r)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const size_t i = wc_pack<B, U>(first, u);
-        if (i < sh.npacks) v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + i);
-      }
+      for (int u = 0; u < U; ++u)
+        v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + wc_pack<B, U>(first, u));
     __asm__ volatile("" ::: "memory");  // the loads are issued before the stores below (the measured order)
     if (prev != ~size_t(0)) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const size_t i = wc_pack<B, U>(prev, u);
-        if (i < sh.npacks) __builtin_nontemporal_store(res[u], dst + i);
-      }
+      for (int u = 0; u < U; ++u) __builtin_nontemporal_store(res[u], dst + wc_pack<B, U>(prev, u));
     }
     __asm__ volatile("" ::: "memory");
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (wc_pack<B, U>(first, u) < sh.npacks) res[u] = sum_ranks<D, W>(v[u]);
+    for (int u = 0; u < U; ++u) res[u] = sum_ranks<D, W>(v[u]);
     prev = first;
   }
   if (prev != ~size_t(0)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t i = wc_pack<B, U>(prev, u);
-      if (i < sh.npacks) __builtin_nontemporal_store(res[u], dst + i);
-    }
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(res[u], dst + wc_pack<B, U>(prev, u));
+  }
+  if (t < ntiles) {  // the partial last tile (t == nfull), on the checked path
+    auto st = [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); };
+    reduce_tile<D, W, B, U, decltype(st)>(in, hb, t * (B * U), sh.npacks, st);
   }
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
 }
@@ -1005,27 +1005,6 @@ hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& 
   hipLaunchKernelGGL((oneshot_vec<D, W, B, U, RA>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh,
                      ntiles, xcd);
   return hipGetLastError();
-}
-
-// Workgroups of `kernel` (B lanes, no dynamic LDS) resident on the current device at once: its
-// occupancy per CU times the CUs, looked up once per device; 0 if the runtime cannot say.
-template <typename K>
-size_t resident_workgroups(K kernel, int B) {
-  constexpr int kDevices = 64;
-  static std::atomic<long long> cache[kDevices];  // 0: not looked up yet, -1: unknown
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < kDevices) {
-    const long long c = cache[dev].load(std::memory_order_relaxed);
-    if (c) return c > 0 ? static_cast<size_t>(c) : 0;
-  }
-  int per_cu = 0, cus = 0;
-  long long n = -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, B, 0) == hipSuccess &&
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 && cus > 0)
-    n = static_cast<long long>(per_cu) * cus;
-  if (dev < kDevices) cache[dev].store(n, std::memory_order_relaxed);
-  return n > 0 ? static_cast<size_t>(n) : 0;
 }
 
 template <typename D, int W>

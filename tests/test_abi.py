@@ -341,3 +341,19 @@ def test_any_alignment_is_accepted(L):
     # argument errors are still the documented ones
     assert L.mr_allreduce_sum(_ptrs(a + 1, None), 2, 64, 0, out, 0, None) == EINVAL
     assert L.mr_allreduce_sum(_ptrs(a + 1, b), 2, 64, 0, a + 3, 0, None) == EALIAS
+
+
+def test_stream_mix_probe_rejects_bad_arguments(L):
+    """The measurement probe (mr_probe.h, not mr.h) validates before it enqueues anything."""
+    f = L.mrx_stream_mix
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                  ctypes.c_void_p]
+    reads = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    assert f(reads, 0, 0x300000, 4096, 1, None) == -1        # K out of range
+    assert f(reads, 9, 0x300000, 4096, 1, None) == -1
+    assert f(reads, 2, 0x300000, 4000 + 8, 1, None) == -1    # not a multiple of 16 bytes
+    assert f(reads, 2, 0x300008, 4096, 1, None) == -1        # out not 16-byte aligned
+    for bad_mode in (-1, 3):
+        assert f(reads, 2, 0x300000, 4096, bad_mode, None) == -1
+    assert f(reads, 2, 0x300000, 0, 2, None) == 0            # empty: no-op

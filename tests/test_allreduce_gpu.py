@@ -515,3 +515,30 @@ def test_rank_buffers_beyond_2GiB():
     finally:
         del dbufs, out
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("write", [1, 2])
+def test_stream_mix_probe_writes_the_xor(write):
+    """The bench's ceiling probe computes what it claims (the XOR of its K streams) on both schedules,
+    with a ragged tail, so its rate is that of the full access pattern."""
+    import ctypes
+
+    L = mr.lib()
+    f = L.mrx_stream_mix
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                  ctypes.c_void_p]
+    nwords = 3 * 1024 * 1024 + 37  # more tiles than resident workgroups, and a partial last tile
+    g = torch.Generator(device=device())
+    g.manual_seed(write)
+    bufs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (4 * nwords,), dtype=torch.int32, device=device(), generator=g)
+            for _ in range(8)]
+    out = torch.full((4 * nwords,), -1, dtype=torch.int32, device=device())
+    ptrs = (ctypes.c_void_p * 8)(*[b.data_ptr() for b in bufs])
+    print(f"[case] stream_mix write={write} words={nwords}", flush=True)
+    assert f(ptrs, 8, out.data_ptr(), 16 * nwords, write, torch.cuda.current_stream().cuda_stream or None) == 0
+    want = bufs[0].clone()
+    for b in bufs[1:]:
+        want ^= b
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
