@@ -62,10 +62,11 @@ enum TileShape : uint32_t { kShapeAuto = 0, kShapeWide = 1, kShapeMedium = 2, kS
 // of resident workgroups, each storing one tile's results while the next tile's loads are in flight
 // (it first held pairs of tiles per workgroup, hence the name); one wide tile per workgroup leads again
 // from 128 MiB.
+constexpr size_t kPipeMaxPacks = size_t(1) << 22;  // largest one-shot on the pipelined wide tiles (64 MiB of bf16)
 inline uint32_t oneshot_shape(size_t npacks, int elem_size, uint32_t forced) {
   if (forced != kShapeAuto) return forced;
   const size_t wide_from = elem_size == 4 ? (size_t(1) << 18) : (size_t(1) << 19);
-  if (npacks >= (size_t(1) << 20) && npacks <= (size_t(1) << 22)) return kShapeWidePair;
+  if (npacks >= (size_t(1) << 20) && npacks <= kPipeMaxPacks) return kShapeWidePair;
   if (npacks >= wide_from) return kShapeWide;          // 256 lanes x 4 packs
   if (npacks >= (size_t(1) << 16)) return kShapeMedium;  // 256 lanes x 1 pack
   return kShapeNarrow;                                   // 64 lanes x 1 pack

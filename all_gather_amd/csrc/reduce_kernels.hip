@@ -297,7 +297,23 @@ __device__ __forceinline__ void reduce_tile_realigned(const RankPtrs& in, size_t
 
 // Reduce a wave-contiguous tile of B*P packs (i < end), PC packs at a time: all W*PC loads in flight,
 // rank by rank, before the adds; each result goes to st(u, i, pack).
-template <typename D, int W, int B, int P, typename Store, bool RA = false>
+// One pack's sum over the W ranks: widened to fp32, added in rank order, narrowed (the arithmetic of
+// reduce_tile, for kernels that issue their loads apart from the sums).
+template <typename D, int W>
+__device__ __forceinline__ u32x4 sum_ranks(const u32x4 (&v)[W]) {
+  float acc[D::V];
+  D::widen(v[0], acc);
+#pragma unroll
+  for (int r = 1; r < W; ++r) {
+    float t[D::V];
+    D::widen(v[r], t);
+#pragma unroll
+    for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
+  }
+  return D::narrow(acc);
+}
+
+template <typename D, int W, int B, int P, typename Store, bool RA = false, bool FULL = false>
 __device__ __forceinline__ void reduce_tile(const RankPtrs& in, size_t hb, size_t first, size_t end, Store st) {
   if constexpr (RA) {
     reduce_tile_realigned<D, W, B, P, Store>(in, hb, first, end, st);
@@ -305,6 +321,22 @@ __device__ __forceinline__ void reduce_tile(const RankPtrs& in, size_t hb, size_
   }
   constexpr int PC = (W <= 8 || P == 1) ? P : 2;  // wide W: fewer packs in flight per lane
   static_assert(P % PC == 0, "pack groups");
+  if (FULL && first + static_cast<size_t>(B) * P <= end) {
+    // A tile wholly inside the packs, without per-lane checks: straight-line code, so the compiler
+    // waits for each rank's packs in turn and the sums start while later loads are in flight.
+#pragma unroll
+    for (int u0 = 0; u0 < P; u0 += PC) {
+      u32x4 v[PC][W];
+#pragma unroll
+      for (int r = 0; r < W; ++r)
+#pragma unroll
+        for (int u = 0; u < PC; ++u)
+          v[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in.p[r] + hb) + wc_pack<B, P>(first, u0 + u));
+#pragma unroll
+      for (int u = 0; u < PC; ++u) st(u0 + u, wc_pack<B, P>(first, u0 + u), sum_ranks<D, W>(v[u]));
+    }
+    return;
+  }
 #pragma unroll
   for (int u0 = 0; u0 < P; u0 += PC) {
     u32x4 v[PC][W];
@@ -390,32 +422,16 @@ __device__ __forceinline__ size_t xcd_tile(size_t b, size_t ntiles) {
   return x * q + (x < rem ? x : rem) + b / kXcds;
 }
 
-template <typename D, int W, int B, int U, bool RA = false>
+template <typename D, int W, int B, int U, bool RA = false, bool FULL = false>
 __global__ __launch_bounds__(B) void oneshot_vec(RankPtrs in, char* out, ReduceShape sh, size_t ntiles, int xcd) {
   const size_t hb = sh.head * D::kSize;
   u32x4* dst = reinterpret_cast<u32x4*>(out + hb);
   auto store = [&](int, size_t i, const u32x4& o) { __builtin_nontemporal_store(o, dst + i); };
   for (size_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
     const size_t t = xcd ? xcd_tile(b, ntiles) : b;
-    reduce_tile<D, W, B, U, decltype(store), RA>(in, hb, t * (B * U), sh.npacks, store);
+    reduce_tile<D, W, B, U, decltype(store), RA, FULL>(in, hb, t * (B * U), sh.npacks, store);
   }
   if (blockIdx.x == 0) reduce_edges<D, W, false>(in, out, sh);
-}
-
-// One pack's sum over the W ranks: widened to fp32, added in rank order, narrowed (the arithmetic of
-// reduce_tile, for kernels that issue their loads apart from the sums).
-template <typename D, int W>
-__device__ __forceinline__ u32x4 sum_ranks(const u32x4 (&v)[W]) {
-  float acc[D::V];
-  D::widen(v[0], acc);
-#pragma unroll
-  for (int r = 1; r < W; ++r) {
-    float t[D::V];
-    D::widen(v[r], t);
-#pragma unroll
-    for (int k = 0; k < D::V; ++k) acc[k] = acc[k] + t[k];
-  }
-  return D::narrow(acc);
 }
 
 // Wide tiles, pipelined (W <= 8, 16 to 64 MiB per rank buffer): a persistent grid of as many
@@ -994,7 +1010,7 @@ __global__ void zero_words(uint32_t* p, size_t words) {
 
 constexpr size_t kMaxGrid = size_t(1) << 20;  // workgroups; beyond this the one-shot kernels grid-stride
 
-template <typename D, int W, int B, int U, bool RA = false>
+template <typename D, int W, int B, int U, bool RA = false, bool FULL = false>
 hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& sh, hipStream_t st) {
   constexpr size_t tile = static_cast<size_t>(B) * U;
   const size_t ntiles = (sh.npacks + tile - 1) / tile;
@@ -1002,8 +1018,8 @@ hipError_t oneshot_vec_launch(const RankPtrs& in, char* out, const ReduceShape& 
   if (grid == 0) grid = 1;  // edges only
   // XCD-contiguous tile order on small grids and on the wide tiles up to 1024 of them (see xcd_tile)
   const int xcd = grid == ntiles && (ntiles <= 512 || (tile == 1024 && ntiles <= 1024)) ? 1 : 0;
-  hipLaunchKernelGGL((oneshot_vec<D, W, B, U, RA>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out, sh,
-                     ntiles, xcd);
+  hipLaunchKernelGGL((oneshot_vec<D, W, B, U, RA, FULL>), dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, in, out,
+                     sh, ntiles, xcd);
   return hipGetLastError();
 }
 
@@ -1039,7 +1055,13 @@ hipError_t oneshot_w(const RankPtrs& in, char* out, const ReduceShape& sh, uint3
     switch (shape) {
       case kShapeNarrow: return oneshot_vec_launch<D, W, 64, 1>(in, out, sh, st);
       case kShapeMedium: return oneshot_vec_launch<D, W, 256, 1>(in, out, sh, st);
-      default: return oneshot_vec_launch<D, W, kOneShotBlock, OneShotU<W>::value>(in, out, sh, st);
+      default:
+        // beyond the pipelined kernel's range, full wide tiles on the unchecked path: same-GPU A/B, W=8
+        // bf16, 128 MiB per rank 202.3-202.6 -> 199.2-200.9 us, 256 MiB 413.0-413.8 -> 404.4-406.2 us;
+        // at 8 MiB it lost (13.7 -> 15.4 us), so smaller messages keep the checked path
+        if (sh.npacks > kPipeMaxPacks)
+          return oneshot_vec_launch<D, W, kOneShotBlock, OneShotU<W>::value, false, true>(in, out, sh, st);
+        return oneshot_vec_launch<D, W, kOneShotBlock, OneShotU<W>::value>(in, out, sh, st);
     }
   }
   const size_t need = (sh.n + kBlock - 1) / kBlock;

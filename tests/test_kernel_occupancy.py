@@ -75,7 +75,8 @@ def test_register_use_keeps_the_tuned_occupancy(tmp_path):
         if "param_contig" in name:
             want = 8
         elif wm and int(wm.group(1)) <= 8 and "oneshot_vec" in name and name.endswith(
-                tuple(["Li256ELi4ELb0EEEvNS_8RankPtrsEPcNS_11ReduceShapeEmi"])):
+                ("Li256ELi4ELb0ELb0EEEvNS_8RankPtrsEPcNS_11ReduceShapeEmi",
+                 "Li256ELi4ELb0ELb1EEEvNS_8RankPtrsEPcNS_11ReduceShapeEmi")):
             want = 3  # the wide one-shot tile keeps 4 packs x W ranks in flight per lane (tuned that way)
         elif wm and int(wm.group(1)) <= 8 and "oneshot_pipe" in name:
             want = 3  # pipelined wide tiles: three resident workgroups per CU at W=8 (measured that way)
