@@ -900,6 +900,24 @@ __global__ __launch_bounds__(B) void twoshot_xcd(RankPtrs in, char* out, char* s
   if (from_stage) {  // the common case: every unit from the stage, all loads in flight before the stores
     const i32x4 rs = make_rsrc(stage + hb + first * 16, static_cast<uint32_t>(UP * R * 16));
     u32x4 v[R * U];
+    if (s_mode[R - 1] == 1u && first + R * UP <= sh.npacks) {
+      // A whole group (every member present, inside the packs) without per-lane checks: straight-line
+      // code, so each store waits only for its own load.  Same-GPU A/B, W=8 bf16, last arriver: 1 MiB
+      // per rank 5.81 -> 5.19 us, 4 MiB 10.86 -> 9.87, 16 MiB 31.9 -> 31.3, 32 MiB 63.1 -> 62.0; fp32
+      // 16 MiB 31.6 -> 30.8.
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu)
+          v[r * U + uu] = __builtin_bit_cast(
+              u32x4, raw_buffer_load_v4(rs, static_cast<int>((wc_pack<B, U>(first + r * UP, uu) - first) * 16), 0,
+                                        kXcdStageLoadAux));
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) __builtin_nontemporal_store(v[r * U + uu], dst + wc_pack<B, U>(first + r * UP, uu));
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
