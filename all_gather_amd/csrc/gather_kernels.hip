@@ -54,6 +54,20 @@ __device__ __forceinline__ u32x4 realign(const u32x4& A, const u32x4& B) {
 // source occupies.
 template <int M>
 __device__ __forceinline__ void copy_realigned(const u32x4* sa, u32x4* d4, uint32_t nw) {
+  if (nw == kCopyU * kGB) {
+    // a whole tile: no per-lane checks (same-GPU A/B, three interleaved repeats, W=8 G=4 P=64
+    // log-uniform splits of any size: bf16 156.0-158.8 -> 146.7-148.0 us, fp32 294.4-294.7 -> 281.9-282.5 us)
+    u32x4 a[kCopyU], b[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const uint32_t i = u * kGB + threadIdx.x;
+      a[u] = __builtin_nontemporal_load(sa + i);
+      b[u] = sa[i + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) __builtin_nontemporal_store(realign<M>(a[u], b[u]), d4 + u * kGB + threadIdx.x);
+    return;
+  }
   for (uint32_t w0 = 0; w0 < nw; w0 += kCopyU * kGB) {
     u32x4 a[kCopyU], b[kCopyU];
 #pragma unroll
@@ -86,6 +100,18 @@ __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t l
     const uint32_t nw = body >> 4;
     const u32x4* s4 = reinterpret_cast<const u32x4*>(src + head);
     u32x4* d4 = reinterpret_cast<u32x4*>(dst + head);
+    if (nw == kCopyU * kGB && head == 0 && len == nw * 16u) {
+      // a whole aligned tile: straight-line loads and stores with no per-lane checks, so each store
+      // waits only for its own load (same-GPU A/B, three interleaved repeats, W=8 G=4 P=64
+      // log-uniform splits: bf16 142.2-143.2 -> 137.9-138.6 us, fp32 279.7-280.1 -> 276.7-277.1 us;
+      // 8 shards into one tensor 134.2-134.5 -> 131.9-132.2 us)
+      u32x4 v[kCopyU];
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u) v[u] = __builtin_nontemporal_load(s4 + u * kGB + threadIdx.x);
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u) __builtin_nontemporal_store(v[u], d4 + u * kGB + threadIdx.x);
+      return;
+    }
     for (uint32_t w0 = 0; w0 < nw; w0 += kCopyU * kGB) {
       u32x4 v[kCopyU];
 #pragma unroll

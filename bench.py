@@ -513,6 +513,24 @@ def main():
                 f"({fbytes / tf / 1e9 / PEAK_GBS:.1%} of peak)")
             del fsets
             torch.cuda.empty_cache()
+            # log-uniform splits of any element count (not rounded to 8): most pieces sit at a source
+            # 16-byte phase other than their destination's, so the realigning build runs
+            splits_any = [int(x) for x in workloads.log_uniform_splits(c4["seed"], c4["P"], mult=1)]
+            Ta = sum(splits_any)
+            asets = []
+            for k in range(2):
+                src = torch.randint(-32768, 32767, (c4["W"] * Ta,), dtype=torch.int16, device=dev).view(torch.bfloat16)
+                asets.append(mr.prepare_allgather_param_contig(src, c4["W"], c4["G"], splits_any, torch.empty_like(src)))
+            abytes = 2 * c4["W"] * Ta * 2
+            msa = time_steps(asets, Kg, max(2, args.warmup // 10), stream)
+            ta = msa / Kg * 1e-3
+            paths["param_contig_any_size"] = {"us": ta * 1e6, "GBps": abytes / ta / 1e9, "bytes": abytes, "W": c4["W"],
+                                              "G": c4["G"], "P": c4["P"], "T": Ta, "dtype": "bf16",
+                                              "unaligned_splits": sum(E % 8 != 0 for E in splits_any),
+                                              "frac": abytes / ta / 1e9 / PEAK_GBS}
+            log(f"[bench] param_contig any-size splits: {ta * 1e6:.1f} us/launch, {abytes / ta / 1e9:.1f} GB/s")
+            del asets
+            torch.cuda.empty_cache()
             # the same gathers written straight from W separate shard buffers
             shard_sets = []
             for k in range(2):

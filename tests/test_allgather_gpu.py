@@ -262,3 +262,14 @@ def test_sdma_gather_waits_for_earlier_stream_work():
             assert bad.size == 0, f"cu_below={cu_below}: {bad.size} mismatches, first at {bad[:8].tolist()}"
     finally:
         mr.set_option("sdma_cu_below", prev)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_fsdp_splits_of_any_size(dtype):
+    """The FSDP-style workload with split sizes not rounded to 8 elements: most pieces take the realigning
+    16-byte copy, in whole 16 KiB tiles and in partial ones, at the full size."""
+    c = workloads.FSDP_SPLITS_W8_G4_P64
+    splits = workloads.log_uniform_splits(c["seed"], c["P"], mult=1)
+    T = int(splits.sum())
+    src = workloads.gather_source(c["seed"] + 1, c["W"], T, dtype)
+    _check(src, c["W"], c["G"], splits, dtype, f"FSDP splits of any size W=8 G=4 P=64 {dtype} T={T}")
