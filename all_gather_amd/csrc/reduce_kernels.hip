@@ -1058,6 +1058,10 @@ hipError_t oneshot_pipe_launch(const RankPtrs& in, char* out, const ReduceShape&
 // 234 VGPRs, two waves per SIMD).  Same-GPU A/B, W=8, 16 MiB per rank, inputs at alternating phases:
 // two packs per lane with both aligned packs loaded 30.3 us (bf16); two packs per lane, neighbour moves
 // 27.4; four packs per lane, neighbour moves 26.2 (the aligned wide one-shot: 25.6).  One pack for W > 8.
+// The aligned one-shot's pipelined persistent schedule does not carry over: a resident grid storing one
+// realigned tile's sums while the next tile loads ran slower at both widths (same GPU, three interleaved
+// repeats, W=8, odd ranks one element off: bf16 16 MiB 26.9-27.3 -> 28.5-28.6 us with four packs per
+// lane, 224 VGPRs, and 28.6-29.0 us with two, 160 VGPRs; bf16 63 MiB 96.6-97.0 -> 100.5-100.9 us).
 #ifndef MR_RA_U
 #define MR_RA_U 4
 #endif

@@ -67,6 +67,23 @@ def test_pipelined_oneshot_ragged(W, n, dtype):
     _check_modes(bufs, dtype, f"pipelined range {dtype} W={W} n={n}")
 
 
+def test_pipelined_oneshot_every_W():
+    """The pipelined one-shot is a separate build for every W up to 8: each runs just under 4 Mi packs
+    (the top of its range, several tiles per resident workgroup at any occupancy) with a ragged element
+    tail, one-shot only, every element against the oracle."""
+    for W in range(1, 9):
+        dtype = ("fp32", "bf16", "fp16")[W % 3]
+        V = 4 if dtype == "fp32" else 8
+        n = (4 << 20) * V - (V * W + 3)
+        bufs = workloads.rank_buffers(700 + W, W, n, dtype, "uniform")
+        want = oracle.allreduce_sum_ref(bufs, dtype)
+        print(f"[case] pipelined one-shot W={W} {dtype} n={n}", flush=True)
+        got = to_bits(_run([to_dev(b, dtype) for b in bufs], dtype, n, "oneshot"))
+        assert_reduce_equal(got, want, dtype, f"pipelined one-shot W={W} {dtype} n={n}")
+        del bufs, want, got
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("W", [1, 2, 3, 5, 8, 11, 16])
 def test_dtypes_W_and_ragged_sizes(dtype, W):
