@@ -93,7 +93,9 @@ template <int S, bool RA>
 __device__ __forceinline__ void copy_span(const char* src, char* dst, uint32_t len) {
   const uintptr_t ps = reinterpret_cast<uintptr_t>(src), pd = reinterpret_cast<uintptr_t>(dst);
   if (((ps ^ pd) & 15u) == 0) {
-    // same 16-byte phase: element-wise head up to 16-byte alignment, 16-byte body, element-wise tail
+    // same 16-byte phase: element-wise head up to 16-byte alignment, 16-byte body, element-wise tail.
+    // Loads and stores are non-temporal: plain loads cost 6% and plain stores 5% (same-GPU A/B, W=8 G=4
+    // P=64 bf16 splits: 138.7 us against 147.0-147.4 and 145.0-145.3 us)
     uint32_t head = static_cast<uint32_t>((16u - (ps & 15u)) & 15u);
     if (head > len) head = len;
     const uint32_t body = (len - head) & ~15u;
