@@ -72,8 +72,8 @@ int mr_last_hip_error(void);
  *         Pointers may repeat.  Any alignment is accepted.  When every pointer and out have the same
  *         address modulo 16 the kernels use aligned 16-byte loads and stores; when they are all
  *         multiples of the element size but their 16-byte phases differ, each input pack is realigned
- *         in registers from the two aligned packs it straddles (slightly slower: about 26 us instead
- *         of 25 us one-shot, 36 us instead of 32 us two-shot, for W=8 bf16 at 16 MiB); when some
+ *         in registers from the two aligned packs it straddles (slightly slower: about 26.4 us
+ *         instead of 24.5 us one-shot, 35 us instead of 31.5 us two-shot, for W=8 bf16 at 16 MiB); when some
  *         pointer is not a multiple of the element size, the call runs element by element with
  *         single-byte loads and stores only (much slower), never an unaligned multi-byte access.
  *  W      1 .. MR_MAX_W.
