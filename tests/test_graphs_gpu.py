@@ -167,3 +167,55 @@ def test_graphs_captured_on_one_stream_replay_together(mode):
         mr.set_workspace(None, cap)  # frees the capture workspaces of the stream
     finally:
         mr.set_option("twoshot_sync", "auto")
+
+
+_PIPE_CAPTURE_CHILD = r"""
+import torch
+import all_gather_amd as mr
+import oracle
+import workloads
+from gpu_util import assert_reduce_equal, to_bits, to_dev
+W, n = 8, 8_388_608 + 5
+dbufs = [torch.empty(n, dtype=torch.bfloat16, device="cuda:0") for _ in range(W)]
+out = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+torch.cuda.synchronize()
+s = torch.cuda.Stream()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g, stream=s):
+    mr.allreduce_sum(dbufs, out, mode="oneshot")
+for rep in range(3):
+    bufs = workloads.rank_buffers(140 + rep, W, n, "bf16", "normal")
+    want = oracle.allreduce_sum_ref(bufs, "bf16")
+    for d, b in zip(dbufs, bufs):
+        d.copy_(to_dev(b, "bf16"))
+    out.fill_(0)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert_reduce_equal(to_bits(out), want, "bf16", f"replay {rep}")
+    out.fill_(0)
+    mr.allreduce_sum(dbufs, out, mode="oneshot")
+    torch.cuda.synchronize()
+    assert_reduce_equal(to_bits(out), want, "bf16", f"eager call after replay {rep}")
+print("replays ok", flush=True)
+"""
+
+
+def test_pipelined_oneshot_first_called_under_capture():
+    """A fresh process whose first pipelined one-shot (W=8 bf16, 16 MiB per rank) is made under HIP graph
+    capture, so the kernel's resident-grid lookup runs during the capture; the graph is replayed three
+    times with new inputs, an eager call after each, and every result is checked against the oracle.
+    The launch trace confirms the pipelined shape was chosen."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, MR_TRACE="1", PYTHONPATH=os.pathsep.join([root, os.path.join(root, "tests")]))
+    print("[case] pipelined one-shot first called under capture (child process, MR_TRACE=1)", flush=True)
+    r = subprocess.run([sys.executable, "-c", _PIPE_CAPTURE_CHILD], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-3000:]
+    assert "replays ok" in r.stdout
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[mr] allreduce oneshot")]
+    assert lines and all("shape=4" in ln for ln in lines), lines
