@@ -84,6 +84,14 @@ def test_pipelined_oneshot_every_W():
         torch.cuda.empty_cache()
 
 
+def test_w16_large_every_mode():
+    """W = 16, the largest rank count, at about 8 MiB per rank buffer: the one-shot's wide tiles of one
+    pack per lane (W > 8) over many tiles, and every two-shot hand-off on chunk tiles (the XCD-local
+    units are for W <= 8), with a ragged element tail."""
+    bufs = workloads.rank_buffers(716, 16, 4_194_304 + 13, "bf16", "normal")
+    _check_modes(bufs, "bf16", "W=16 bf16 n=4,194,317")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("W", [1, 2, 3, 5, 8, 11, 16])
 def test_dtypes_W_and_ragged_sizes(dtype, W):
