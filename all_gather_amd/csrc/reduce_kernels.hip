@@ -447,7 +447,8 @@ __global__ __launch_bounds__(B) void oneshot_vec(RankPtrs in, char* out, ReduceS
 // with XCD-contiguous tiles it lost at 24 MiB and beyond, and at 256 MiB it lost to one tile per
 // workgroup (411 -> 419 us).  Full tiles without bounds checks (below) then gained 0.3-1.5%: W=8 bf16
 // 16 MiB 24.77-24.83 -> 24.55-24.57 us, 64 MiB 99.8-101.0 -> 98.3-99.5, W=4 bf16 16 MiB 15.09-15.14 ->
-// 14.86-14.90.
+// 14.86-14.90.  XCD-contiguous tile runs on this unchecked kernel lost at 16 MiB too (24.49-24.54 ->
+// 25.71-25.93 us; 32 MiB 48.05-48.16 -> 50.75-51.12 us).
 template <typename D, int W, int B, int U>
 __global__ __launch_bounds__(B) void oneshot_pipe(RankPtrs in, char* out, ReduceShape sh, size_t ntiles) {
   const size_t hb = sh.head * D::kSize;
