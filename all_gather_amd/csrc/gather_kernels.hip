@@ -204,6 +204,36 @@ __device__ __forceinline__ void param_block_tile(const GatherArgs& a, uint32_t t
   const uint64_t b0 = b0r > lead ? b0r - lead : 0;
   const uint64_t b1r = b0r + kGatherTileBytes - lead;
   const uint64_t b1 = b1r < seg ? b1r : seg;
+  if constexpr (!RA) {
+    // A whole tile that crosses exactly one rank boundary, on a 16-byte pack boundary: each lane takes
+    // its pack from rank r0 or r0 + 1 with a select, in straight-line code, instead of two checked
+    // spans.  343 of the 26,303 tiles of the W=8 G=4 P=64 bf16 splits; same-GPU A/B, three interleaved
+    // repeats: 138.8-139.6 -> 137.3-137.4 us (fp32 277.4-278.8 -> 277.3-277.8 us).
+    if (b1 - b0 == kGatherTileBytes) {
+      const uint64_t r0 = b0 / ES;
+      const uint64_t xb = (r0 + 1) * ES;  // the first rank boundary after b0
+      if (xb < b1 && b1 - xb <= ES && ((xb - b0) & 15u) == 0) {
+        const char* s0 = (a.src_table ? a.src_tab[r0] + Os * S : a.src + (r0 * a.T + Os) * S) + (b0 - r0 * ES);
+        const char* s1 = a.src_table ? a.src_tab[r0 + 1] + Os * S : a.src + ((r0 + 1) * a.T + Os) * S;
+        char* d = pd + b0;
+        if (((reinterpret_cast<uintptr_t>(s0) | reinterpret_cast<uintptr_t>(s1) | reinterpret_cast<uintptr_t>(d)) & 15u) == 0) {
+          const uint32_t split = static_cast<uint32_t>((xb - b0) >> 4);  // packs taken from rank r0
+          const u32x4* q0 = reinterpret_cast<const u32x4*>(s0);
+          const u32x4* q1 = reinterpret_cast<const u32x4*>(s1);
+          u32x4* d4 = reinterpret_cast<u32x4*>(d);
+          u32x4 v[kCopyU];
+#pragma unroll
+          for (int u = 0; u < kCopyU; ++u) {
+            const uint32_t i = u * kGB + threadIdx.x;
+            v[u] = __builtin_nontemporal_load(i < split ? q0 + i : q1 + (i - split));
+          }
+#pragma unroll
+          for (int u = 0; u < kCopyU; ++u) __builtin_nontemporal_store(v[u], d4 + u * kGB + threadIdx.x);
+          return;
+        }
+      }
+    }
+  }
   for (uint64_t x = b0; x < b1;) {  // one piece per rank the tile touches (rank r = m*G + g)
     const uint64_t r = x / ES;
     const uint64_t xe = (r + 1) * ES < b1 ? (r + 1) * ES : b1;

@@ -273,3 +273,23 @@ def test_fsdp_splits_of_any_size(dtype):
     T = int(splits.sum())
     src = workloads.gather_source(c["seed"] + 1, c["W"], T, dtype)
     _check(src, c["W"], c["G"], splits, dtype, f"FSDP splits of any size W=8 G=4 P=64 {dtype} T={T}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_tiles_crossing_one_rank_boundary(dtype):
+    """Splits whose rank pieces are 16 to 40 KiB, all whole 16-byte packs, so many whole tiles cross one
+    rank boundary at many different pack offsets (the straight-line two-rank copy), beside tiles crossing
+    none or several; from a rank-major source and from separate shards, every element against the oracle."""
+    W, G = 8, 2
+    es = 2 if dtype == "bf16" else 4
+    splits = [(16384 + 16 * 37 * k) // es for k in range(40)]
+    T = sum(splits)
+    print(f"[case] two-rank tiles {dtype} T={T}", flush=True)
+    src = workloads.gather_source(430, W, T, dtype)
+    want = oracle.allgather_param_contig_ref(src, W, G, splits)
+    assert np.array_equal(_gather(src, W, G, splits, dtype), want)
+    shards = [src[r * T:(r + 1) * T] for r in range(W)]
+    out = torch.empty(W * T, dtype=TORCH_DT[dtype], device=device())
+    mr.allgather_param_contig_shards([to_dev(s, dtype) for s in shards], G, splits, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), want)
