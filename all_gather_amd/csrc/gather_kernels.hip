@@ -47,6 +47,11 @@ __device__ __forceinline__ u32x4 realign(const u32x4& A, const u32x4& B) {
   return o;
 }
 
+// wave_shl:1 (a DPP move across the 64-lane wave): lane l receives v of lane l + 1; lane 63 keeps `old`.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), 0x130, 0xf, 0xf, false));
+}
+
 // 16-byte stores to a 16-byte-aligned destination from a source M (1..15; a multiple of the element
 // size, so even unless the gather is planned in bytes) bytes past a 16-byte
 // boundary: each lane loads the two aligned source packs its output straddles and realigns them in
@@ -56,16 +61,26 @@ template <int M>
 __device__ __forceinline__ void copy_realigned(const u32x4* sa, u32x4* d4, uint32_t nw) {
   if (nw == kCopyU * kGB) {
     // a whole tile: no per-lane checks (same-GPU A/B, three interleaved repeats, W=8 G=4 P=64
-    // log-uniform splits of any size: bf16 156.0-158.8 -> 146.7-148.0 us, fp32 294.4-294.7 -> 281.9-282.5 us)
-    u32x4 a[kCopyU], b[kCopyU];
+    // log-uniform splits of any size: bf16 156.0-158.8 -> 146.7-148.0 us, fp32 294.4-294.7 -> 281.9-282.5 us).
+    // Pack i + 1 is the next lane's pack i, so only lane 63 of each wave loads it (it lies in the next
+    // wave's first lane); the others take it over with a DPP move: fp32 278.4-278.8 -> 276.9-277.3 us,
+    // 8 shards one element off 140.7-142.3 -> 139.8-140.6 us, bf16 144.8-146.0 -> 144.9-145.3 us.
+    const bool l63 = (threadIdx.x & 63) == 63;
+    u32x4 a[kCopyU], nx[kCopyU];
 #pragma unroll
     for (int u = 0; u < kCopyU; ++u) {
       const uint32_t i = u * kGB + threadIdx.x;
       a[u] = __builtin_nontemporal_load(sa + i);
-      b[u] = sa[i + 1];
+      nx[u] = u32x4{0u, 0u, 0u, 0u};
+      if (l63) nx[u] = sa[i + 1];
     }
 #pragma unroll
-    for (int u = 0; u < kCopyU; ++u) __builtin_nontemporal_store(realign<M>(a[u], b[u]), d4 + u * kGB + threadIdx.x);
+    for (int u = 0; u < kCopyU; ++u) {
+      u32x4 b;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) b[k] = from_next_lane(nx[u][k], a[u][k]);
+      __builtin_nontemporal_store(realign<M>(a[u], b), d4 + u * kGB + threadIdx.x);
+    }
     return;
   }
   for (uint32_t w0 = 0; w0 < nw; w0 += kCopyU * kGB) {
