@@ -84,6 +84,24 @@ def test_pipelined_oneshot_every_W():
         torch.cuda.empty_cache()
 
 
+def test_xcd_twoshot_wide_units_every_W():
+    """The XCD-local two-shot is a separate build for every W up to 8; at 16 MiB per rank buffer it runs
+    on wide units, under the last arriver (the default) and under per-tile flags with copier workgroups.
+    W = 5 and 8 run there in other tests; these are the rest, with a ragged element tail."""
+    for W in (2, 3, 4, 6, 7):
+        n = 8_388_608 + 2 * W + 1
+        bufs = workloads.rank_buffers(740 + W, W, n, "bf16", "uniform")
+        want = oracle.allreduce_sum_ref(bufs, "bf16")
+        dbufs = [to_dev(b, "bf16") for b in bufs]
+        for mode in ("twoshot", "twoshot:tile"):
+            print(f"[case] XCD two-shot W={W} n={n} {mode}", flush=True)
+            got = to_bits(_run(dbufs, "bf16", n, mode))
+            assert_reduce_equal(got, want, "bf16", f"XCD two-shot W={W} {mode}")
+        del dbufs
+        torch.cuda.empty_cache()
+    assert mr.workspace_check() == 0
+
+
 def test_w16_large_every_mode():
     """W = 16, the largest rank count, at about 8 MiB per rank buffer: the one-shot's wide tiles of one
     pack per lane (W > 8) over many tiles, and every two-shot hand-off on chunk tiles (the XCD-local
