@@ -111,7 +111,7 @@ def test_w16_large_every_mode():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("W", [1, 2, 3, 5, 8, 11, 16])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 6, 7, 8, 11, 16])
 def test_dtypes_W_and_ragged_sizes(dtype, W):
     for n in (1, 7, 8, 9, 1000, 4096 * W + 3, 300_007):
         bufs = workloads.rank_buffers(100 + W, W, n, dtype, "uniform")
