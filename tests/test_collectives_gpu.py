@@ -152,3 +152,46 @@ def test_binding_rejects_mismatched_extents():
     torch.cuda.synchronize()
     assert bool((sentinel == 7).all())
     assert bool((out == 0).all())
+
+
+def test_gathers_at_large_rank_counts():
+    """Rank counts far above 8: a rank-major scatter with W = 1000 (125 node-blocks of G = 8), and the
+    shard gathers at MR_MAX_TABLE_W = 64 ranks (param-contiguous, rank-major and list outputs), every element
+    against the oracle; 65 shards are refused with nothing written."""
+    import ctypes
+
+    W, G = 1000, 8
+    splits = [3, 17, 64, 0, 129, 8]
+    T = sum(splits)
+    print(f"[case] rank-major scatter W={W} G={G} T={T}", flush=True)
+    src = workloads.gather_source(780, W, T, "bf16")
+    out = torch.empty(W * T, dtype=torch.bfloat16, device=device())
+    mr.allgather_param_contig(to_dev(src, "bf16"), W, G, splits, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), oracle.allgather_param_contig_ref(src, W, G, splits))
+
+    W, G = 64, 16
+    splits = [7, 4096, 33, 1000]
+    T = sum(splits)
+    print(f"[case] shard gathers W={W} G={G} T={T}", flush=True)
+    shards = [workloads.random_bits(781, r, T, "fp32") for r in range(W)]
+    dshards = [to_dev(x, "fp32") for x in shards]
+    out = torch.empty(W * T, dtype=torch.float32, device=device())
+    mr.allgather_param_contig_shards(dshards, G, splits, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), oracle.allgather_param_contig_shards_ref(shards, G, splits))
+    mr.allgather_into_tensor(dshards, out)
+    outs = [torch.empty(T, dtype=torch.float32, device=device()) for _ in range(W)]
+    mr.allgather_list(dshards, outs)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), oracle.allgather_into_tensor_ref(shards))
+    for o, want in zip(outs, oracle.allgather_list_ref(shards)):
+        assert np.array_equal(to_bits(o), want)
+
+    extra = dshards + [dshards[0].clone()]
+    big = torch.zeros(65 * T, dtype=torch.float32, device=device())
+    ptrs = (ctypes.c_void_p * 65)(*[x.data_ptr() for x in extra])
+    rc = mr.lib().mr_allgather_into_tensor(ptrs, 65, T, mr.DTYPE_CODE["fp32"], big.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert rc == -1, rc  # MR_ERR_INVALID_ARG
+    assert int(torch.count_nonzero(big)) == 0
